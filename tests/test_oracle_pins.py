@@ -1,0 +1,407 @@
+"""Pins for the CPU oracle: each checks it against something other than itself
+(the pages' worked examples, a library routine, closed forms, invariants,
+brute force on tiny inputs).  CPU only."""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+from hypothesis import given, settings, strategies as st
+from scipy.special import logsumexp
+
+import oracle
+from oracle import APPEND, DROP, REPOS, OpSequenceError
+from oracle.replay import NEVER
+from segmented_attention_seq_amd import workload
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+KIND = {"APPEND": APPEND, "DROP": DROP, "REPOS": REPOS}
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _ops_from(g):
+    return oracle.canonical_ops(g["msg_len"], {int(k): v for k, v in g["drop"].items()},
+                                g["reposition"])
+
+
+def _runs(runs, T):
+    out = np.empty(T, np.int64)
+    for a, b, v in runs:
+        out[a:b] = NEVER if v == "never" else v
+    return out
+
+
+# ---------------------------------------------------------------- worked examples
+
+def test_request_example_structure():
+    g = _golden("request_example_tiny.json")
+    ops = _ops_from(g)
+    assert ops == [tuple([KIND[o[0]]] + o[1:]) for o in g["expected"]["ops"]]
+    t = oracle.plan_tables(ops, bq=16, bk=16)
+    e = g["expected"]
+    assert t["segments"][:, :2].tolist() == e["segments"]
+    assert np.array_equal(t["tok_drop"], _runs(e["tok_drop_runs"], 80))
+    assert np.array_equal(t["tok_pos"], _runs(e["tok_pos_runs"], 80) + np.arange(80))
+    assert t["visible_pairs"] == e["visible_pairs"]
+    assert t["final_tok"].tolist() == list(range(*e["final_tok_range"]))
+    assert t["final_pos"].tolist() == list(range(*e["final_pos_range"]))
+    assert t["p_next"] == e["p_next"]
+    # the repos sits at the last boundary: no stretch after it appends tokens
+    assert t["epochs"].tolist() == [[0, 80, 0, 0]]
+    recs, _ = oracle.replay_tokens(ops)
+    assert sum(len(v) for _, v in recs) == e["visible_pairs"]
+
+
+def test_readme_request_example():
+    g = _golden("readme_request_example.json")
+    ops = _ops_from(g)
+    assert ops == [tuple([KIND[o[0]]] + o[1:]) for o in g["expected"]["ops"]]
+    _, (act, pos, p_next) = oracle.replay_tokens(ops)
+    assert act == g["expected"]["final_tok"]
+    assert pos == g["expected"]["final_pos"]
+    assert p_next == g["expected"]["p_next"]
+
+
+def test_drop_before_repos_at_same_boundary():
+    # if repos ran first the dropped message would hold positions in the renumbering
+    ops = oracle.canonical_ops([2, 3, 4], {2: [0]}, [2])
+    _, (act, pos, p_next) = oracle.replay_tokens(ops)
+    assert act == list(range(2, 9)) and pos == list(range(7)) and p_next == 7
+
+
+@pytest.mark.parametrize("bad", [
+    dict(drop={3: [0]}), dict(drop={1: [2]}), dict(drop={0: [-1]}), dict(reposition=[5]),
+])
+def test_invalid_op_sequences(bad):
+    with pytest.raises(OpSequenceError):
+        oracle.canonical_ops([2, 2, 2], bad.get("drop"), bad.get("reposition"))
+
+
+def test_drop_twice_and_repeated_repos_are_harmless():
+    a = oracle.canonical_ops([2, 2, 2], {1: [0], 2: [0]}, [1, 1])
+    b = oracle.canonical_ops([2, 2, 2], {1: [0]}, [1])
+    ra, fa = oracle.replay_tokens(a)
+    rb, fb = oracle.replay_tokens(b)
+    assert ra == rb and fa == fb
+
+
+# ---------------------------------------------------------------- RoPE
+
+def _complex_rope(x, pos, base, layout):
+    """RoPE written as complex multiplication (a different formulation)."""
+    d = x.shape[-1]
+    if layout == 0:
+        z = x[..., : d // 2] + 1j * x[..., d // 2:]
+    else:
+        z = x[..., 0::2] + 1j * x[..., 1::2]
+    f = base ** (-np.arange(d // 2) * 2.0 / d)
+    z = z * np.exp(1j * np.asarray(pos, np.float64)[..., None] * f)
+    out = np.empty_like(x)
+    if layout == 0:
+        out[..., : d // 2], out[..., d // 2:] = z.real, z.imag
+    else:
+        out[..., 0::2], out[..., 1::2] = z.real, z.imag
+    return out
+
+
+@pytest.mark.parametrize("layout", [0, 1])
+def test_rope_matches_complex_rotation(layout):
+    rng = np.random.default_rng(0)
+    x = rng.standard_normal((50, 64))
+    p = rng.integers(0, 1 << 20, 50)
+    np.testing.assert_allclose(oracle.rope(x, p, 150000.0, layout),
+                               _complex_rope(x, p, 150000.0, layout), atol=1e-9)
+
+
+def test_rope_highest_frequency_is_one_radian_per_position():
+    x = np.zeros(64)
+    x[0] = 1.0
+    for p in (1, 7, 12345):
+        y = oracle.rope(x, np.array(p), 150000.0)
+        assert abs(y[0] - np.cos(p)) < 1e-12 and abs(y[32] - np.sin(p)) < 1e-12
+        assert np.abs(np.delete(y, [0, 32])).max() == 0
+
+
+@pytest.mark.parametrize("layout", [0, 1])
+def test_rope_composition_norm_and_relativity(layout):
+    rng = np.random.default_rng(1)
+    k = rng.standard_normal((200, 64))
+    q = rng.standard_normal((200, 64))
+    p = rng.integers(0, 1 << 20, 200)
+    r = rng.integers(0, 1 << 20, 200)
+    kp = oracle.rope(k, p, 150000.0, layout)
+    # moving a key built at p to r equals building it at r
+    np.testing.assert_allclose(oracle.rotate(kp, p, r, 150000.0, layout),
+                               oracle.rope(k, r, 150000.0, layout), atol=1e-8)
+    np.testing.assert_allclose(np.linalg.norm(kp, axis=1), np.linalg.norm(k, axis=1), rtol=1e-12)
+    # scores depend on the position difference only
+    s = 777
+    a = np.sum(oracle.rope(q, r, 150000.0, layout) * kp, axis=1)
+    b = np.sum(oracle.rope(q, r + s, 150000.0, layout) * oracle.rope(k, p + s, 150000.0, layout), axis=1)
+    np.testing.assert_allclose(a, b, atol=1e-8)
+
+
+# ---------------------------------------------------------------- bf16 rounding
+
+def test_bf16_rounding_matches_torch():
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal(100_000).astype(np.float32) * 3
+    # exact ties: float32 values whose low 16 bits are 0x8000
+    ties = (np.uint32(0x3F800000) + (rng.integers(0, 1 << 7, 1000).astype(np.uint32) << np.uint32(16))
+            + (rng.integers(0, 20, 1000).astype(np.uint32) << np.uint32(23))) | np.uint32(0x8000)
+    x = np.concatenate([x, ties.view(np.float32), -ties.view(np.float32)])
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(workload.f32_to_bf16_bits(x), ref)
+    assert np.array_equal(oracle.f64_to_bf16_bits(x.astype(np.float64)), ref)
+    # float64 rounding is direct (no float32 detour)
+    y = np.float64(1.0) + 2.0 ** -8 + 2.0 ** -40     # just above the tie -> rounds up
+    assert oracle.f64_to_bf16_bits(np.array([y]))[0] == 0x3F81
+
+
+# ---------------------------------------------------------------- attention
+
+def _sdpa_causal(q, k, v, hq, hkv):
+    """Library routine: PyTorch's float64 CPU scaled-dot-product attention."""
+    qt = torch.from_numpy(q).permute(1, 0, 2)[None]
+    kt = torch.from_numpy(k).permute(1, 0, 2)[None]
+    vt = torch.from_numpy(v).permute(1, 0, 2)[None]
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=True,
+                                                         enable_gqa=(hq != hkv))
+    return o[0].permute(1, 0, 2).numpy()
+
+
+@pytest.mark.parametrize("layout", [0, 1])
+def test_no_ops_is_causal_attention(layout):
+    rng = np.random.default_rng(3)
+    T, hq, hkv, d = 70, 8, 2, 16
+    q, k, v = (rng.standard_normal((T, h, d)) for h in (hq, hkv, hkv))
+    ops = oracle.canonical_ops([10, 25, 35])
+    o, lse = oracle.segment_attention(q, k, v, ops, base=150000.0, layout=layout)
+    pos = np.arange(T)
+    qr = _complex_rope(q, pos[:, None], 150000.0, layout)
+    kr = _complex_rope(k, pos[:, None], 150000.0, layout)
+    np.testing.assert_allclose(o, _sdpa_causal(qr, kr, v, hq, hkv), atol=1e-12)
+    o2, lse2 = oracle.attention_replay(q, k, v, ops, layout=layout)
+    np.testing.assert_allclose(o2, o, atol=1e-12)
+    # log-sum-exp against scipy for a few rows
+    for i, h in [(0, 0), (33, 5), (69, 7)]:
+        s = (qr[i, h] @ kr[: i + 1, h // 4].T) / np.sqrt(d)
+        assert abs(lse[i, h] - logsumexp(s)) < 1e-12
+
+
+@st.composite
+def op_sequences(draw):
+    M = draw(st.integers(1, 6))
+    lens = draw(st.lists(st.integers(0, 6), min_size=M, max_size=M))
+    drop = {}
+    for k in range(M):
+        tg = draw(st.lists(st.integers(0, k), max_size=3))
+        if tg:
+            drop[k] = tg
+    repos = draw(st.lists(st.integers(0, M - 1), max_size=3))
+    return lens, drop, repos
+
+
+@settings(max_examples=150, deadline=None)
+@given(op_sequences())
+def test_segment_batch_equals_replay(seq):
+    lens, drop, repos = seq
+    ops = oracle.canonical_ops(lens, drop, repos)
+    T = sum(lens)
+    if T == 0:
+        return
+    rng = np.random.default_rng(T)
+    q, k, v = (rng.standard_normal((T, h, 8)) for h in (4, 2, 2))
+    o1, l1 = oracle.attention_replay(q, k, v, ops, base=10000.0)
+    o2, l2 = oracle.segment_attention(q, k, v, ops, base=10000.0)
+    np.testing.assert_allclose(o2, o1, atol=1e-12)
+    np.testing.assert_allclose(l2, l1, atol=1e-12)
+
+
+@settings(max_examples=200, deadline=None)
+@given(op_sequences())
+def test_closed_form_mask_equals_replay(seq):
+    lens, drop, repos = seq
+    ops = oracle.canonical_ops(lens, drop, repos)
+    recs, fin = oracle.replay_tokens(ops)
+    ev = oracle.replay_events(ops)
+    assert ev.visible_pairs == sum(len(v) for _, v in recs)
+    for i, (pi, vis) in enumerate(recs):
+        assert ev.tok_pos[i] == pi
+        closed = [j for j in range(i + 1) if i < ev.tok_drop[j]]
+        assert [j for j, _ in vis] == closed
+    # every visible key's position equals its index on its stretch's virtual axis
+    for e, (tb, te, src) in enumerate(ev.epochs):
+        _, key_tok, key_pos = oracle.visibility_mask(ev, e)
+        where = {int(t): int(p) for t, p in zip(key_tok, key_pos)}
+        for i in range(tb, te):
+            for j, pj in recs[i][1]:
+                assert where[j] == pj
+    assert (list(ev.final[0]), list(ev.final[1]), ev.final[2]) == fin
+
+
+@settings(max_examples=100, deadline=None)
+@given(op_sequences(), st.sampled_from([(2, 2), (3, 2), (4, 4)]))
+def test_tile_classes_account_for_every_visible_pair(seq, tiles):
+    lens, drop, repos = seq
+    ops = oracle.canonical_ops(lens, drop, repos)
+    bq, bk = tiles
+    t = oracle.plan_tables(ops, bq=bq, bk=bk)
+    ev = oracle.replay_events(ops)
+    total = 0
+    for n, (e, qt) in enumerate(t["items"]):
+        mask, _, _ = oracle.visibility_mask(ev, e)
+        tb, te, src = ev.epochs[e]
+        r = src.size
+        rows = mask[qt * bq:(qt + 1) * bq]
+        for kt, c in zip(t["tile_k"][t["tile_ptr"][n]:t["tile_ptr"][n + 1]],
+                         t["tile_cls"][t["tile_ptr"][n]:t["tile_ptr"][n + 1]]):
+            nvt = -(-r // bk)
+            lo, hi = (kt * bk, min(r, (kt + 1) * bk)) if kt < nvt else \
+                (r + (kt - nvt) * bk, min(r + te - tb, r + (kt - nvt + 1) * bk))
+            blk = rows[:, lo:hi]
+            if c == 2:
+                assert blk.all() and hi - lo == bk
+            else:
+                assert blk.any() and not (blk.all() and hi - lo == bk)
+            total += int(blk.sum())
+    assert total == t["visible_pairs"]
+
+
+def _one_layer(ops, q, k, v):
+    o, _ = oracle.segment_attention(q, k, v, ops, base=10000.0)
+    return o
+
+
+def test_repos_without_drop_changes_nothing():
+    rng = np.random.default_rng(4)
+    q, k, v = (rng.standard_normal((30, h, 8)) for h in (4, 2, 2))
+    a = _one_layer(oracle.canonical_ops([10, 8, 12], {}, [0, 1]), q, k, v)
+    b = _one_layer(oracle.canonical_ops([10, 8, 12]), q, k, v)
+    np.testing.assert_allclose(a, b, atol=1e-13)
+
+
+def test_drop_at_final_boundary_only_changes_final_state():
+    rng = np.random.default_rng(5)
+    q, k, v = (rng.standard_normal((30, h, 8)) for h in (4, 2, 2))
+    ops_a = oracle.canonical_ops([10, 8, 12], {2: [1]}, [2])
+    ops_b = oracle.canonical_ops([10, 8, 12])
+    assert np.array_equal(_one_layer(ops_a, q, k, v), _one_layer(ops_b, q, k, v))
+    ta, tb = oracle.plan_tables(ops_a), oracle.plan_tables(ops_b)
+    assert ta["final_tok"].tolist() == list(range(10)) + list(range(18, 30))
+    assert ta["p_next"] == 22 and tb["p_next"] == 30
+
+
+# ---------------------------------------------------------------- Figure 5
+
+A, B, C = 16, 24, 40
+
+
+def _paths():
+    return {
+        1: ([A, B, C], {2: [0]}),      # read A,B; compute C; drop A
+        2: ([A, B, C], {1: [0]}),      # read A,B; drop A; compute C
+        3: ([B, C], {}),               # start at B; append C
+    }
+
+
+def test_shift_invariance_one_layer_paths_2_and_3():
+    """One layer: C under path 2 (B at 16..39, C at 40..79) equals path 3 (B at
+    0..23, C at 24..63); only relative positions matter."""
+    rng = np.random.default_rng(6)
+    q, k, v = (rng.standard_normal((A + B + C, h, 16)) for h in (4, 2, 2))
+    (l2, d2), (l3, d3) = _paths()[2], _paths()[3]
+    o2 = _one_layer(oracle.canonical_ops(l2, d2), q, k, v)
+    o3 = _one_layer(oracle.canonical_ops(l3, d3), q[A:], k[A:], v[A:])
+    np.testing.assert_allclose(o2[A + B:], o3[B:], atol=1e-10)
+    assert not np.allclose(o2[A:A + B], o3[:B], atol=1e-3)   # B itself saw A in path 2
+
+
+def test_figure5_history_dependence_two_layers():
+    """[P1] 'history dependence' (§3.4, Fig. 5), [P2] §2: the same surviving
+    tokens B, C hold different states under the three op orders.  Two-layer
+    attention-only residual toy with seeded weights."""
+    rng = np.random.default_rng(7)
+    dm, hq, hkv, d = 32, 4, 2, 8
+    x = rng.standard_normal((A + B + C, dm))
+    W = [[rng.standard_normal((dm, h * d)) / np.sqrt(dm) for h in (hq, hkv, hkv)] +
+         [rng.standard_normal((hq * d, dm)) / np.sqrt(hq * d)] for _ in range(2)]
+
+    def run(lens, drop, xin):
+        ops = oracle.canonical_ops(lens, drop)
+        h = xin.copy()
+        for wq, wk, wv, wo in W:
+            n = h.shape[0]
+            o, _ = oracle.segment_attention((h @ wq).reshape(n, hq, d), (h @ wk).reshape(n, hkv, d),
+                                            (h @ wv).reshape(n, hkv, d), ops, base=10000.0)
+            h = h + o.reshape(n, hq * d) @ wo
+        return h
+
+    h = {p: run(l, dr, x if p < 3 else x[A:]) for p, (l, dr) in _paths().items()}
+    Cs = {1: h[1][A + B:], 2: h[2][A + B:], 3: h[3][B:]}
+    Bs = {1: h[1][A:A + B], 2: h[2][A:A + B], 3: h[3][:B]}
+    for a_, b_ in [(1, 2), (1, 3), (2, 3)]:
+        assert np.abs(Cs[a_] - Cs[b_]).max() > 1e-3, (a_, b_)
+    assert np.array_equal(Bs[1], Bs[2])
+    assert np.abs(Bs[1] - Bs[3]).max() > 1e-3
+
+
+# ---------------------------------------------------------------- decode and repos
+
+def test_decode_is_one_row_prefill():
+    rng = np.random.default_rng(8)
+    lens, drop, repos = [5, 7, 9, 6], {2: [0], 3: [1]}, [2]
+    T = sum(lens)
+    q, k, v = (rng.standard_normal((T + 1, h, 8)) for h in (4, 2, 2))
+    ops = oracle.canonical_ops(lens, drop, repos)
+    od, _ = oracle.decode_after_ops(q[T], k[T], v[T], k[:T], v[:T], ops, base=10000.0)
+    full, _ = oracle.attention_replay(q, k, v, ops + [(APPEND, 1)], base=10000.0)
+    np.testing.assert_allclose(od[0], full[T], atol=1e-12)
+
+
+def test_decode_brute_force_and_gqa():
+    rng = np.random.default_rng(9)
+    q = rng.standard_normal((3, 8, 16))
+    n = [5, 1, 9]
+    ptr = np.concatenate([[0], np.cumsum(n)])
+    k, v = rng.standard_normal((2, ptr[-1], 2, 16))
+    o, lse = oracle.decode(q, k, v, ptr)
+    for b in range(3):
+        kk = torch.from_numpy(k[ptr[b]:ptr[b + 1]]).permute(1, 0, 2)[None]
+        vv = torch.from_numpy(v[ptr[b]:ptr[b + 1]]).permute(1, 0, 2)[None]
+        qq = torch.from_numpy(q[b])[None, :, None]
+        ref = torch.nn.functional.scaled_dot_product_attention(qq, kk, vv, enable_gqa=True)
+        np.testing.assert_allclose(o[b], ref[0, :, 0].numpy(), atol=1e-12)
+    assert np.allclose(o[1], np.repeat(v[ptr[1]], 4, axis=0))  # one key: output is its value
+
+
+def test_batched_repos_oracle():
+    rng = np.random.default_rng(10)
+    k = rng.standard_normal((100, 8, 64))
+    p = rng.integers(0, 200000, 100)
+    q = np.arange(100)
+    built_at_p = oracle.rope(k, p, 150000.0)
+    np.testing.assert_allclose(oracle.repos(built_at_p, p, q), oracle.rope(k, q, 150000.0), atol=1e-8)
+
+
+# ---------------------------------------------------------------- large-plan events
+
+def test_replay_events_on_workloads():
+    for cfg in (2, 3, 4):
+        tr = workload.config_trajectory(cfg)
+        ops = oracle.canonical_ops(tr.msg_len, tr.drop, tr.reposition)
+        ev = oracle.replay_events(ops)
+        assert ev.T == tr.n_tokens
+        # positions never reach the model's range after repos in the 96k config
+        if cfg == 3:
+            assert len(ev.epochs) == 7 and ev.tok_pos.max() < 96_000 + 4001 + 801
+        if cfg == 4:
+            assert len(ev.epochs) == 200
+        # tokens of a stretch sit at consecutive positions starting at r
+        for tb, te, src in ev.epochs:
+            assert np.array_equal(ev.tok_pos[tb:te], src.size + np.arange(te - tb))
