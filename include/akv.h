@@ -1,0 +1,221 @@
+/*
+ * akv.h -- C ABI of libakv: the AKV state-restoration hot path on MI355X (gfx950).
+ *
+ * What it computes (pages about "Cache Engineering for Agents", arXiv 2610.28577v1):
+ *   - the cache ops append / drop / repos and the operate-after request syntax
+ *     (jaehun.me review "Cache Engineering for Agents", sections "three cache
+ *     operations" (§3.3) and "AKV serving system" (§4, Fig. 6));
+ *   - segment-batch attention: one restore prefill whose causal attention is cut
+ *     at every drop/repos boundary; a dropped entry stays visible to the
+ *     segments that used it and is hidden from later ones; with repos, per-segment
+ *     KV versions are made by key rotation and value copy (same review, section
+ *     "single-prefill restore with segment-batch attention", §4.2, App. A.1.1, Fig. 10);
+ *   - repos: keys moved from position p to q by a RoPE rotation, values untouched
+ *     (same review, section "what to keep, how to align positions", §3.3);
+ *   - decode over the active cache only (same review, serving results, Fig. 12,
+ *     App. A.4.1), at page size 1 (vibeprogramminglab explainer, section 4).
+ *
+ * Conventions for every entry point:
+ *   - Return AKV_OK (0) or a negative AKV_E* status; akv_last_error() gives a
+ *     thread-local message for the last failure on the calling thread.  No C++
+ *     exception crosses this boundary.
+ *   - Host pointers are read during the call only.  Device pointers are owned by
+ *     the caller; the library never allocates device memory.  GPU entry points
+ *     enqueue work on the caller's stream and return without synchronising; a
+ *     launch error (hipGetLastError) is reported as AKV_EHIP.
+ *   - Tensors are dense, row-major, token-major:
+ *       Q / O     [tokens][Hq][d]
+ *       K / V     [tokens or pool slots or version rows][Hkv][d]
+ *     with element type given by `dtype` (AKV_BF16 or AKV_F32).  GQA maps query
+ *     head h to kv head h / (Hq / Hkv).
+ *   - RoPE: theta_i = base^(-2i/d), i < d/2; pair i is (x[i], x[i+d/2]) for
+ *     AKV_ROPE_HALF or (x[2i], x[2i+1]) for AKV_ROPE_INTERLEAVED; moving a vector
+ *     from position p to q rotates pair i by (q-p)*theta_i.  Angles are reduced
+ *     in float64 from the exact integer position difference.
+ */
+#ifndef AKV_H
+#define AKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define AKV_OK            0
+#define AKV_EINVAL       -1   /* bad argument (null pointer, size, capacity) */
+#define AKV_EOPSEQ       -2   /* invalid op sequence (drop of a future message, ...) */
+#define AKV_EUNSUPPORTED -3   /* valid but not implemented (e.g. head dim != 64) */
+#define AKV_EHIP         -4   /* HIP runtime / launch error */
+#define AKV_ENOMEM       -5   /* host allocation failed */
+
+/* Element types. */
+#define AKV_F32  0
+#define AKV_BF16 1
+
+/* RoPE pair layouts. */
+#define AKV_ROPE_HALF        0
+#define AKV_ROPE_INTERLEAVED 1
+
+/* Canonical cache ops. */
+#define AKV_OP_APPEND 0   /* a = number of tokens appended (>= 0) */
+#define AKV_OP_DROP   1   /* drop logical tokens [a, b) (already appended) */
+#define AKV_OP_REPOS  2   /* renumber the active keys 0..r-1, next position r */
+
+/* Tile classes in the plan's tile lists (tile entry = k_tile * 4 + class). */
+#define AKV_TILE_PARTIAL 1
+#define AKV_TILE_FULL    2
+
+typedef struct { int32_t kind; int32_t reserved; int64_t a, b; } akv_op;
+
+typedef struct akv_plan akv_plan;   /* opaque, host-owned, immutable once built */
+
+typedef void* akv_stream_t;         /* a hipStream_t (NULL = the null stream) */
+
+const char* akv_status_string(int status);
+const char* akv_last_error(void);
+const char* akv_version(void);
+
+/* ---------------------------------------------------------------- A1: op compile (host)
+ *
+ * akv_ops_from_messages: the operate-after request -> canonical op list.
+ *   msg_len[n_msgs]            tokens per message (message k is an implicit append);
+ *   drop_after/drop_target[n_drop]   pairs "after message k, drop message j";
+ *   repos_after[n_repos]       "after message k, repos".
+ * Canonical form: for k = 0..n_msgs-1: APPEND(msg_len[k]); then one DROP per
+ * distinct non-empty target of k in ascending message order (token range of the
+ * target); then one REPOS if k is listed in repos_after.  Drop comes before repos
+ * at the same boundary (review §4, Fig. 6; explainer section 4).
+ * Errors: AKV_EOPSEQ if k or j is outside [0, n_msgs) or j > k; AKV_EINVAL for a
+ * negative length, null arrays with non-zero counts, or ops_cap too small.
+ * *n_ops_out always receives the number of ops required; ops_out may be NULL to
+ * query it.
+ */
+int akv_ops_from_messages(int32_t n_msgs, const int32_t* msg_len,
+                          int32_t n_drop, const int32_t* drop_after, const int32_t* drop_target,
+                          int32_t n_repos, const int32_t* repos_after,
+                          akv_op* ops_out, int64_t ops_cap, int64_t* n_ops_out);
+
+/* akv_build_visibility: replay the ops and compile the restore plan (all host).
+ * bq / bk: query / key tile sizes of the tile-class lists (the GPU attention
+ * kernel needs bq == 64 and bk == 64).
+ * Tables (all int32, see akv_plan_tables):
+ *   T1 tok_pos[T]    position of each token when appended;
+ *   T2 tok_drop[T]   token index of the boundary at which it is dropped, or INT32_MAX;
+ *                    query i sees key j  <=>  j <= i < tok_drop[j];
+ *   T3 segments      (begin, end, stretch) per maximal run with no drop/repos inside;
+ *   T4 stretches     (tok_begin, tok_end, r, ver_offset) per repos stretch that
+ *                    appends tokens; r = keys active right after its repos;
+ *   T5 versions      (src token, from_pos, to_pos) per version row, stretch by
+ *                    stretch; to_pos = row index v in the stretch;
+ *   T6 tiles         per work item (stretch, q-tile): ascending non-empty key tiles
+ *                    with class FULL or PARTIAL; key tiles run over the version rows
+ *                    from 0 and restart at the stretch's own tokens; a tile is FULL
+ *                    only if it holds bk keys and every in-range query sees all;
+ *   T7 final         active tokens ascending, their positions, p_next.
+ * Errors: AKV_EOPSEQ (bad kind, negative append, drop range not yet appended),
+ * AKV_EINVAL (bq/bk < 1, > 2^20, or more than 2^31-1 tokens), AKV_ENOMEM.
+ */
+int akv_build_visibility(const akv_op* ops, int64_t n_ops, int32_t bq, int32_t bk, akv_plan** out);
+
+typedef struct {
+  int64_t n_tokens, n_segments, n_epochs, n_versions;
+  int64_t n_items, n_tiles, n_full, n_partial;
+  int64_t visible_pairs;       /* exact number of (query, key) pairs attended */
+  int64_t n_final, p_next;
+  int32_t bq, bk;
+  uint64_t device_bytes;       /* size of the device image for akv_plan_upload */
+} akv_plan_info;
+
+typedef struct {
+  const int32_t* tok_pos;      /* [n_tokens] */
+  const int32_t* tok_drop;     /* [n_tokens] */
+  const int32_t* segments;     /* [n_segments][3] */
+  const int32_t* epochs;       /* [n_epochs][4] */
+  const int32_t* versions;     /* [n_versions][3] */
+  const int32_t* items;        /* [n_items][2] stretch, q-tile */
+  const int32_t* tile_ptr;     /* [n_items + 1] */
+  const int32_t* tiles;        /* [n_tiles] k_tile * 4 + class */
+  const int32_t* item_order;   /* [n_items] launch order: descending tile count */
+  const int32_t* final_tok;    /* [n_final] */
+  const int32_t* final_pos;    /* [n_final] */
+} akv_plan_tables;
+
+int  akv_plan_info_get(const akv_plan* plan, akv_plan_info* info);
+/* Read-only views into the plan (valid until akv_plan_destroy). */
+int  akv_plan_tables_get(const akv_plan* plan, akv_plan_tables* views);
+/* Copy the plan's device image (info.device_bytes) to caller memory `dev`,
+ * asynchronously on `stream`; the plan must outlive the copy. */
+int  akv_plan_upload(const akv_plan* plan, void* dev, uint64_t dev_bytes, akv_stream_t stream);
+void akv_plan_destroy(akv_plan* plan);
+
+/* ---------------------------------------------------------------- A2/A5: RoPE rotation
+ *
+ * akv_rope_repos: out[n] = R((pos_to[n] - pos_from[n]) theta) * in[gather ? gather[n] : n]
+ * for n < n_rows; each row holds `heads` vectors of length d (d even, d <= 256,
+ * d % 16 == 0).  pos_from may be NULL (all zero: "in" holds raw un-rotated vectors,
+ * i.e. RoPE-apply); gather may be NULL.  pos_from / pos_to / gather are device
+ * int32 arrays.  out must not overlap in unless gather is NULL and out == in.
+ * This is the batched repos of the review (§3.3: rotation only, values untouched).
+ */
+int akv_rope_repos(void* out, const void* in, int dtype, int64_t n_rows, int32_t heads, int32_t d,
+                   const int32_t* gather, const int32_t* pos_from, const int32_t* pos_to,
+                   double rope_base, int rope_layout, akv_stream_t stream);
+
+/* akv_rope_apply: rotate raw Q or K rows [n_tokens][heads][d] to their append
+ * positions (plan T1), out of place or in place.  dev_plan = the uploaded image. */
+int akv_rope_apply(const akv_plan* plan, const void* dev_plan, void* out, const void* in,
+                   int dtype, int32_t heads, int32_t d, double rope_base, int rope_layout,
+                   akv_stream_t stream);
+
+/* ---------------------------------------------------------------- A3: KV versions
+ *
+ * For every version row (T5): k_ver[row] = R((to_pos - from_pos) theta) * k[src],
+ * v_ver[row] = v[src] (bit copy).  k must already be rotated to the append
+ * positions (akv_rope_apply).  k_ver / v_ver: [n_versions][hkv][d].
+ * Review §4.2 / App. A.1.1: temporary per-segment versions by key rotation and
+ * value copy.
+ */
+int akv_build_kv_versions(const akv_plan* plan, const void* dev_plan, const void* k, const void* v,
+                          void* k_ver, void* v_ver, int dtype, int32_t hkv, int32_t d,
+                          double rope_base, int rope_layout, akv_stream_t stream);
+
+/* ---------------------------------------------------------------- A4: segment attention
+ *
+ * out[i][h] = sum_key softmax(scale * <q[i][h], key>) value over the keys visible
+ * to token i on its stretch's axis: the stretch's version rows (k_ver/v_ver) with
+ * tok_drop[src] > i, then its own tokens j <= i with tok_drop[j] > i.
+ * q, k: rotated to append positions; out [n_tokens][hq][d]; lse (nullable, float32
+ * [n_tokens][hq]) receives the natural-log sum of exp(scale * score).
+ * scale <= 0 means 1/sqrt(d).  bf16 needs d == 64 and plan bq == bk == 64; f32
+ * (a CUDA-core path for small problems) needs d <= 128.
+ */
+int akv_segment_attention(const akv_plan* plan, const void* dev_plan,
+                          const void* q, const void* k, const void* v,
+                          const void* k_ver, const void* v_ver, void* out, float* lse,
+                          int dtype, int32_t hq, int32_t hkv, int32_t d, float scale,
+                          akv_stream_t stream);
+
+/* ---------------------------------------------------------------- A6: decode
+ *
+ * One query token per request b < batch: out[b][h] = attention of q[b][h] over the
+ * pool rows indices[indptr[b] .. indptr[b+1]) (its active cache plus its own new
+ * slot, gathered at page size 1).  q, k_pool, v_pool: bf16; indptr/indices: device
+ * int32; max_n >= every request's key count (host-side bound, sets the split
+ * count).  A request with zero keys is an error the kernel cannot report; callers
+ * must include the new token's own slot.  ws: device workspace of at least
+ * akv_decode_workspace_bytes(...) bytes.  scale <= 0 means 1/sqrt(d).  d == 64.
+ */
+uint64_t akv_decode_workspace_bytes(int32_t batch, int32_t hq, int32_t hkv, int32_t d, int64_t max_n);
+int akv_decode_attention(const void* q, const void* k_pool, const void* v_pool,
+                         const int32_t* indptr, const int32_t* indices, int32_t batch,
+                         int32_t hq, int32_t hkv, int32_t d, int64_t max_n, float scale,
+                         int dtype, void* out, float* lse, void* ws, uint64_t ws_bytes,
+                         akv_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* AKV_H */

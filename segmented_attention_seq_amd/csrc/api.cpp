@@ -1,0 +1,257 @@
+// C ABI of libakv: argument validation, error reporting, dispatch.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <climits>
+#include <cmath>
+#include <new>
+#include <set>
+#include <string>
+
+#include "internal.h"
+
+namespace akv {
+
+static thread_local std::string g_last_error;
+
+void set_error(const std::string& msg) { g_last_error = msg; }
+
+int fail(int status, const std::string& msg) {
+  g_last_error = msg;
+  return status;
+}
+
+}  // namespace akv
+
+using akv::fail;
+
+extern "C" {
+
+const char* akv_status_string(int status) {
+  switch (status) {
+    case AKV_OK: return "ok";
+    case AKV_EINVAL: return "invalid argument";
+    case AKV_EOPSEQ: return "invalid op sequence";
+    case AKV_EUNSUPPORTED: return "unsupported configuration";
+    case AKV_EHIP: return "HIP runtime error";
+    case AKV_ENOMEM: return "out of host memory";
+    default: return "unknown status";
+  }
+}
+
+const char* akv_last_error(void) { return akv::g_last_error.c_str(); }
+
+const char* akv_version(void) { return "akv-mi355x 0.1 (gfx950)"; }
+
+int akv_ops_from_messages(int32_t n_msgs, const int32_t* msg_len, int32_t n_drop,
+                          const int32_t* drop_after, const int32_t* drop_target, int32_t n_repos,
+                          const int32_t* repos_after, akv_op* ops_out, int64_t ops_cap,
+                          int64_t* n_ops_out) {
+  if (!n_ops_out) return fail(AKV_EINVAL, "n_ops_out is NULL");
+  *n_ops_out = 0;
+  if (n_msgs < 0 || n_drop < 0 || n_repos < 0) return fail(AKV_EINVAL, "negative count");
+  if ((n_msgs && !msg_len) || (n_drop && (!drop_after || !drop_target)) || (n_repos && !repos_after))
+    return fail(AKV_EINVAL, "NULL array with non-zero count");
+  try {
+    std::vector<int64_t> start(n_msgs + 1, 0);
+    for (int32_t k = 0; k < n_msgs; ++k) {
+      if (msg_len[k] < 0) return fail(AKV_EINVAL, "message " + std::to_string(k) + " has negative length");
+      start[k + 1] = start[k] + msg_len[k];
+    }
+    std::vector<std::set<int32_t>> targets(n_msgs);
+    for (int32_t n = 0; n < n_drop; ++n) {
+      const int32_t k = drop_after[n], j = drop_target[n];
+      if (k < 0 || k >= n_msgs) return fail(AKV_EOPSEQ, "drop after message " + std::to_string(k) + ": no such message");
+      if (j < 0 || j >= n_msgs) return fail(AKV_EOPSEQ, "drop target " + std::to_string(j) + ": no such message");
+      if (j > k) return fail(AKV_EOPSEQ, "drop target " + std::to_string(j) + " comes after message " + std::to_string(k));
+      targets[k].insert(j);
+    }
+    std::vector<char> repos(n_msgs, 0);
+    for (int32_t n = 0; n < n_repos; ++n) {
+      const int32_t k = repos_after[n];
+      if (k < 0 || k >= n_msgs) return fail(AKV_EOPSEQ, "reposition after message " + std::to_string(k) + ": no such message");
+      repos[k] = 1;
+    }
+    int64_t need = 0;
+    for (int32_t k = 0; k < n_msgs; ++k) {
+      need += 1 + repos[k];
+      for (int32_t j : targets[k]) need += msg_len[j] > 0;
+    }
+    *n_ops_out = need;
+    if (!ops_out) return AKV_OK;
+    if (ops_cap < need) return fail(AKV_EINVAL, "ops_cap too small: need " + std::to_string(need));
+    int64_t w = 0;
+    for (int32_t k = 0; k < n_msgs; ++k) {
+      ops_out[w++] = akv_op{AKV_OP_APPEND, 0, msg_len[k], 0};
+      for (int32_t j : targets[k])
+        if (msg_len[j] > 0) ops_out[w++] = akv_op{AKV_OP_DROP, 0, start[j], start[j + 1]};
+      if (repos[k]) ops_out[w++] = akv_op{AKV_OP_REPOS, 0, 0, 0};
+    }
+    return AKV_OK;
+  } catch (const std::bad_alloc&) {
+    return fail(AKV_ENOMEM, "host allocation failed");
+  }
+}
+
+int akv_build_visibility(const akv_op* ops, int64_t n_ops, int32_t bq, int32_t bk, akv_plan** out) {
+  return akv::build_plan(ops, n_ops, bq, bk, out);
+}
+
+int akv_plan_info_get(const akv_plan* p, akv_plan_info* info) {
+  if (!p || !info) return fail(AKV_EINVAL, "NULL plan or info");
+  info->n_tokens = p->T;
+  info->n_segments = (int64_t)p->segments.size() / 3;
+  info->n_epochs = (int64_t)p->epochs.size() / 4;
+  info->n_versions = (int64_t)p->versions.size() / 3;
+  info->n_items = (int64_t)p->items.size() / 2;
+  info->n_tiles = (int64_t)p->tiles.size();
+  info->n_full = p->n_full;
+  info->n_partial = p->n_partial;
+  info->visible_pairs = p->visible_pairs;
+  info->n_final = (int64_t)p->final_tok.size();
+  info->p_next = p->p_next;
+  info->bq = p->bq;
+  info->bk = p->bk;
+  info->device_bytes = p->image.size();
+  return AKV_OK;
+}
+
+int akv_plan_tables_get(const akv_plan* p, akv_plan_tables* v) {
+  if (!p || !v) return fail(AKV_EINVAL, "NULL plan or views");
+  v->tok_pos = p->tok_pos.data();
+  v->tok_drop = p->tok_drop.data();
+  v->segments = p->segments.data();
+  v->epochs = p->epochs.data();
+  v->versions = p->versions.data();
+  v->items = p->items.data();
+  v->tile_ptr = p->tile_ptr.data();
+  v->tiles = p->tiles.data();
+  v->item_order = p->item_order.data();
+  v->final_tok = p->final_tok.data();
+  v->final_pos = p->final_pos.data();
+  return AKV_OK;
+}
+
+int akv_plan_upload(const akv_plan* p, void* dev, uint64_t dev_bytes, akv_stream_t stream) {
+  if (!p || !dev) return fail(AKV_EINVAL, "NULL plan or device buffer");
+  if (dev_bytes < p->image.size()) return fail(AKV_EINVAL, "device buffer smaller than the plan image");
+  hipError_t e = hipMemcpyAsync(dev, p->image.data(), p->image.size(), hipMemcpyHostToDevice,
+                                (hipStream_t)stream);
+  if (e != hipSuccess) return fail(AKV_EHIP, std::string("plan upload: ") + hipGetErrorString(e));
+  return AKV_OK;
+}
+
+void akv_plan_destroy(akv_plan* p) { delete p; }
+
+static int check_rope(int dtype, int32_t heads, int32_t d, int layout, double base) {
+  if (dtype != AKV_F32 && dtype != AKV_BF16) return fail(AKV_EINVAL, "dtype must be AKV_F32 or AKV_BF16");
+  if (heads < 1) return fail(AKV_EINVAL, "heads must be >= 1");
+  if (d < 16 || d > 256 || d % 16) return fail(AKV_EUNSUPPORTED, "RoPE needs d % 16 == 0 and 16 <= d <= 256");
+  if (layout != AKV_ROPE_HALF && layout != AKV_ROPE_INTERLEAVED) return fail(AKV_EINVAL, "unknown RoPE layout");
+  if (!(base > 1.0) || !std::isfinite(base)) return fail(AKV_EINVAL, "RoPE base must be finite and > 1");
+  return AKV_OK;
+}
+
+int akv_rope_repos(void* out, const void* in, int dtype, int64_t n_rows, int32_t heads, int32_t d,
+                   const int32_t* gather, const int32_t* pos_from, const int32_t* pos_to,
+                   double rope_base, int rope_layout, akv_stream_t stream) {
+  int st = check_rope(dtype, heads, d, rope_layout, rope_base);
+  if (st) return st;
+  if (n_rows < 0) return fail(AKV_EINVAL, "n_rows < 0");
+  if (n_rows == 0) return AKV_OK;
+  if (!out || !in || !pos_to) return fail(AKV_EINVAL, "NULL out, in or pos_to");
+  if (gather && out == in) return fail(AKV_EINVAL, "in-place rotation cannot gather");
+  akv::RopeArgs a{out, in, nullptr, nullptr, n_rows, heads, d, gather, pos_from, pos_to,
+                  rope_base, rope_layout, dtype};
+  return akv::launch_rope(a, stream);
+}
+
+int akv_rope_apply(const akv_plan* p, const void* dev_plan, void* out, const void* in, int dtype,
+                   int32_t heads, int32_t d, double rope_base, int rope_layout, akv_stream_t stream) {
+  if (!p || !dev_plan) return fail(AKV_EINVAL, "NULL plan or device plan");
+  int st = check_rope(dtype, heads, d, rope_layout, rope_base);
+  if (st) return st;
+  if (p->T == 0) return AKV_OK;
+  if (!out || !in) return fail(AKV_EINVAL, "NULL out or in");
+  const auto* base = (const uint8_t*)dev_plan;
+  akv::RopeArgs a{out, in, nullptr, nullptr, p->T, heads, d, nullptr, nullptr,
+                  (const int32_t*)(base + p->off_tok_pos), rope_base, rope_layout, dtype};
+  return akv::launch_rope(a, stream);
+}
+
+int akv_build_kv_versions(const akv_plan* p, const void* dev_plan, const void* k, const void* v,
+                          void* k_ver, void* v_ver, int dtype, int32_t hkv, int32_t d,
+                          double rope_base, int rope_layout, akv_stream_t stream) {
+  if (!p || !dev_plan) return fail(AKV_EINVAL, "NULL plan or device plan");
+  int st = check_rope(dtype, hkv, d, rope_layout, rope_base);
+  if (st) return st;
+  const int64_t nv = (int64_t)p->versions.size() / 3;
+  if (nv == 0) return AKV_OK;
+  if (!k || !v || !k_ver || !v_ver) return fail(AKV_EINVAL, "NULL k, v, k_ver or v_ver");
+  const auto* base = (const uint8_t*)dev_plan;
+  akv::RopeArgs a{k_ver, k, v_ver, v, nv, hkv, d, (const int32_t*)(base + p->off_ver_src),
+                  (const int32_t*)(base + p->off_ver_from), (const int32_t*)(base + p->off_ver_to),
+                  rope_base, rope_layout, dtype};
+  return akv::launch_rope(a, stream);
+}
+
+int akv_segment_attention(const akv_plan* p, const void* dev_plan, const void* q, const void* k,
+                          const void* v, const void* k_ver, const void* v_ver, void* out, float* lse,
+                          int dtype, int32_t hq, int32_t hkv, int32_t d, float scale,
+                          akv_stream_t stream) {
+  if (!p || !dev_plan) return fail(AKV_EINVAL, "NULL plan or device plan");
+  if (dtype != AKV_F32 && dtype != AKV_BF16) return fail(AKV_EINVAL, "dtype must be AKV_F32 or AKV_BF16");
+  if (hq < 1 || hkv < 1 || hq % hkv) return fail(AKV_EINVAL, "hq must be a positive multiple of hkv");
+  const int32_t grp = hq / hkv;
+  if (dtype == AKV_BF16) {
+    if (d != 64) return fail(AKV_EUNSUPPORTED, "bf16 segment attention needs d == 64");
+    if (p->bq != 64 || p->bk != 64) return fail(AKV_EUNSUPPORTED, "bf16 segment attention needs a plan with bq == bk == 64");
+    if (grp != 1 && grp != 2 && grp != 4 && grp != 8)
+      return fail(AKV_EUNSUPPORTED, "bf16 segment attention needs hq/hkv in {1, 2, 4, 8}");
+  } else {
+    if (d < 1 || d > 128) return fail(AKV_EUNSUPPORTED, "f32 segment attention needs d <= 128");
+    if (p->bq > 256) return fail(AKV_EUNSUPPORTED, "f32 segment attention needs bq <= 256");
+  }
+  if (p->T == 0) return AKV_OK;
+  if (!q || !k || !v || !out) return fail(AKV_EINVAL, "NULL q, k, v or out");
+  if (!p->versions.empty() && (!k_ver || !v_ver)) return fail(AKV_EINVAL, "plan has version rows: k_ver/v_ver required");
+  if (!(scale > 0.0f)) scale = 1.0f / std::sqrt((float)d);
+  const auto* base = (const uint8_t*)dev_plan;
+  akv::AttnArgs a{q, k, v, k_ver, v_ver, out, lse,
+                  (const int32_t*)(base + p->off_item_desc), (const int32_t*)(base + p->off_tiles),
+                  (const int32_t*)(base + p->off_order), (const int32_t*)(base + p->off_tok_drop),
+                  (const int32_t*)(base + p->off_ver_drop), (int64_t)p->items.size() / 2,
+                  hq, hkv, d, p->bq, p->bk, scale, dtype};
+  return akv::launch_segment_attention(a, stream);
+}
+
+uint64_t akv_decode_workspace_bytes(int32_t batch, int32_t hq, int32_t hkv, int32_t d, int64_t max_n) {
+  (void)hkv;
+  int32_t splits = 0, chunk = 0;
+  if (batch < 1 || hq < 1 || d < 1 || akv::decode_split_plan(max_n, &splits, &chunk)) return 0;
+  return 4 * akv::decode_ws_floats(batch, hq, d, splits);
+}
+
+int akv_decode_attention(const void* q, const void* k_pool, const void* v_pool, const int32_t* indptr,
+                         const int32_t* indices, int32_t batch, int32_t hq, int32_t hkv, int32_t d,
+                         int64_t max_n, float scale, int dtype, void* out, float* lse, void* ws,
+                         uint64_t ws_bytes, akv_stream_t stream) {
+  if (dtype != AKV_BF16) return fail(AKV_EUNSUPPORTED, "decode attention is bf16 only");
+  if (d != 64) return fail(AKV_EUNSUPPORTED, "decode attention needs d == 64");
+  if (hq < 1 || hkv < 1 || hq % hkv || hq / hkv > 16)
+    return fail(AKV_EUNSUPPORTED, "decode needs hq a multiple of hkv with hq/hkv <= 16");
+  if (batch < 0) return fail(AKV_EINVAL, "batch < 0");
+  if (batch == 0) return AKV_OK;
+  if (!q || !k_pool || !v_pool || !indptr || !indices || !out || !ws)
+    return fail(AKV_EINVAL, "NULL pointer argument");
+  int32_t splits = 0, chunk = 0;
+  if (akv::decode_split_plan(max_n, &splits, &chunk)) return fail(AKV_EINVAL, "max_n must be in [1, 2^31)");
+  if (ws_bytes < 4 * akv::decode_ws_floats(batch, hq, d, splits))
+    return fail(AKV_EINVAL, "decode workspace too small");
+  if (!(scale > 0.0f)) scale = 1.0f / std::sqrt((float)d);
+  akv::DecodeArgs a{q, k_pool, v_pool, indptr, indices, batch, hq, hkv, d, splits, chunk, scale,
+                    out, lse, (float*)ws};
+  return akv::launch_decode(a, stream);
+}
+
+}  // extern "C"

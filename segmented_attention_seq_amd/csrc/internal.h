@@ -1,0 +1,83 @@
+// Internal declarations shared by the translation units of libakv.
+#pragma once
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "akv.h"
+
+struct akv_plan {
+  int32_t bq = 0, bk = 0;
+  int64_t T = 0;
+  // host tables (layouts documented in akv.h)
+  std::vector<int32_t> tok_pos, tok_drop;
+  std::vector<int32_t> segments;    // 3 per segment
+  std::vector<int32_t> epochs;      // 4 per stretch
+  std::vector<int32_t> versions;    // 3 per version row
+  std::vector<int32_t> items;       // 2 per item
+  std::vector<int32_t> tile_ptr;    // n_items + 1
+  std::vector<int32_t> tiles;       // k_tile * 4 + class
+  std::vector<int32_t> item_order;
+  std::vector<int32_t> final_tok, final_pos;
+  int64_t visible_pairs = 0, p_next = 0, n_full = 0, n_partial = 0;
+  // device image: contiguous int32 arrays at 256-byte aligned offsets
+  std::vector<uint8_t> image;
+  uint64_t off_tok_pos = 0, off_tok_drop = 0, off_ver_src = 0, off_ver_from = 0, off_ver_to = 0,
+           off_ver_drop = 0, off_item_desc = 0, off_tiles = 0, off_order = 0;
+};
+
+namespace akv {
+
+// Per-item descriptor in the device image (8 int32).
+enum { ID_QBEGIN = 0, ID_QEND, ID_TB, ID_TE, ID_R, ID_VEROFF, ID_TILE0, ID_TILE1, ID_WORDS };
+
+void set_error(const std::string& msg);
+int fail(int status, const std::string& msg);
+
+int build_plan(const akv_op* ops, int64_t n_ops, int32_t bq, int32_t bk, akv_plan** out);
+
+// Kernel launchers (return AKV_OK or AKV_EHIP); arguments are validated by the callers.
+struct RopeArgs {
+  void* out;
+  const void* in;
+  void* v_out;          // optional value copy (versions); nullptr if none
+  const void* v_in;
+  int64_t n_rows;
+  int32_t heads, d;
+  const int32_t* gather;
+  const int32_t* pos_from;
+  const int32_t* pos_to;
+  double base;
+  int layout;
+  int dtype;
+};
+int launch_rope(const RopeArgs& a, void* stream);
+
+struct AttnArgs {
+  const void *q, *k, *v, *k_ver, *v_ver;
+  void* out;
+  float* lse;
+  const int32_t *item_desc, *tiles, *order, *tok_drop, *ver_drop;
+  int64_t n_items;
+  int32_t hq, hkv, d, bq, bk;
+  float scale;
+  int dtype;
+};
+int launch_segment_attention(const AttnArgs& a, void* stream);
+
+struct DecodeArgs {
+  const void *q, *k, *v;
+  const int32_t *indptr, *indices;
+  int32_t batch, hq, hkv, d;
+  int32_t splits, chunk;
+  float scale;
+  void* out;
+  float* lse;
+  float* ws;
+};
+int decode_split_plan(int64_t max_n, int32_t* splits, int32_t* chunk);
+uint64_t decode_ws_floats(int32_t batch, int32_t hq, int32_t d, int32_t splits);
+int launch_decode(const DecodeArgs& a, void* stream);
+
+}  // namespace akv

@@ -1,0 +1,165 @@
+// RoPE rotation kernel: repos (key re-rotation p -> q), RoPE-apply (raw -> append
+// position) and the KV-version builder (rotated key + value copy).
+//
+// "Cache Engineering for Agents" review, "what to keep, how to align positions"
+// (§3.3): moving a cached key from position p to q multiplies it by a rotation
+// matrix and leaves the value untouched; "single-prefill restore" (§4.2, App.
+// A.1.1): per-segment KV versions are made by key rotation and value copy.
+//
+// Bandwidth-bound.  One thread owns one 8-pair chunk of a row (pairs 8c..8c+7)
+// and walks every head of that row, so its 8 (cos, sin) values are computed once
+// and reused heads times.  Loads and stores are 16-byte vectors; a wave covers
+// 16 rows x 64 contiguous bytes per instruction (the partner half-chunk load
+// completes each 128-byte line).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+
+#include "internal.h"
+
+namespace akv {
+namespace {
+
+// 2*pi split in two doubles for Cody & Waite's reduction (Cody, W. and Waite, W.,
+// "Software Manual for the Elementary Functions", 1980): x - k*2pi is evaluated as
+// (x - k*C1) - k*C2 with fma, so the reduced angle keeps ~1e-15 absolute accuracy
+// for |x| up to ~1e9.
+constexpr double kTwoPiHi = 6.283185307179586232;     // double nearest 2*pi
+constexpr double kTwoPiLo = 2.4492935982947064e-16;   // 2*pi - kTwoPiHi
+constexpr double kInvTwoPi = 0.15915494309189533577;
+
+struct Freqs { double theta[128]; };
+
+__device__ __forceinline__ void angle_cs(long long delta, double th, float& c, float& s) {
+  const double x = (double)delta * th;
+  const double k = rint(x * kInvTwoPi);
+  double r = fma(-k, kTwoPiHi, x);
+  r = fma(-k, kTwoPiLo, r);
+  sincosf((float)r, &s, &c);
+}
+
+__device__ __forceinline__ float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  const __bf16 x = (__bf16)a, y = (__bf16)b;  // round to nearest even
+  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+}
+
+// 8 consecutive elements <-> float[8]
+template <typename T> struct Vec8;
+template <> struct Vec8<uint16_t> {  // bf16 storage
+  static __device__ __forceinline__ void load(const uint16_t* p, float f[8]) {
+    const uint4 u = *(const uint4*)p;
+    f[0] = bf_lo(u.x); f[1] = bf_hi(u.x); f[2] = bf_lo(u.y); f[3] = bf_hi(u.y);
+    f[4] = bf_lo(u.z); f[5] = bf_hi(u.z); f[6] = bf_lo(u.w); f[7] = bf_hi(u.w);
+  }
+  static __device__ __forceinline__ void store(uint16_t* p, const float f[8]) {
+    uint4 u;
+    u.x = pack_bf16(f[0], f[1]); u.y = pack_bf16(f[2], f[3]);
+    u.z = pack_bf16(f[4], f[5]); u.w = pack_bf16(f[6], f[7]);
+    *(uint4*)p = u;
+  }
+  static __device__ __forceinline__ void copy(uint16_t* d, const uint16_t* s) { *(uint4*)d = *(const uint4*)s; }
+};
+template <> struct Vec8<float> {
+  static __device__ __forceinline__ void load(const float* p, float f[8]) {
+    const float4 a = *(const float4*)p, b = *(const float4*)(p + 4);
+    f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w; f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+  }
+  static __device__ __forceinline__ void store(float* p, const float f[8]) {
+    *(float4*)p = make_float4(f[0], f[1], f[2], f[3]);
+    *(float4*)(p + 4) = make_float4(f[4], f[5], f[6], f[7]);
+  }
+  static __device__ __forceinline__ void copy(float* d, const float* s) {
+    *(float4*)d = *(const float4*)s;
+    *(float4*)(d + 4) = *(const float4*)(s + 4);
+  }
+};
+
+template <typename T, int LAYOUT>
+__global__ __launch_bounds__(256) void rope_kernel(T* __restrict__ out, const T* __restrict__ in,
+                                                   T* __restrict__ vout, const T* __restrict__ vin,
+                                                   long long n_rows, int heads, int d,
+                                                   const int* __restrict__ gather,
+                                                   const int* __restrict__ pos_from,
+                                                   const int* __restrict__ pos_to, Freqs fr) {
+  const int cpr = d >> 4;  // 8-pair chunks per head vector
+  const long long tid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long long row = tid / cpr;
+  const int c = (int)(tid - row * cpr);
+  if (row >= n_rows) return;
+  const long long src = gather ? (long long)gather[row] : row;
+  const long long delta = (long long)pos_to[row] - (pos_from ? (long long)pos_from[row] : 0LL);
+  float cs[8], sn[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) angle_cs(delta, fr.theta[c * 8 + i], cs[i], sn[i]);
+
+  const long long stride = (long long)heads * d;
+  const T* x = in + src * stride;
+  T* y = out + row * stride;
+  // element offsets of the chunk's two 8-element pieces within a head vector
+  int oa, ob;
+  if (LAYOUT == AKV_ROPE_HALF) { oa = c * 8; ob = (d >> 1) + c * 8; }
+  else { oa = c * 16; ob = c * 16 + 8; }
+  for (int h = 0; h < heads; ++h) {
+    float a[8], b[8], ya[8], yb[8];
+    Vec8<T>::load(x + h * d + oa, a);
+    Vec8<T>::load(x + h * d + ob, b);
+    if (LAYOUT == AKV_ROPE_HALF) {
+      // pair i = (a[i], b[i])
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        ya[i] = a[i] * cs[i] - b[i] * sn[i];
+        yb[i] = a[i] * sn[i] + b[i] * cs[i];
+      }
+    } else {
+      // pairs are adjacent: (a[0],a[1]) .. (a[6],a[7]), (b[0],b[1]) .. (b[6],b[7])
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        ya[2 * i] = a[2 * i] * cs[i] - a[2 * i + 1] * sn[i];
+        ya[2 * i + 1] = a[2 * i] * sn[i] + a[2 * i + 1] * cs[i];
+        yb[2 * i] = b[2 * i] * cs[i + 4] - b[2 * i + 1] * sn[i + 4];
+        yb[2 * i + 1] = b[2 * i] * sn[i + 4] + b[2 * i + 1] * cs[i + 4];
+      }
+    }
+    Vec8<T>::store(y + h * d + oa, ya);
+    Vec8<T>::store(y + h * d + ob, yb);
+    if (vout) {
+      Vec8<T>::copy(vout + row * stride + h * d + oa, vin + src * stride + h * d + oa);
+      Vec8<T>::copy(vout + row * stride + h * d + ob, vin + src * stride + h * d + ob);
+    }
+  }
+}
+
+template <typename T, int LAYOUT>
+void launch_t(const RopeArgs& a, const Freqs& fr, hipStream_t s) {
+  const long long threads = a.n_rows * (a.d / 16);
+  const unsigned blocks = (unsigned)((threads + 255) / 256);
+  hipLaunchKernelGGL((rope_kernel<T, LAYOUT>), dim3(blocks), dim3(256), 0, s, (T*)a.out, (const T*)a.in,
+                     (T*)a.v_out, (const T*)a.v_in, (long long)a.n_rows, a.heads, a.d, a.gather,
+                     a.pos_from, a.pos_to, fr);
+}
+
+}  // namespace
+
+int launch_rope(const RopeArgs& a, void* stream) {
+  Freqs fr;
+  for (int i = 0; i < a.d / 2; ++i) fr.theta[i] = std::pow(a.base, -2.0 * i / a.d);
+  for (int i = a.d / 2; i < 128; ++i) fr.theta[i] = 0.0;
+  const long long threads = a.n_rows * (a.d / 16);
+  if ((threads + 255) / 256 > 0x7fffffffLL) return fail(AKV_EINVAL, "too many rows for one launch");
+  hipStream_t s = (hipStream_t)stream;
+  (void)hipGetLastError();
+  if (a.dtype == AKV_BF16) {
+    if (a.layout == AKV_ROPE_HALF) launch_t<uint16_t, AKV_ROPE_HALF>(a, fr, s);
+    else launch_t<uint16_t, AKV_ROPE_INTERLEAVED>(a, fr, s);
+  } else {
+    if (a.layout == AKV_ROPE_HALF) launch_t<float, AKV_ROPE_HALF>(a, fr, s);
+    else launch_t<float, AKV_ROPE_INTERLEAVED>(a, fr, s);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(AKV_EHIP, std::string("rope launch: ") + hipGetErrorString(e));
+  return AKV_OK;
+}
+
+}  // namespace akv
