@@ -328,3 +328,35 @@ def decode_attention(q, k_pool, v_pool, indptr, indices, max_n: int, out, lse=No
                                      indices.data_ptr(), B, hq, hkv, d, max_n, scale, BF16, out.data_ptr(),
                                      lp, ws.data_ptr(), nbytes, _stream(dev)), "akv_decode_attention")
     return out
+
+
+def restore(plan: Plan, q_raw, k_raw, v, base: float = 150000.0, layout: int = ROPE_HALF,
+            with_lse: bool = False, scale: float = 0.0, bufs: Optional[dict] = None):
+    """Restore prefill: RoPE-apply Q and K to their append positions, build the
+    per-stretch KV versions, run segment attention.  Returns (out, lse or None).
+    `bufs` may hold preallocated q_rot/k_rot/k_ver/v_ver/out/lse tensors."""
+    import torch
+    T, hq, d = q_raw.shape
+    hkv = k_raw.shape[1]
+    dev, dt = q_raw.device, q_raw.dtype
+    nv = int(plan.info["n_versions"])
+    b = {} if bufs is None else bufs
+    qr = b.get("q_rot")
+    qr = torch.empty_like(q_raw) if qr is None else qr
+    kr = b.get("k_rot")
+    kr = torch.empty_like(k_raw) if kr is None else kr
+    kv = b.get("k_ver")
+    kv = torch.empty((nv, hkv, d), dtype=dt, device=dev) if kv is None else kv
+    vv = b.get("v_ver")
+    vv = torch.empty((nv, hkv, d), dtype=dt, device=dev) if vv is None else vv
+    out = b.get("out")
+    out = torch.empty_like(q_raw) if out is None else out
+    lse = b.get("lse")
+    if with_lse and lse is None:
+        lse = torch.empty((T, hq), dtype=torch.float32, device=dev)
+    rope_apply(plan, qr, q_raw, base, layout)
+    rope_apply(plan, kr, k_raw, base, layout)
+    if nv:
+        build_kv_versions(plan, kr, v, kv, vv, base, layout)
+    segment_attention(plan, qr, kr, v, kv, vv, out, lse if with_lse else None, scale)
+    return out, (lse if with_lse else None)

@@ -1,0 +1,346 @@
+"""GPU parity: every libakv kernel against the CPU oracle on the same seeded inputs.
+
+Tolerances (written here, reasoned in the design doc):
+  bf16 attention / decode outputs  max-abs 2e-2
+  fp32 attention                   max-abs 1e-5 (also lse)
+  fp32 repos / RoPE                max-abs 1e-5
+  bf16 repos / RoPE                <= 1 bf16 ulp of the exact value + 1e-6 x |pair| (fp32
+                                   evaluation), and rounding disagreements with the exactly
+                                   rounded value rare (round-to-nearest-even)
+  bf16 versions (two roundings)    |err| <= 2^-7 * |rotated pair|; values bit-exact
+Output buffers start as NaN so unwritten rows fail.
+"""
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from segmented_attention_seq_amd import akv, workload
+from tests.gpu_helpers import (Bf16Rows, as_f64, boundary_rows, dev_int, dev_tensor, host_bf16_bits,
+                               host_f64, nan_like)
+
+pytestmark = pytest.mark.gpu
+BASE = workload.ROPE_BASE
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    print(f"\n[gpu] {torch.cuda.get_device_name(0)} lib={akv.lib_path()}", flush=True)
+
+
+def _ulp_bf16(x):
+    """Spacing of bf16 numbers at |x| (normal range)."""
+    e = np.floor(np.log2(np.maximum(np.abs(x), 2.0 ** -126)))
+    return 2.0 ** (e - 7)
+
+
+def _bf16_rot_bound(exact, layout=akv.ROPE_HALF):
+    """One bf16 ulp of the exact element plus the float32 evaluation error of the
+    rotation (angle ~3e-7 rad after fp64 reduction, products ~1e-7), which scales
+    with the norm of the element's pair, not with the element itself: an element
+    that cancels to ~0 cannot be within one of its own tiny ulps."""
+    if layout == akv.ROPE_HALF:
+        h = exact.shape[-1] // 2
+        pn = np.sqrt(exact[..., :h] ** 2 + exact[..., h:] ** 2)
+        pn = np.concatenate([pn, pn], axis=-1)
+    else:
+        pn = np.sqrt(exact[..., 0::2] ** 2 + exact[..., 1::2] ** 2)
+        pn = np.repeat(pn, 2, axis=-1)
+    return _ulp_bf16(exact) + 1e-6 * pn
+
+
+# ---------------------------------------------------------------- RoPE / repos
+
+@pytest.mark.parametrize("layout", [akv.ROPE_HALF, akv.ROPE_INTERLEAVED])
+def test_repos_fp32_large_shifts(layout):
+    rng = np.random.default_rng(11)
+    rows, n, H, d = 5000, 3000, 8, 64
+    k = rng.standard_normal((rows, H, d)).astype(np.float32)
+    g = rng.integers(0, rows, n).astype(np.int32)
+    pf = rng.integers(0, 1 << 20, n).astype(np.int32)
+    pt = rng.integers(0, 1 << 20, n).astype(np.int32)
+    out = nan_like((n, H, d), torch.float32)
+    akv.rope_repos(out, dev_tensor(k, False), dev_int(pt), dev_int(pf),
+                   dev_int(g), BASE, layout)
+    ref = oracle.repos(k[g], pf, pt, BASE, layout)
+    err = np.abs(host_f64(out) - ref).max()
+    print(f"[repos fp32 layout={layout}] max-abs {err:.2e}")
+    assert err <= 1e-5
+
+
+def test_repos_bf16_one_ulp_and_rne():
+    rng = np.random.default_rng(12)
+    n, H, d = 4000, 8, 64
+    kb = workload.f32_to_bf16_bits(rng.standard_normal((n, H, d)).astype(np.float32))
+    pf = rng.integers(0, 200_000, n).astype(np.int32)
+    pt = rng.integers(0, 100_000, n).astype(np.int32)
+    out = nan_like((n, H, d), torch.bfloat16)
+    akv.rope_repos(out, dev_tensor(kb, True), dev_int(pt), dev_int(pf))
+    exact = oracle.repos(as_f64(kb, True), pf, pt, BASE)
+    ref_bits = oracle.f64_to_bf16_bits(exact)
+    got = host_f64(out)
+    assert np.all(np.abs(got - exact) <= _bf16_rot_bound(exact))
+    mism = np.mean(host_bf16_bits(out) != ref_bits)
+    print(f"[repos bf16] rounding disagreements {mism:.4%}")
+    assert mism < 0.01
+
+
+@pytest.mark.parametrize("bf16", [True, False])
+def test_rope_apply_and_versions(bf16):
+    tr = workload.agent_trajectory(4, seed=21, total=900, keep=2, repos="every",
+                                   user_len=50, assist_range=(20, 90), tool_range=(60, 200))
+    plan = akv.build_visibility(akv.ops_from_messages(tr.msg_len, tr.drop, tr.reposition))
+    t = plan.tables()
+    T, H, d = tr.n_tokens, 8, 64
+    _, k, v = workload.prefill_tensors(T, 1, H, d, seed=22, bf16=bf16)
+    kd, vd = dev_tensor(k, bf16), dev_tensor(v, bf16)
+    kr = torch.empty_like(kd)
+    akv.rope_apply(plan, kr, kd)
+    kexact = oracle.rope(as_f64(k, bf16), t["tok_pos"], BASE)
+    nv = plan.info["n_versions"]
+    assert nv > 0
+    kv, vv = nan_like((nv, H, d), kd.dtype), nan_like((nv, H, d), kd.dtype)
+    akv.build_kv_versions(plan, kr, vd, kv, vv)
+    src, to = t["versions"][:, 0], t["versions"][:, 2]
+    vexact = oracle.rope(as_f64(k, bf16)[src], to, BASE)
+    if bf16:
+        assert np.all(np.abs(host_f64(kr) - kexact) <= _bf16_rot_bound(kexact))
+        # versions round twice (append position, then the repos shift)
+        pair = np.sqrt(vexact[..., :32] ** 2 + vexact[..., 32:] ** 2)
+        bound = 2.0 ** -7 * np.concatenate([pair, pair], axis=-1) + 1e-30
+        assert np.all(np.abs(host_f64(kv) - vexact) <= bound)
+        assert np.array_equal(host_bf16_bits(vv), v[src])
+    else:
+        assert np.abs(host_f64(kr) - kexact).max() <= 1e-5
+        assert np.abs(host_f64(kv) - vexact).max() <= 1e-5
+        assert np.array_equal(vv.cpu().numpy(), v[src])
+
+
+def test_repos_workload_96k_keys():
+    """Batched repos of 96,000 surviving keys (gathered from a pool with NaN holes)."""
+    for bf16 in (True, False):
+        rb = workload.repos_batch(bf16=bf16)
+        dt = torch.bfloat16 if bf16 else torch.float32
+        pool = nan_like((rb.pool_slots, rb.hkv, rb.d), dt)
+        pool[torch.from_numpy(rb.slots.astype(np.int64)).cuda()] = dev_tensor(rb.k_rows, bf16)
+        out = nan_like((rb.slots.size, rb.hkv, rb.d), dt)
+        akv.rope_repos(out, pool, dev_int(rb.pos_to), dev_int(rb.pos_from),
+                       dev_int(rb.slots))
+        exact = oracle.repos(as_f64(rb.k_rows, bf16), rb.pos_from, rb.pos_to, BASE)
+        got = host_f64(out)
+        if bf16:
+            assert np.all(np.abs(got - exact) <= _bf16_rot_bound(exact))
+        else:
+            err = np.abs(got - exact).max()
+            print(f"[repos 96k fp32] max-abs {err:.2e}")
+            assert err <= 1e-5
+
+
+# ---------------------------------------------------------------- segment attention
+
+def _run_restore(tr, hq, hkv, d, bf16, seed, layout=akv.ROPE_HALF, lse=True):
+    plan = akv.build_visibility(akv.ops_from_messages(tr.msg_len, tr.drop, tr.reposition))
+    q, k, v = workload.prefill_tensors(tr.n_tokens, hq, hkv, d, seed=seed, bf16=bf16)
+    dt = torch.bfloat16 if bf16 else torch.float32
+    T = tr.n_tokens
+    bufs = {"out": nan_like((T, hq, d), dt), "lse": nan_like((T, hq), torch.float32)}
+    out, l = akv.restore(plan, dev_tensor(q, bf16), dev_tensor(k, bf16), dev_tensor(v, bf16),
+                         BASE, layout, with_lse=lse, bufs=bufs)
+    torch.cuda.synchronize()
+    return plan, (q, k, v), out, l
+
+
+def _check_rows(tr, qkv, out, lse, bf16, rows=None, layout=akv.ROPE_HALF, tol=None):
+    q, k, v = qkv
+    ops = oracle.canonical_ops(tr.msg_len, tr.drop, tr.reposition)
+    view = (lambda a: Bf16Rows(a)) if bf16 else (lambda a: a)
+    o_ref, l_ref = oracle.segment_attention(view(q), view(k), view(v), ops, base=BASE, layout=layout,
+                                            rows=rows)
+    sel = np.arange(tr.n_tokens) if rows is None else rows
+    got = host_f64(out[torch.from_numpy(sel).cuda()]) if rows is not None else host_f64(out)
+    err = np.abs(got - o_ref[sel]).max()
+    lerr = np.abs(host_f64(lse)[sel] - l_ref[sel]).max()
+    tol = tol if tol is not None else (2e-2 if bf16 else 1e-5)
+    print(f"[attn {tr.name or 'traj'} bf16={bf16} rows={sel.size}] max-abs {err:.3e} lse {lerr:.3e}")
+    assert np.isfinite(got).all()
+    assert err <= tol
+    assert lerr <= (2e-2 if bf16 else 1e-5)
+
+
+def test_tiny_request_example_fp32():
+    tr = workload.config_trajectory(1)
+    plan, qkv, out, lse = _run_restore(tr, 1, 1, 64, bf16=False, seed=1)
+    _check_rows(tr, qkv, out, lse, bf16=False)
+
+
+@pytest.mark.parametrize("seed", [31, 32, 33])
+def test_random_small_fp32(seed):
+    tr = workload.agent_trajectory(5, seed=seed, total=700, keep=2, repos="every" if seed % 2 else "none",
+                                   user_len=30, assist_range=(10, 60), tool_range=(40, 150))
+    plan, qkv, out, lse = _run_restore(tr, 4, 2, 64, bf16=False, seed=seed)
+    _check_rows(tr, qkv, out, lse, bf16=False)
+
+
+SMALL = [
+    # rounds, total, keep, repos, hq, hkv
+    (3, 1500, 1, "every", 64, 8),
+    (6, 2300, 2, "none", 64, 8),
+    (8, 3100, 3, "every", 16, 4),
+    (5, 1234, 1, "every", 8, 8),
+    (4, 999, 2, "every", 16, 8),
+]
+
+
+@pytest.mark.parametrize("case", range(len(SMALL)))
+def test_random_small_bf16(case):
+    rounds, total, keep, repos, hq, hkv = SMALL[case]
+    tr = workload.agent_trajectory(rounds, seed=40 + case, total=total, keep=keep, repos=repos,
+                                   user_len=64, assist_range=(30, 200), tool_range=(100, 500),
+                                   name=f"small{case}")
+    plan, qkv, out, lse = _run_restore(tr, hq, hkv, 64, bf16=True, seed=50 + case)
+    _check_rows(tr, qkv, out, lse, bf16=True)
+
+
+def test_interleaved_layout_bf16():
+    tr = workload.agent_trajectory(3, seed=61, total=800, keep=1, repos="every", user_len=40,
+                                   assist_range=(30, 100), tool_range=(100, 300))
+    plan, qkv, out, lse = _run_restore(tr, 16, 2, 64, bf16=True, seed=62, layout=akv.ROPE_INTERLEAVED)
+    _check_rows(tr, qkv, out, lse, bf16=True, layout=akv.ROPE_INTERLEAVED)
+
+
+EDGE = {
+    "single-token-messages": workload.Trajectory([1] * 9, ["x"] * 9, {3: [0, 1], 6: [2, 4]}, [3, 6, 8]),
+    "drop-everything": workload.Trajectory([70, 5, 80], ["x"] * 3, {0: [0], 1: [1]}, [1]),
+    "zero-length-and-repeats": workload.Trajectory([65, 0, 0, 130, 1], ["x"] * 5,
+                                                   {1: [0, 0], 2: [1], 3: [0]}, [1, 2, 2, 3]),
+    "final-boundary-only": workload.Trajectory([100, 29], ["x"] * 2, {1: [0, 1]}, [1]),
+    "no-ops": workload.Trajectory([129, 64, 63], ["x"] * 3, {}, []),
+}
+
+
+@pytest.mark.parametrize("name", sorted(EDGE))
+def test_edge_cases_bf16(name):
+    tr = EDGE[name]
+    tr.name = name
+    plan, qkv, out, lse = _run_restore(tr, 16, 2, 64, bf16=True, seed=71)
+    _check_rows(tr, qkv, out, lse, bf16=True)
+
+
+def test_empty_plan_and_unsupported():
+    plan = akv.build_visibility([])
+    x = torch.empty((0, 8, 64), dtype=torch.bfloat16, device="cuda")
+    akv.segment_attention(plan, torch.empty((0, 64, 64), dtype=torch.bfloat16, device="cuda"), x, x, None,
+                          None, torch.empty((0, 64, 64), dtype=torch.bfloat16, device="cuda"))
+    p16 = akv.build_visibility([(akv.OP_APPEND, 10)], bq=16, bk=16)
+    q = torch.zeros((10, 8, 64), dtype=torch.bfloat16, device="cuda")
+    kv = torch.zeros((10, 1, 64), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(akv.AkvError) as e:
+        akv.segment_attention(p16, q, kv, kv, None, None, torch.empty_like(q))
+    assert e.value.status == akv.EUNSUPPORTED
+    p = akv.build_visibility([(akv.OP_APPEND, 10)])
+    q3 = torch.zeros((10, 3, 64), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(akv.AkvError) as e:
+        akv.segment_attention(p, q3, kv, kv, None, None, torch.empty_like(q3))
+    assert e.value.status == akv.EUNSUPPORTED
+
+
+def test_deterministic():
+    tr = workload.agent_trajectory(3, seed=81, total=1500, keep=1, repos="every", user_len=64,
+                                   assist_range=(30, 200), tool_range=(100, 500))
+    _, _, a, la = _run_restore(tr, 64, 8, 64, bf16=True, seed=82)
+    _, _, b, lb = _run_restore(tr, 64, 8, 64, bf16=True, seed=82)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16)) and torch.equal(la, lb)
+
+
+@functools.lru_cache(maxsize=1)
+def _workload(cfg):
+    return workload.config_prefill(cfg)
+
+
+@pytest.mark.parametrize("cfg,n_random", [(2, 192), (3, 48), (4, 32)])
+def test_workloads_full_size_sampled(cfg, n_random):
+    """The three prefill workloads at full size (the launch bench.py times); the
+    oracle checks every row next to a segment/stretch boundary plus seeded rows."""
+    tr, q, k, v = _workload(cfg)
+    print(f"[cfg{cfg}] T={tr.n_tokens}", flush=True)
+    plan = akv.build_visibility(akv.ops_from_messages(tr.msg_len, tr.drop, tr.reposition))
+    T, hq, d = q.shape
+    bufs = {"out": nan_like((T, hq, d), torch.bfloat16), "lse": nan_like((T, hq), torch.float32)}
+    out, lse = akv.restore(plan, dev_tensor(q, True), dev_tensor(k, True), dev_tensor(v, True), BASE,
+                           with_lse=True, bufs=bufs)
+    torch.cuda.synchronize()
+    assert not torch.isnan(out).any().item()
+    rng = np.random.default_rng(cfg)
+    rows = boundary_rows(plan.tables(), T, rng, n_random, edge=1 if cfg == 4 else 2)
+    if cfg == 4:   # keep the oracle's per-stretch key rotation bounded
+        rows = rows[rng.choice(rows.size, size=min(rows.size, 160), replace=False)]
+        rows.sort()
+    _check_rows(tr, (q, k, v), out, lse, bf16=True, rows=rows)
+
+
+# ---------------------------------------------------------------- decode
+
+def _decode_case(batch, lo, hi, seed, hq=64, hkv=8, shuffle=False):
+    db = workload.decode_batch(batch=batch, lo=lo, hi=hi, seed=seed, hq=hq, hkv=hkv, shuffle_slots=shuffle)
+    pool_k = nan_like((db.pool_slots, hkv, db.d), torch.bfloat16)
+    pool_v = nan_like((db.pool_slots, hkv, db.d), torch.bfloat16)
+    idx = torch.from_numpy(db.indices.astype(np.int64)).cuda()
+    pool_k[idx] = dev_tensor(db.k_rows, True)
+    pool_v[idx] = dev_tensor(db.v_rows, True)
+    out = nan_like((batch, hq, db.d), torch.bfloat16)
+    lse = nan_like((batch, hq), torch.float32)
+    max_n = int(np.diff(db.indptr).max())
+    akv.decode_attention(dev_tensor(db.q, True), pool_k, pool_v, dev_int(db.indptr),
+                         dev_int(db.indices), max_n, out, lse)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.decode(Bf16Rows(db.q)[:], Bf16Rows(db.k_rows), Bf16Rows(db.v_rows), db.indptr)
+    err = np.abs(host_f64(out) - o_ref).max()
+    lerr = np.abs(host_f64(lse) - l_ref).max()
+    print(f"[decode batch={batch} n=[{lo},{hi}) hq={hq}/{hkv} shuffle={shuffle}] max-abs {err:.3e} lse {lerr:.3e}")
+    assert err <= 2e-2 and lerr <= 2e-2
+
+
+@pytest.mark.parametrize("args", [(5, 1, 40, 91, 64, 8), (7, 900, 5000, 92, 64, 8),
+                                  (3, 2000, 3000, 93, 16, 4), (4, 1, 3000, 94, 8, 8)])
+def test_decode_small(args):
+    b, lo, hi, seed, hq, hkv = args
+    _decode_case(b, lo, hi, seed, hq, hkv)
+
+
+def test_decode_workload_batch14():
+    _decode_case(14, 32_000, 96_001, 1005)
+
+
+def test_decode_workload_shuffled_slots():
+    _decode_case(6, 32_000, 96_001, 1006, shuffle=True)
+
+
+def test_decode_equals_last_prefill_row():
+    """Decode of the next token = the last row of a restore over the extended sequence."""
+    tr = workload.agent_trajectory(4, seed=101, total=2000, keep=2, repos="every", user_len=64,
+                                   assist_range=(30, 200), tool_range=(100, 500))
+    ext = workload.Trajectory(tr.msg_len + [1], tr.roles + ["x"], tr.drop, tr.reposition)
+    plan, (q, k, v), out, _ = _run_restore(ext, 64, 8, 64, bf16=True, seed=102)
+    T = ext.n_tokens
+    # decode inputs: rotated q of the new token and the final state's keys, from the GPU restore
+    ops = akv.ops_from_messages(tr.msg_len, tr.drop, tr.reposition)
+    p0 = akv.build_visibility(ops)
+    t0 = p0.tables()
+    act = t0["final_tok"]
+    pos_all = np.concatenate([t0["final_pos"], [p0.info["p_next"]]]).astype(np.int32)
+    rows = np.concatenate([act, [T - 1]]).astype(np.int32)
+    kd, qd = dev_tensor(k, True), dev_tensor(q, True)
+    kfin = torch.empty((rows.size, 8, 64), dtype=torch.bfloat16, device="cuda")
+    akv.rope_repos(kfin, kd, dev_int(pos_all), None, dev_int(rows))
+    qn = torch.empty((1, 64, 64), dtype=torch.bfloat16, device="cuda")
+    akv.rope_repos(qn, qd, dev_int(np.array([p0.info["p_next"]], np.int32)), None,
+                   dev_int(np.array([T - 1], np.int32)))
+    vfin = dev_tensor(v, True)[torch.from_numpy(rows.astype(np.int64)).cuda()].contiguous()
+    o = torch.empty((1, 64, 64), dtype=torch.bfloat16, device="cuda")
+    akv.decode_attention(qn, kfin, vfin, torch.tensor([0, rows.size], dtype=torch.int32, device="cuda"),
+                         torch.arange(rows.size, dtype=torch.int32, device="cuda"), rows.size, o)
+    assert (o[0].float() - out[T - 1].float()).abs().max().item() <= 2e-2
