@@ -1,0 +1,284 @@
+"""Benchmark of the AKV restore hot path on one MI355X.
+
+One step = one pass over every stage of the path on synthetic agent inputs:
+  A1  host: operate-after request -> canonical ops -> restore plan; upload
+  A2  RoPE-apply of the raw Q and K to their append positions
+  A3  KV versions of every repos stretch (rotated keys + copied values)
+  A4  segment-batch attention (bf16 MFMA)
+  A5  batched repos of 96,000 surviving keys (gathered, p -> q)
+  A6  decode: 14 requests x 1 query over 32k-96k gathered active keys each
+The restore stages run on the 48k-token, 20-round trajectory with tool-response
+rolling drop (64/8 GQA heads, d = 64, bf16) unless --config picks another.
+
+Prints one JSON line.  `value` = algorithmic attention FLOP of the restore
+(4 * d * Hq * visible pairs) per step / wall time per step (all stages included).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "segment-attn restore TFLOP/s (% MFMA peak); repos+decode HBM GB/s (% peak)"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+ATTN_SRC = os.path.join(ROOT, "segmented_attention_seq_amd", "csrc", "attention.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "segment_attention_48k_traffic.md")
+
+
+def parse_args():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4],
+                    help="restore workload: 2 = 48k/20 rounds, 3 = ~300k/100 rounds with 96k repos "
+                         "window, 4 = 192k/200 rounds with repos every round")
+    ap.add_argument("--repos-sets", type=int, default=4, help="repos buffer sets rotated per step")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--only", default="", help="comma list of stages to run (profiling aid): "
+                                               "restore,repos,decode")
+    return ap.parse_args()
+
+
+def attn_src_hash():
+    with open(ATTN_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic(cfg):
+    """HBM bytes per segment-attention launch measured with rocprofv3 counters, if
+    the file was taken on this exact kernel source and workload; else None."""
+    if cfg != 2 or not os.path.exists(TRAFFIC_FILE):
+        return None
+    txt = open(TRAFFIC_FILE).read()
+    h = re.search(r"kernel source sha256\[:16\]:\s*([0-9a-f]{16})", txt)
+    b = re.search(r"HBM bytes per launch \(scaled\):\s*([0-9.e+]+)", txt)
+    if not h or not b or h.group(1) != attn_src_hash():
+        return None
+    return float(b.group(1))
+
+
+class _Bf16Rows:
+    """Decode rows of a bf16-bits array to float64 on indexing (the oracle reads a
+    few rows of a multi-hundred-MB input)."""
+
+    def __init__(self, bits):
+        self.bits, self.shape = bits, bits.shape
+
+    def __getitem__(self, idx):
+        from segmented_attention_seq_amd.workload import bf16_bits_to_f32
+        return bf16_bits_to_f32(self.bits[idx]).astype(np.float64)
+
+
+def cpu_baseline(tr, q, k, v, target_s):
+    """Time the CPU oracle (as it stands) on a seeded sample of query rows of the
+    same restore workload; report its rate in the metric's unit."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count()
+    ops = oracle.canonical_ops(tr.msg_len, tr.drop, tr.reposition)
+    ev = oracle.replay_events(ops)
+    ep = ev.epoch_of_token()
+    T, hq, d = q.shape
+    order = np.random.default_rng(12345).permutation(T)
+    n, done, secs, flop = 64, 0, 0.0, 0.0
+    while secs < target_s and done < T:
+        rows = np.sort(order[done:done + n])
+        t0 = time.perf_counter()
+        oracle.segment_attention(_Bf16Rows(q), _Bf16Rows(k), _Bf16Rows(v), ev=ev, rows=rows,
+                                 base=150000.0)
+        secs += time.perf_counter() - t0
+        for i in rows:   # keys row i attends to: version rows and own tokens j <= i not yet dropped
+            tb, te, src = ev.epochs[ep[i]]
+            nvis = int((ev.tok_drop[src] > i).sum() + (ev.tok_drop[tb:i + 1] > i).sum())
+            flop += 4.0 * d * hq * nvis
+        done += rows.size
+        n = int(min(4 * n, max(64, n * (target_s - secs) / max(secs, 1e-3))))
+    return {"value": flop / secs / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{done} random query rows (all {hq} heads) of the restore workload, float64 "
+                      f"NumPy oracle, {secs:.1f} s"}
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the per-GPU shard design is in DESIGN.md", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from segmented_attention_seq_amd import akv, workload
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    only = set(args.only.split(",")) if args.only else {"restore", "repos", "decode"}
+
+    def t_bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    # ---------------- inputs (resident in HBM before timing)
+    tr, q, k, v = workload.config_prefill(args.config)
+    T, hq, d = q.shape
+    hkv = k.shape[1]
+    qd, kd, vd = t_bf16(q), t_bf16(k), t_bf16(v)
+    req_ops = (tr.msg_len, tr.drop, tr.reposition)
+    plan0 = akv.build_visibility(akv.ops_from_messages(*req_ops))
+    nv = int(plan0.info["n_versions"])
+    pairs = int(plan0.info["visible_pairs"])
+    attn_flop = 4.0 * d * hq * pairs
+    bufs = {"q_rot": torch.empty_like(qd), "k_rot": torch.empty_like(kd),
+            "k_ver": torch.empty((nv, hkv, d), dtype=torch.bfloat16, device=dev),
+            "v_ver": torch.empty((nv, hkv, d), dtype=torch.bfloat16, device=dev),
+            "out": torch.empty_like(qd)}
+    dev_plans = [torch.empty(1 << 20, dtype=torch.uint8, device=dev) for _ in range(2)]
+
+    rb = workload.repos_batch()
+    nrep = rb.slots.size
+    repos_sets = []
+    for s in range(args.repos_sets):
+        pool = torch.zeros((rb.pool_slots, rb.hkv, rb.d), dtype=torch.bfloat16, device=dev)
+        pool[torch.from_numpy(rb.slots.astype(np.int64)).to(dev)] = t_bf16(rb.k_rows)
+        repos_sets.append((pool, torch.empty((nrep, rb.hkv, rb.d), dtype=torch.bfloat16, device=dev)))
+    r_from = torch.from_numpy(rb.pos_from).to(dev)
+    r_to = torch.from_numpy(rb.pos_to).to(dev)
+    r_idx = torch.from_numpy(rb.slots).to(dev)
+    repos_bytes = nrep * rb.hkv * rb.d * 2 * 2 + 12 * nrep
+
+    db = workload.decode_batch()
+    pool_k = torch.zeros((db.pool_slots, db.hkv, db.d), dtype=torch.bfloat16, device=dev)
+    pool_v = torch.zeros_like(pool_k)
+    didx = torch.from_numpy(db.indices.astype(np.int64)).to(dev)
+    pool_k[didx] = t_bf16(db.k_rows)
+    pool_v[didx] = t_bf16(db.v_rows)
+    dq = t_bf16(db.q)
+    d_indptr = torch.from_numpy(db.indptr).to(dev)
+    d_indices = torch.from_numpy(db.indices).to(dev)
+    max_n = int(np.diff(db.indptr).max())
+    n_keys = int(db.indptr[-1])
+    dout = torch.empty((db.q.shape[0], db.hq, db.d), dtype=torch.bfloat16, device=dev)
+    dws = torch.empty(akv.decode_workspace_bytes(db.q.shape[0], db.hq, db.hkv, db.d, max_n),
+                      dtype=torch.uint8, device=dev)
+    decode_bytes = n_keys * db.hkv * db.d * 2 * 2 + 4 * n_keys + 2 * dq.numel() * 2
+    torch.cuda.synchronize()
+
+    ev_names = ["rope", "versions", "attn", "repos", "decode"]
+    stage_ms = {n: [] for n in ev_names}
+    host_ms = []
+    keep_plans = []
+
+    def step(i, timed):
+        t0 = time.perf_counter()
+        ev = {}
+        if "restore" in only:
+            plan = akv.build_visibility(akv.ops_from_messages(*req_ops))
+            buf = dev_plans[i % 2]
+            if buf.numel() < plan.info["device_bytes"]:
+                buf = dev_plans[i % 2] = torch.empty(int(plan.info["device_bytes"]), dtype=torch.uint8,
+                                                     device=dev)
+            akv._check(akv._lib.akv_plan_upload(plan.handle, buf.data_ptr(), buf.numel(), akv._stream(dev)),
+                       "akv_plan_upload")
+            plan._dev[str(dev)] = buf
+            keep_plans.append(plan)
+            del keep_plans[:-3]      # host images stay alive until their copies ran
+            host_ms.append((time.perf_counter() - t0) * 1e3)
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            e[0].record()
+            akv.rope_apply(plan, bufs["q_rot"], qd)
+            akv.rope_apply(plan, bufs["k_rot"], kd)
+            e[1].record()
+            if nv:
+                akv.build_kv_versions(plan, bufs["k_rot"], vd, bufs["k_ver"], bufs["v_ver"])
+            e[2].record()
+            akv.segment_attention(plan, bufs["q_rot"], bufs["k_rot"], vd, bufs["k_ver"], bufs["v_ver"],
+                                  bufs["out"])
+            e[3].record()
+            ev.update(rope=(e[0], e[1]), versions=(e[1], e[2]), attn=(e[2], e[3]))
+        if "repos" in only:
+            pool, out = repos_sets[i % len(repos_sets)]
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            e[0].record()
+            akv.rope_repos(out, pool, r_to, r_from, r_idx)
+            e[1].record()
+            ev["repos"] = (e[0], e[1])
+        if "decode" in only:
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            e[0].record()
+            akv.decode_attention(dq, pool_k, pool_v, d_indptr, d_indices, max_n, dout, ws=dws)
+            e[1].record()
+            ev["decode"] = (e[0], e[1])
+        return ev
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    pending = []
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        pending.append(step(args.warmup + i, True))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    for evs in pending:
+        for n, (a, b) in evs.items():
+            stage_ms[n].append(a.elapsed_time(b))
+    ms_per_step = wall * 1e3 / args.steps
+    avg = {n: (float(np.mean(v)) if v else None) for n, v in stage_ms.items()}
+
+    value = attn_flop / (ms_per_step * 1e-3) / 1e12 if "restore" in only else 0.0
+    attn_tflops = attn_flop / (avg["attn"] * 1e-3) / 1e12 if avg["attn"] else None
+    traffic = read_traffic(args.config)
+    comps = {"host_plan_ms": float(np.mean(host_ms)) if host_ms else None}
+    for n in ev_names:
+        comps[f"{n}_ms"] = avg[n]
+    if avg["repos"]:
+        gbs = repos_bytes / (avg["repos"] * 1e-3) / 1e9
+        comps["repos"] = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                          "frac": gbs / PEAK_HBM_GBS, "bytes_per_launch": repos_bytes, "keys": nrep}
+    if avg["decode"]:
+        gbs = decode_bytes / (avg["decode"] * 1e-3) / 1e9
+        comps["decode"] = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                           "frac": gbs / PEAK_HBM_GBS, "bytes_per_launch": decode_bytes,
+                           "gathered_keys": n_keys, "requests": int(db.q.shape[0])}
+    if avg["rope"]:
+        rope_bytes = 2 * (qd.numel() + kd.numel()) * 2 + 8 * T
+        comps["rope_apply_gbs"] = rope_bytes / (avg["rope"] * 1e-3) / 1e9
+    if avg["versions"] and nv:
+        comps["versions_gbs"] = (nv * hkv * d * 2 * 4 + 12 * nv) / (avg["versions"] * 1e-3) / 1e9
+
+    workload_name = {2: "48k-token 20-round agent trajectory, rolling drop keep 12 (8 drops)",
+                     3: "300,200-token 100-round trajectory, keep 12 + repos at the 96k position window",
+                     4: "192k-token 200-round trajectory, keep 12 + repos every round"}[args.config]
+    line = {
+        "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"restore of a {workload_name} (64/8 GQA heads, d=64, RoPE base 150000) "
+                               f"+ batched repos of {nrep} keys + decode of {db.q.shape[0]} requests over "
+                               f"{n_keys} gathered keys", "restore_tokens": T, "visible_pairs": pairs,
+                   "attn_flop_per_step": attn_flop, "version_rows": nv,
+                   "stages": sorted(only)},
+        "roofline": {"bound": "mfma", "kernel": "segment attention (seg_attn_bf16)",
+                     "achieved": attn_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": (attn_tflops / PEAK_BF16_TFLOPS) if attn_tflops else None,
+                     "traffic": traffic},
+        "components": comps,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline and "restore" in only:
+        line["cpu_baseline"] = cpu_baseline(tr, q, k, v, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
