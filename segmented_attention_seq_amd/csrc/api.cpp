@@ -112,7 +112,7 @@ int akv_plan_info_get(const akv_plan* p, akv_plan_info* info) {
   info->p_next = p->p_next;
   info->bq = p->bq;
   info->bk = p->bk;
-  info->device_bytes = p->image.size();
+  info->device_bytes = p->image_bytes;
   return AKV_OK;
 }
 
@@ -134,8 +134,8 @@ int akv_plan_tables_get(const akv_plan* p, akv_plan_tables* v) {
 
 int akv_plan_upload(const akv_plan* p, void* dev, uint64_t dev_bytes, akv_stream_t stream) {
   if (!p || !dev) return fail(AKV_EINVAL, "NULL plan or device buffer");
-  if (dev_bytes < p->image.size()) return fail(AKV_EINVAL, "device buffer smaller than the plan image");
-  hipError_t e = hipMemcpyAsync(dev, p->image.data(), p->image.size(), hipMemcpyHostToDevice,
+  if (dev_bytes < p->image_bytes) return fail(AKV_EINVAL, "device buffer smaller than the plan image");
+  hipError_t e = hipMemcpyAsync(dev, p->image.get(), p->image_bytes, hipMemcpyHostToDevice,
                                 (hipStream_t)stream);
   if (e != hipSuccess) return fail(AKV_EHIP, std::string("plan upload: ") + hipGetErrorString(e));
   return AKV_OK;
@@ -161,7 +161,7 @@ int akv_rope_repos(void* out, const void* in, int dtype, int64_t n_rows, int32_t
   if (n_rows == 0) return AKV_OK;
   if (!out || !in || !pos_to) return fail(AKV_EINVAL, "NULL out, in or pos_to");
   if (gather && out == in) return fail(AKV_EINVAL, "in-place rotation cannot gather");
-  akv::RopeArgs a{out, in, nullptr, nullptr, n_rows, heads, d, gather, pos_from, pos_to,
+  akv::RopeArgs a{out, in, nullptr, nullptr, n_rows, heads, d, gather, pos_from, false, pos_to,
                   rope_base, rope_layout, dtype};
   return akv::launch_rope(a, stream);
 }
@@ -174,7 +174,7 @@ int akv_rope_apply(const akv_plan* p, const void* dev_plan, void* out, const voi
   if (p->T == 0) return AKV_OK;
   if (!out || !in) return fail(AKV_EINVAL, "NULL out or in");
   const auto* base = (const uint8_t*)dev_plan;
-  akv::RopeArgs a{out, in, nullptr, nullptr, p->T, heads, d, nullptr, nullptr,
+  akv::RopeArgs a{out, in, nullptr, nullptr, p->T, heads, d, nullptr, nullptr, false,
                   (const int32_t*)(base + p->off_tok_pos), rope_base, rope_layout, dtype};
   return akv::launch_rope(a, stream);
 }
@@ -190,7 +190,7 @@ int akv_build_kv_versions(const akv_plan* p, const void* dev_plan, const void* k
   if (!k || !v || !k_ver || !v_ver) return fail(AKV_EINVAL, "NULL k, v, k_ver or v_ver");
   const auto* base = (const uint8_t*)dev_plan;
   akv::RopeArgs a{k_ver, k, v_ver, v, nv, hkv, d, (const int32_t*)(base + p->off_ver_src),
-                  (const int32_t*)(base + p->off_ver_from), (const int32_t*)(base + p->off_ver_to),
+                  (const int32_t*)(base + p->off_tok_pos), true, (const int32_t*)(base + p->off_ver_to),
                   rope_base, rope_layout, dtype};
   return akv::launch_rope(a, stream);
 }
@@ -220,7 +220,7 @@ int akv_segment_attention(const akv_plan* p, const void* dev_plan, const void* q
   akv::AttnArgs a{q, k, v, k_ver, v_ver, out, lse,
                   (const int32_t*)(base + p->off_item_desc), (const int32_t*)(base + p->off_tiles),
                   (const int32_t*)(base + p->off_order), (const int32_t*)(base + p->off_tok_drop),
-                  (const int32_t*)(base + p->off_ver_drop), (int64_t)p->items.size() / 2,
+                  (const int32_t*)(base + p->off_ver_src), (int64_t)p->items.size() / 2,
                   hq, hkv, d, p->bq, p->bk, scale, dtype};
   return akv::launch_segment_attention(a, stream);
 }

@@ -61,16 +61,43 @@ __device__ __forceinline__ bf16x8 cat4(s16x4 a, s16x4 b) {
   return __builtin_bit_cast(bf16x8, v);
 }
 
+// Running-max slack (log2 units): the accumulators are rescaled only when a new
+// score exceeds the running max by more than this, so exp2 arguments stay <= 8
+// (p <= 256, exact in fp32, no bf16 overflow) and most tiles skip the rescale.
+constexpr float kRescaleSlack = 8.0f;
+
+struct TileSrc {
+  const uint16_t* k;
+  const uint16_t* v;
+  int row0, nrows;
+  bool ver;
+};
+
+__device__ __forceinline__ TileSrc tile_src(int ent, int nvt, int voff, int r, int tb, int te,
+                                            const uint16_t* k, const uint16_t* v,
+                                            const uint16_t* kver, const uint16_t* vver) {
+  const int kt = ent >> 2;
+  TileSrc ts;
+  ts.ver = kt < nvt;
+  ts.row0 = ts.ver ? voff + kt * BK : tb + (kt - nvt) * BK;
+  ts.nrows = ts.ver ? min(BK, r - kt * BK) : min(BK, te - ts.row0);
+  ts.k = ts.ver ? kver : k;
+  ts.v = ts.ver ? vver : v;
+  return ts;
+}
+
 template <int GROUP>
 __global__ __launch_bounds__(64 * GROUP) void seg_attn_bf16(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ kver, const uint16_t* __restrict__ vver,
     const int* __restrict__ item_desc, const int* __restrict__ tiles, const int* __restrict__ order,
-    const int* __restrict__ tok_drop, const int* __restrict__ ver_drop, uint16_t* __restrict__ out,
+    const int* __restrict__ tok_drop, const int* __restrict__ ver_src, uint16_t* __restrict__ out,
     float* __restrict__ lse, int hq, int hkv, float scale) {
-  __shared__ __attribute__((aligned(16))) uint16_t lk[BK * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t lv[BK * VP];
-  __shared__ int mtok[BK], mdrop[BK];
+  constexpr int NT = 64 * GROUP;            // threads
+  constexpr int CPT = (BK * 8 + NT - 1) / NT;  // 16-byte K (and V) chunks per thread per tile
+  __shared__ __attribute__((aligned(16))) uint16_t lk[2][BK * KP];
+  __shared__ __attribute__((aligned(16))) uint16_t lv[2][BK * VP];
+  __shared__ int mtok[2][BK], mdrop[2][BK];
 
   const int hk = blockIdx.x % hkv;
   const int item = order[blockIdx.x / hkv];
@@ -97,6 +124,49 @@ __global__ __launch_bounds__(64 * GROUP) void seg_attn_bf16(
     }
   }
 
+  // global -> register staging of one K/V tile (+ mask metadata), then -> LDS buffer
+  uint4 kx[CPT], vx[CPT];
+  int mt = INT_MAX, md = INT_MIN;
+  auto fetch = [&](int ent) {
+    const TileSrc ts = tile_src(ent, nvt, voff, r, tb, te, k, v, kver, vver);
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      const int c = threadIdx.x + j * NT;
+      const int key = c >> 3, ch = c & 7;
+      kx[j] = make_uint4(0, 0, 0, 0);
+      vx[j] = make_uint4(0, 0, 0, 0);
+      if (c < BK * 8 && key < ts.nrows) {
+        const long long off = ((long long)(ts.row0 + key) * hkv + hk) * D + ch * 8;
+        kx[j] = *(const uint4*)(ts.k + off);
+        vx[j] = *(const uint4*)(ts.v + off);
+      }
+    }
+    if ((ent & 3) == AKV_TILE_PARTIAL && threadIdx.x < BK) {
+      const int key = threadIdx.x;
+      mt = INT_MAX;
+      md = INT_MIN;
+      if (key < ts.nrows) {
+        mt = ts.ver ? -1 : ts.row0 + key;
+        md = tok_drop[ts.ver ? ver_src[ts.row0 + key] : ts.row0 + key];
+      }
+    }
+  };
+  auto stash = [&](int buf, int ent) {
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      const int c = threadIdx.x + j * NT;
+      if (c < BK * 8) {
+        const int key = c >> 3, ch = c & 7;
+        *(uint4*)(&lk[buf][key * KP + ch * 8]) = kx[j];
+        *(uint4*)(&lv[buf][key * VP + ch * 8]) = vx[j];
+      }
+    }
+    if ((ent & 3) == AKV_TILE_PARTIAL && threadIdx.x < BK) {
+      mtok[buf][threadIdx.x] = mt;
+      mdrop[buf][threadIdx.x] = md;
+    }
+  };
+
   f32x16 o[2][2];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb)
@@ -104,42 +174,24 @@ __global__ __launch_bounds__(64 * GROUP) void seg_attn_bf16(
     for (int db = 0; db < 2; ++db)
 #pragma unroll
       for (int i = 0; i < 16; ++i) o[qb][db][i] = 0.f;
-  float mrun[2] = {-INFINITY, -INFINITY}, lrun[2] = {0.f, 0.f};
+  float ms[2] = {-INFINITY, -INFINITY};  // running max, already scaled to log2 units
+  float lrun[2] = {0.f, 0.f};
+
+  if (t0 < t1) {
+    fetch(tiles[t0]);
+    stash(0, tiles[t0]);
+  }
+  __syncthreads();
 
   for (int t = t0; t < t1; ++t) {
+    const int buf = (t - t0) & 1;
     const int ent = tiles[t];
-    const int kt = ent >> 2;
-    const bool partial = (ent & 3) == AKV_TILE_PARTIAL;
-    const bool ver = kt < nvt;
-    const int row0 = ver ? voff + kt * BK : tb + (kt - nvt) * BK;
-    const int nrows = ver ? min(BK, r - kt * BK) : min(BK, te - row0);
-    const uint16_t* ks = ver ? kver : k;
-    const uint16_t* vs = ver ? vver : v;
+    const bool has_next = t + 1 < t1;
+    const int ent_next = has_next ? tiles[t + 1] : 0;
+    if (has_next) fetch(ent_next);  // in flight while this tile computes
 
-    __syncthreads();  // the previous tile's LDS readers are done
-    for (int c = threadIdx.x; c < BK * 8; c += 64 * GROUP) {
-      const int key = c >> 3, ch = c & 7;
-      uint4 kx = make_uint4(0, 0, 0, 0), vx = make_uint4(0, 0, 0, 0);
-      if (key < nrows) {
-        const long long off = ((long long)(row0 + key) * hkv + hk) * D + ch * 8;
-        kx = *(const uint4*)(ks + off);
-        vx = *(const uint4*)(vs + off);
-      }
-      *(uint4*)(lk + key * KP + ch * 8) = kx;
-      *(uint4*)(lv + key * VP + ch * 8) = vx;
-    }
-    if (partial && threadIdx.x < BK) {
-      const int key = threadIdx.x;
-      if (key < nrows) {
-        mtok[key] = ver ? -1 : row0 + key;
-        mdrop[key] = ver ? ver_drop[row0 + key] : tok_drop[row0 + key];
-      } else {
-        mtok[key] = INT_MAX;
-        mdrop[key] = INT_MIN;
-      }
-    }
-    __syncthreads();
-
+    const uint16_t* lkb = lk[buf];
+    const uint16_t* lvb = lv[buf];
     // S^T[key][q]: s[kb][qb][i] is key 32kb + 8(i/4) + 4lg + i%4, query 32qb + lq
     f32x16 s[2][2];
 #pragma unroll
@@ -152,13 +204,13 @@ __global__ __launch_bounds__(64 * GROUP) void seg_attn_bf16(
     for (int ds = 0; ds < 4; ++ds) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 a = *(const bf16x8*)(lk + (kb * 32 + lq) * KP + ds * 16 + lg * 8);
+        const bf16x8 a = *(const bf16x8*)(lkb + (kb * 32 + lq) * KP + ds * 16 + lg * 8);
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
           s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qb][ds], s[kb][qb], 0, 0, 0);
       }
     }
-    if (partial) {
+    if ((ent & 3) == AKV_TILE_PARTIAL) {
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         const int tok = q0 + qb * 32 + lq;
@@ -167,13 +219,13 @@ __global__ __launch_bounds__(64 * GROUP) void seg_attn_bf16(
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int key = kb * 32 + 8 * (i >> 2) + 4 * lg + (i & 3);
-            if (!(mtok[key] <= tok && tok < mdrop[key])) s[kb][qb][i] = -INFINITY;
+            if (!(mtok[buf][key] <= tok && tok < mdrop[buf][key])) s[kb][qb][i] = -INFINITY;
           }
       }
     }
 
-    // online softmax (base 2, scale folded into the exponent)
-    bf16x8 pb[2][2][2];  // [kb][qb][half]: P^T B operand, keys 32kb + 16half + ...
+    // online softmax in log2 units with a lazily rescaled running max
+    bf16x8 pb[2][2][2];  // [kb][qb][half]: P^T B operand
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       float mx = -INFINITY;
@@ -181,26 +233,28 @@ __global__ __launch_bounds__(64 * GROUP) void seg_attn_bf16(
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][qb][i]);
-      mx = xhalf_max(mx);
-      const float mnew = fmaxf(mrun[qb], mx);
-      const float alpha = (mrun[qb] == -INFINITY) ? 0.f : exp2f((mrun[qb] - mnew) * sl2);
-      const float msub = (mnew == -INFINITY) ? 0.f : mnew * sl2;
+      mx = xhalf_max(mx) * sl2;
+      const bool grow = mx > ms[qb] + kRescaleSlack;
+      if (__any(grow)) {
+        const float alpha = grow ? __builtin_amdgcn_exp2f(ms[qb] - mx) : 1.f;
+        ms[qb] = grow ? mx : ms[qb];
+        lrun[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) o[qb][db][i] *= alpha;
+      }
+      const float msub = (ms[qb] == -INFINITY) ? 0.f : ms[qb];
       float sum = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float p = exp2f(fmaf(s[kb][qb][i], sl2, -msub));
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][qb][i], sl2, -msub));
           s[kb][qb][i] = p;
           sum += p;
         }
-      sum = xhalf_sum(sum);
-      lrun[qb] = lrun[qb] * alpha + sum;
-      mrun[qb] = mnew;
-#pragma unroll
-      for (int db = 0; db < 2; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) o[qb][db][i] *= alpha;
+      lrun[qb] += xhalf_sum(sum);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -219,13 +273,16 @@ __global__ __launch_bounds__(64 * GROUP) void seg_attn_bf16(
         for (int db = 0; db < 2; ++db) {
           const int key = kb * 32 + 16 * hf + 4 * (G >> 1) + (i16 >> 2);
           const int dc = db * 32 + 16 * (G & 1) + 4 * (i16 & 3);
-          const s16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lv + key * VP + dc));
-          const s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lv + (key + 8) * VP + dc));
+          const s16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lvb + key * VP + dc));
+          const s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lvb + (key + 8) * VP + dc));
           const bf16x8 a = cat4(r0, r1);
 #pragma unroll
           for (int qb = 0; qb < 2; ++qb)
             o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb][qb][hf], o[qb][db], 0, 0, 0);
         }
+
+    if (has_next) stash(buf ^ 1, ent_next);
+    __syncthreads();  // next buffer written; this buffer's readers done
   }
 
   // epilogue: O^T[d][q] / l -> out[q][h][d]; o[qb][db][i] is d = 32db + 8(i/4) + 4lg + i%4
@@ -247,7 +304,8 @@ __global__ __launch_bounds__(64 * GROUP) void seg_attn_bf16(
         w.y = (uint32_t)__builtin_bit_cast(uint16_t, b2) | ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
         *(uint2*)(dst + d0) = w;
       }
-    if (lse && lg == 0) lse[(long long)tok * hq + h] = mrun[qb] * scale + logf(lrun[qb]);
+    // natural-log sum of exp(scale * score) = (ms + log2 l) / log2 e
+    if (lse && lg == 0) lse[(long long)tok * hq + h] = (ms[qb] + __log2f(lrun[qb])) / kLog2e;
   }
 }
 
@@ -258,7 +316,7 @@ __global__ __launch_bounds__(256) void seg_attn_f32(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     const float* __restrict__ kver, const float* __restrict__ vver, const int* __restrict__ item_desc,
     const int* __restrict__ tiles, const int* __restrict__ order, const int* __restrict__ tok_drop,
-    const int* __restrict__ ver_drop, float* __restrict__ out, float* __restrict__ lse, int hq,
+    const int* __restrict__ ver_src, float* __restrict__ out, float* __restrict__ lse, int hq,
     int hkv, int bk, float scale) {
   const int h = blockIdx.x % hq;
   const int item = order[blockIdx.x / hq];
@@ -281,7 +339,7 @@ __global__ __launch_bounds__(256) void seg_attn_f32(
     const int nrows = ver ? min(bk, r - kt * bk) : min(bk, te - row0);
     for (int key = 0; key < nrows; ++key) {
       const int row = row0 + key;
-      const bool vis = ver ? (tok < ver_drop[row]) : (row <= tok && tok < tok_drop[row]);
+      const bool vis = ver ? (tok < tok_drop[ver_src[row]]) : (row <= tok && tok < tok_drop[row]);
       if (!vis) continue;
       const float* kp = (ver ? kver : k) + ((long long)row * hkv + g) * DD;
       const float* vp = (ver ? vver : v) + ((long long)row * hkv + g) * DD;
@@ -324,7 +382,7 @@ int launch_segment_attention(const AttnArgs& a, void* stream) {
   hipLaunchKernelGGL(seg_attn_bf16<G>, dim3((unsigned)blocks), dim3(64 * G), 0, s,                  \
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,              \
                      (const uint16_t*)a.k_ver, (const uint16_t*)a.v_ver, a.item_desc, a.tiles,      \
-                     a.order, a.tok_drop, a.ver_drop, (uint16_t*)a.out, a.lse, a.hq, a.hkv, a.scale)
+                     a.order, a.tok_drop, a.ver_src, (uint16_t*)a.out, a.lse, a.hq, a.hkv, a.scale)
     switch (grp) {
       case 1: AKV_LAUNCH_BF16(1); break;
       case 2: AKV_LAUNCH_BF16(2); break;
@@ -340,7 +398,7 @@ int launch_segment_attention(const AttnArgs& a, void* stream) {
   hipLaunchKernelGGL(seg_attn_f32<DD>, dim3((unsigned)blocks), dim3(threads), 0, s,                 \
                      (const float*)a.q, (const float*)a.k, (const float*)a.v,                       \
                      (const float*)a.k_ver, (const float*)a.v_ver, a.item_desc, a.tiles, a.order,   \
-                     a.tok_drop, a.ver_drop, (float*)a.out, a.lse, a.hq, a.hkv, a.bk, a.scale)
+                     a.tok_drop, a.ver_src, (float*)a.out, a.lse, a.hq, a.hkv, a.bk, a.scale)
     switch (a.d) {
       case 32: AKV_LAUNCH_F32(32); break;
       case 64: AKV_LAUNCH_F32(64); break;

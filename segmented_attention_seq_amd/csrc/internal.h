@@ -2,6 +2,7 @@
 #pragma once
 
 #include <cstdint>
+#include <memory>
 #include <string>
 #include <vector>
 
@@ -22,9 +23,10 @@ struct akv_plan {
   std::vector<int32_t> final_tok, final_pos;
   int64_t visible_pairs = 0, p_next = 0, n_full = 0, n_partial = 0;
   // device image: contiguous int32 arrays at 256-byte aligned offsets
-  std::vector<uint8_t> image;
-  uint64_t off_tok_pos = 0, off_tok_drop = 0, off_ver_src = 0, off_ver_from = 0, off_ver_to = 0,
-           off_ver_drop = 0, off_item_desc = 0, off_tiles = 0, off_order = 0;
+  std::unique_ptr<uint8_t[]> image;
+  uint64_t image_bytes = 0;
+  uint64_t off_tok_pos = 0, off_tok_drop = 0, off_ver_src = 0, off_ver_to = 0, off_item_desc = 0,
+           off_tiles = 0, off_order = 0;
 };
 
 namespace akv {
@@ -47,6 +49,7 @@ struct RopeArgs {
   int32_t heads, d;
   const int32_t* gather;
   const int32_t* pos_from;
+  bool pos_from_by_src;  // pos_from indexed by the gathered source row instead of the output row
   const int32_t* pos_to;
   double base;
   int layout;
@@ -58,7 +61,7 @@ struct AttnArgs {
   const void *q, *k, *v, *k_ver, *v_ver;
   void* out;
   float* lse;
-  const int32_t *item_desc, *tiles, *order, *tok_drop, *ver_drop;
+  const int32_t *item_desc, *tiles, *order, *tok_drop, *ver_src;
   int64_t n_items;
   int32_t hq, hkv, d, bq, bk;
   float scale;

@@ -18,6 +18,7 @@
 #include <cstring>
 #include <new>
 #include <numeric>
+#include <stdexcept>
 
 #include "internal.h"
 
@@ -159,13 +160,22 @@ int build_plan(const akv_op* ops, int64_t n_ops, int32_t bq, int32_t bk, akv_pla
       }
     }
     int64_t ver_total = 0;
-    for (const Stretch& st : stretches) {
-      p->epochs.insert(p->epochs.end(), {(int32_t)st.tb, (int32_t)st.te, (int32_t)st.src.size(),
-                                         (int32_t)ver_total});
-      for (size_t v = 0; v < st.src.size(); ++v)
-        p->versions.insert(p->versions.end(), {st.src[v], p->tok_pos[st.src[v]], (int32_t)v});
-      ver_total += (int64_t)st.src.size();
-      if (ver_total > INT32_MAX) throw std::length_error("more than 2^31-1 version rows");
+    for (const Stretch& st : stretches) ver_total += (int64_t)st.src.size();
+    if (ver_total > INT32_MAX) throw std::length_error("more than 2^31-1 version rows");
+    p->versions.resize(3 * ver_total);
+    {
+      int64_t row = 0;
+      for (const Stretch& st : stretches) {
+        p->epochs.insert(p->epochs.end(), {(int32_t)st.tb, (int32_t)st.te, (int32_t)st.src.size(),
+                                           (int32_t)row});
+        int32_t* w = p->versions.data() + 3 * row;
+        for (size_t v = 0; v < st.src.size(); ++v, w += 3) {
+          w[0] = st.src[v];
+          w[1] = p->tok_pos[st.src[v]];
+          w[2] = (int32_t)v;
+        }
+        row += (int64_t)st.src.size();
+      }
     }
 
     // T6: tile classes per (stretch, q-tile).
@@ -235,36 +245,33 @@ int build_plan(const akv_op* ops, int64_t n_ops, int32_t bq, int32_t bk, akv_pla
       return p->tile_ptr[a + 1] - p->tile_ptr[a] > p->tile_ptr[b + 1] - p->tile_ptr[b];
     });
 
-    // Device image.
-    const int64_t nv = (int64_t)p->versions.size() / 3;
-    std::vector<int32_t> ver_src(nv), ver_from(nv), ver_to(nv), ver_drop(nv);
-    for (int64_t v = 0; v < nv; ++v) {
-      ver_src[v] = p->versions[3 * v];
-      ver_from[v] = p->versions[3 * v + 1];
-      ver_to[v] = p->versions[3 * v + 2];
-      ver_drop[v] = p->tok_drop[ver_src[v]];
-    }
+    // Device image.  Version rows carry only (src, to); kernels read the source's
+    // append position and drop boundary through tok_pos / tok_drop.
+    const int64_t nv = ver_total;
     uint64_t off = 0;
     auto place = [&](uint64_t bytes) { uint64_t o = off; off += (bytes + 255) & ~uint64_t(255); return o; };
     p->off_tok_pos = place(4 * T);
     p->off_tok_drop = place(4 * T);
     p->off_ver_src = place(4 * nv);
-    p->off_ver_from = place(4 * nv);
     p->off_ver_to = place(4 * nv);
-    p->off_ver_drop = place(4 * nv);
     p->off_item_desc = place(4 * desc.size());
     p->off_tiles = place(4 * p->tiles.size());
     p->off_order = place(4 * n_items);
-    p->image.assign(std::max<uint64_t>(off, 256), 0);
+    p->image_bytes = std::max<uint64_t>(off, 256);
+    p->image.reset(new uint8_t[p->image_bytes]);   // padding between arrays is never read
     auto put = [&](uint64_t o, const std::vector<int32_t>& v) {
-      if (!v.empty()) std::memcpy(p->image.data() + o, v.data(), 4 * v.size());
+      if (!v.empty()) std::memcpy(p->image.get() + o, v.data(), 4 * v.size());
     };
     put(p->off_tok_pos, p->tok_pos);
     put(p->off_tok_drop, p->tok_drop);
-    put(p->off_ver_src, ver_src);
-    put(p->off_ver_from, ver_from);
-    put(p->off_ver_to, ver_to);
-    put(p->off_ver_drop, ver_drop);
+    {
+      int32_t* src = (int32_t*)(p->image.get() + p->off_ver_src);
+      int32_t* to = (int32_t*)(p->image.get() + p->off_ver_to);
+      for (int64_t v = 0; v < nv; ++v) {
+        src[v] = p->versions[3 * v];
+        to[v] = p->versions[3 * v + 2];
+      }
+    }
     put(p->off_item_desc, desc);
     put(p->off_tiles, p->tiles);
     put(p->off_order, p->item_order);

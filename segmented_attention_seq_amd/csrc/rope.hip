@@ -81,7 +81,7 @@ __global__ __launch_bounds__(256) void rope_kernel(T* __restrict__ out, const T*
                                                    T* __restrict__ vout, const T* __restrict__ vin,
                                                    long long n_rows, int heads, int d,
                                                    const int* __restrict__ gather,
-                                                   const int* __restrict__ pos_from,
+                                                   const int* __restrict__ pos_from, int from_by_src,
                                                    const int* __restrict__ pos_to, Freqs fr) {
   const int cpr = d >> 4;  // 8-pair chunks per head vector
   const long long tid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
@@ -89,7 +89,8 @@ __global__ __launch_bounds__(256) void rope_kernel(T* __restrict__ out, const T*
   const int c = (int)(tid - row * cpr);
   if (row >= n_rows) return;
   const long long src = gather ? (long long)gather[row] : row;
-  const long long delta = (long long)pos_to[row] - (pos_from ? (long long)pos_from[row] : 0LL);
+  const long long delta =
+      (long long)pos_to[row] - (pos_from ? (long long)pos_from[from_by_src ? src : row] : 0LL);
   float cs[8], sn[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) angle_cs(delta, fr.theta[c * 8 + i], cs[i], sn[i]);
@@ -137,7 +138,7 @@ void launch_t(const RopeArgs& a, const Freqs& fr, hipStream_t s) {
   const unsigned blocks = (unsigned)((threads + 255) / 256);
   hipLaunchKernelGGL((rope_kernel<T, LAYOUT>), dim3(blocks), dim3(256), 0, s, (T*)a.out, (const T*)a.in,
                      (T*)a.v_out, (const T*)a.v_in, (long long)a.n_rows, a.heads, a.d, a.gather,
-                     a.pos_from, a.pos_to, fr);
+                     a.pos_from, a.pos_from_by_src ? 1 : 0, a.pos_to, fr);
 }
 
 }  // namespace
