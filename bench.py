@@ -48,6 +48,9 @@ def parse_args():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--only", default="", help="comma list of stages to run (profiling aid): "
                                                "restore,repos,decode")
+    ap.add_argument("--copy-mb", type=int, default=0,
+                    help="before timing, run a plain device copy of this many MiB (3 times) so hardware "
+                         "byte counters can be scaled against a transfer of known size")
     return ap.parse_args()
 
 
@@ -144,10 +147,10 @@ def main():
             "out": torch.empty_like(qd)}
     dev_plans = [torch.empty(1 << 20, dtype=torch.uint8, device=dev) for _ in range(2)]
 
-    rb = workload.repos_batch()
+    rb = workload.repos_batch() if "repos" in only else workload.repos_batch(n_keys=64)
     nrep = rb.slots.size
     repos_sets = []
-    for s in range(args.repos_sets):
+    for s in range(args.repos_sets if "repos" in only else 1):
         pool = torch.zeros((rb.pool_slots, rb.hkv, rb.d), dtype=torch.bfloat16, device=dev)
         pool[torch.from_numpy(rb.slots.astype(np.int64)).to(dev)] = t_bf16(rb.k_rows)
         repos_sets.append((pool, torch.empty((nrep, rb.hkv, rb.d), dtype=torch.bfloat16, device=dev)))
@@ -156,7 +159,7 @@ def main():
     r_idx = torch.from_numpy(rb.slots).to(dev)
     repos_bytes = nrep * rb.hkv * rb.d * 2 * 2 + 12 * nrep
 
-    db = workload.decode_batch()
+    db = workload.decode_batch() if "decode" in only else workload.decode_batch(batch=1, lo=64, hi=65)
     pool_k = torch.zeros((db.pool_slots, db.hkv, db.d), dtype=torch.bfloat16, device=dev)
     pool_v = torch.zeros_like(pool_k)
     didx = torch.from_numpy(db.indices.astype(np.int64)).to(dev)
@@ -172,6 +175,13 @@ def main():
                       dtype=torch.uint8, device=dev)
     decode_bytes = n_keys * db.hkv * db.d * 2 * 2 + 4 * n_keys + 2 * dq.numel() * 2
     torch.cuda.synchronize()
+    if args.copy_mb:
+        src = torch.ones(args.copy_mb << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     ev_names = ["rope", "versions", "attn", "repos", "decode"]
     stage_ms = {n: [] for n in ev_names}

@@ -55,6 +55,12 @@ __device__ __forceinline__ float xhalf_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Workgroup barrier that orders LDS only: waits for this wave's LDS accesses
+// (lgkmcnt) but lets global loads into registers stay in flight across it (a
+// __syncthreads release fence would drain them).  The memory clobber keeps the
+// compiler from moving LDS accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 __device__ __forceinline__ bf16x8 cat4(s16x4 a, s16x4 b) {
   typedef __attribute__((__vector_size__(8 * sizeof(short)))) short s16x8;
   s16x8 v = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -65,6 +71,8 @@ __device__ __forceinline__ bf16x8 cat4(s16x4 a, s16x4 b) {
 // score exceeds the running max by more than this, so exp2 arguments stay <= 8
 // (p <= 256, exact in fp32, no bf16 overflow) and most tiles skip the rescale.
 constexpr float kRescaleSlack = 8.0f;
+
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
 
 struct TileSrc {
   const uint16_t* k;
@@ -86,15 +94,253 @@ __device__ __forceinline__ TileSrc tile_src(int ent, int nvt, int voff, int r, i
   return ts;
 }
 
+// Per-wave state: 64 query tokens of one head.  The wave's Q rows live in LDS
+// (see load_q), not in registers.
+struct WaveState {
+  f32x16 o[2][2];         // O^T accumulators [qb][db]: d = 32db + 8(i/4) + 4lg + i%4, query 32qb + lq
+  f32x16 s[2][2];         // S^T [kb][qb]: key 32kb + 8(i/4) + 4lg + i%4, query 32qb + lq
+  bf16x8 pb[2][2][2];     // P^T B operand [kb][qb][half]
+  f32x16 cm[2];           // QK accumulator seed per query block: -running max (0 while unset)
+  float ms[2], lrun[2];   // running max (log2 units; -inf while unset) and sum per query column
+};
+
+// S'^T = K Q'^T - m for one 64-key tile held in LDS (16 MFMAs).  Q' is Q scaled by
+// scale*log2(e), and each accumulation chain starts from the running max seed, so
+// the MFMA result is already the exp2 argument.
+__device__ __forceinline__ void tile_qk(WaveState& w, const uint16_t* lkb, const uint16_t* lqw, int lq, int lg) {
+#pragma unroll
+  for (int ds = 0; ds < 4; ++ds) {
+    bf16x8 b[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) b[qb] = *(const bf16x8*)(lqw + (qb * 32 + lq) * KP + ds * 16 + lg * 8);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const bf16x8 a = *(const bf16x8*)(lkb + (kb * 32 + lq) * KP + ds * 16 + lg * 8);
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+        w.s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b[qb], ds ? w.s[kb][qb] : w.cm[qb], 0, 0, 0);
+    }
+  }
+}
+
+// Mask (PARTIAL tiles), online softmax in log2 units, P -> bf16 B operand.  The
+// scores arrive already shifted by the running max m (tile_qk).  m is raised only
+// when a score exceeds it by more than kRescaleSlack (or on the first visible
+// score); then the accumulators are rescaled and the tile's scores shifted.
+__device__ __forceinline__ void tile_softmax(WaveState& w, bool partial, const int* mtok, const int* mdrop,
+                                             int q0, int lq, int lg) {
+  if (partial) {
+    asm volatile("");  // keep this rare path behind its branch (not speculated into every tile)
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const int tok = q0 + qb * 32 + lq;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = kb * 32 + 8 * (i >> 2) + 4 * lg + (i & 3);
+          const int mt = mtok[key], md = mdrop[key];
+          const bool vis = (mt <= tok) & (tok < md);
+          w.s[kb][qb][i] = vis ? w.s[kb][qb][i] : -INFINITY;
+        }
+    }
+  }
+  float mx[2];
+  bool grow[2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    float m = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) m = fmaxf(m, w.s[kb][qb][i]);
+    mx[qb] = xhalf_max(m);
+    grow[qb] = (w.ms[qb] == -INFINITY) ? (mx[qb] > -INFINITY) : (mx[qb] > kRescaleSlack);
+  }
+  if (__any(grow[0] || grow[1])) {
+    asm volatile("");  // rare path: keep it behind the branch
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const bool unset = w.ms[qb] == -INFINITY;
+      const float shift = grow[qb] ? mx[qb] : 0.f;
+      const float mnew = (unset ? 0.f : w.ms[qb]) + shift;
+      const float alpha = grow[qb] ? __builtin_amdgcn_exp2f(w.ms[qb] - mnew) : 1.f;  // 0 while unset
+      w.ms[qb] = grow[qb] ? mnew : w.ms[qb];
+      w.lrun[qb] *= alpha;
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) w.o[qb][db][i] *= alpha;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) w.s[kb][qb][i] -= shift;
+      const float seed = w.ms[qb] == -INFINITY ? 0.f : -w.ms[qb];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) w.cm[qb][i] = seed;
+    }
+  }
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    float sum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        bf16x8 p;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) p[j] = (__bf16)__builtin_amdgcn_exp2f(w.s[kb][qb][8 * hf + j]);
+        w.pb[kb][qb][hf] = p;
+        // row sum of the rounded probabilities (the values the PV product uses)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const bf16x2 pr = {p[2 * j], p[2 * j + 1]};
+          sum = __builtin_amdgcn_fdot2_f32_bf16(pr, one, sum, false);
+        }
+      }
+    w.lrun[qb] += xhalf_sum(sum);
+  }
+}
+
+// O^T += V^T P^T for one tile (16 MFMAs); V^T comes from the row-major V tile
+// through the transposing LDS read.
+__device__ __forceinline__ void tile_pv(WaveState& w, const uint16_t* lvb, int lane) {
+  const int G = lane >> 4, i16 = lane & 15;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int db = 0; db < 2; ++db) {
+        const int key = kb * 32 + 16 * hf + 4 * (G >> 1) + (i16 >> 2);
+        const int dc = db * 32 + 16 * (G & 1) + 4 * (i16 & 3);
+        const s16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lvb + key * VP + dc));
+        const s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lvb + (key + 8) * VP + dc));
+        const bf16x8 a = cat4(r0, r1);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+          w.o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, w.pb[kb][qb][hf], w.o[qb][db], 0, 0, 0);
+      }
+}
+
+// The wave's 64 Q rows, scaled by sl2 = scale * log2(e) (re-rounded to bf16) so
+// that QK products come out in log2 units, go to the wave's private LDS block
+// lqw[64][KP]; each lane writes exactly the fragments it reads back in tile_qk.
+__device__ __forceinline__ void load_q(WaveState& w, uint16_t* lqw, const uint16_t* q, int q0, int q1, int hq,
+                                       int h, int lq, int lg, float sl2) {
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int tok = q0 + qb * 32 + lq;
+    const uint4* src = (const uint4*)(q + ((long long)tok * hq + h) * D);
+#pragma unroll
+    for (int ds = 0; ds < 4; ++ds) {
+      uint4 x = make_uint4(0, 0, 0, 0);
+      if (tok < q1) x = src[ds * 2 + lg];
+      bf16x8 b = __builtin_bit_cast(bf16x8, x);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) b[j] = (__bf16)((float)b[j] * sl2);
+      *(bf16x8*)(lqw + (qb * 32 + lq) * KP + ds * 16 + lg * 8) = b;
+    }
+    for (int i = 0; i < 16; ++i) w.cm[qb][i] = 0.f;
+  }
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    w.ms[qb] = -INFINITY;
+    w.lrun[qb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) w.o[qb][db][i] = 0.f;
+  }
+}
+
+__device__ __forceinline__ void store_out(const WaveState& w, uint16_t* out, float* lse, int q0, int q1,
+                                          int hq, int h, int lq, int lg) {
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int tok = q0 + qb * 32 + lq;
+    if (tok >= q1) continue;
+    const float inv = 1.f / w.lrun[qb];
+    uint16_t* dst = out + ((long long)tok * hq + h) * D;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d0 = db * 32 + 8 * j + 4 * lg;
+        const __bf16 b0 = (__bf16)(w.o[qb][db][4 * j] * inv), b1 = (__bf16)(w.o[qb][db][4 * j + 1] * inv);
+        const __bf16 b2 = (__bf16)(w.o[qb][db][4 * j + 2] * inv), b3 = (__bf16)(w.o[qb][db][4 * j + 3] * inv);
+        uint2 u;
+        u.x = (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
+        u.y = (uint32_t)__builtin_bit_cast(uint16_t, b2) | ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
+        *(uint2*)(dst + d0) = u;
+      }
+    // natural-log sum of exp(scale * score) = (ms + log2 l) / log2 e
+    if (lse && lg == 0) lse[(long long)tok * hq + h] = (w.ms[qb] + __log2f(w.lrun[qb])) / kLog2e;
+  }
+}
+
+// Cooperative global -> register -> LDS staging of one K/V tile and its mask metadata.
+template <int NT>
+struct TileStage {
+  static constexpr int CPT = (BK * 8 + NT - 1) / NT;  // 16-byte chunks of K (and V) per thread
+  uint4 kx[CPT], vx[CPT];
+  int mt, md;
+  __device__ __forceinline__ void fetch(const TileSrc& ts, bool partial, int hkv, int hk, const int* tok_drop,
+                                        const int* ver_src) {
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      const int c = threadIdx.x + j * NT;
+      const int key = c >> 3, ch = c & 7;
+      kx[j] = make_uint4(0, 0, 0, 0);
+      vx[j] = make_uint4(0, 0, 0, 0);
+      if (c < BK * 8 && key < ts.nrows) {
+        const long long off = ((long long)(ts.row0 + key) * hkv + hk) * D + ch * 8;
+        kx[j] = *(const uint4*)(ts.k + off);
+        vx[j] = *(const uint4*)(ts.v + off);
+      }
+    }
+    if (partial && threadIdx.x < BK) {
+      const int key = threadIdx.x;
+      mt = INT_MAX;
+      md = INT_MIN;
+      if (key < ts.nrows) {
+        mt = ts.ver ? -1 : ts.row0 + key;
+        md = tok_drop[ts.ver ? ver_src[ts.row0 + key] : ts.row0 + key];
+      }
+    }
+  }
+  __device__ __forceinline__ void stash(uint16_t* lkb, uint16_t* lvb, int* mtok, int* mdrop, bool partial) {
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      const int c = threadIdx.x + j * NT;
+      if (c < BK * 8) {
+        const int key = c >> 3, ch = c & 7;
+        *(uint4*)(lkb + key * KP + ch * 8) = kx[j];
+        *(uint4*)(lvb + key * VP + ch * 8) = vx[j];
+      }
+    }
+    if (partial && threadIdx.x < BK) {
+      mtok[threadIdx.x] = mt;
+      mdrop[threadIdx.x] = md;
+    }
+  }
+};
+
+#define AKV_ATTN_PARAMS                                                                            \
+  const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v, \
+      const uint16_t *__restrict__ kver, const uint16_t *__restrict__ vver,                        \
+      const int *__restrict__ item_desc, const int *__restrict__ tiles,                            \
+      const int *__restrict__ order, const int *__restrict__ tok_drop,                             \
+      const int *__restrict__ ver_src, uint16_t *__restrict__ out, float *__restrict__ lse,       \
+      int hq, int hkv, float scale
+
+// Double-buffered pipeline: tile t+1 is loaded while tile t computes.  Used when
+// the query-head group is smaller than 8 (fewer than two waves per SIMD).
 template <int GROUP>
-__global__ __launch_bounds__(64 * GROUP) void seg_attn_bf16(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const uint16_t* __restrict__ kver, const uint16_t* __restrict__ vver,
-    const int* __restrict__ item_desc, const int* __restrict__ tiles, const int* __restrict__ order,
-    const int* __restrict__ tok_drop, const int* __restrict__ ver_src, uint16_t* __restrict__ out,
-    float* __restrict__ lse, int hq, int hkv, float scale) {
-  constexpr int NT = 64 * GROUP;            // threads
-  constexpr int CPT = (BK * 8 + NT - 1) / NT;  // 16-byte K (and V) chunks per thread per tile
+__global__ __launch_bounds__(64 * GROUP) void seg_attn_bf16(AKV_ATTN_PARAMS) {
+  constexpr int NT = 64 * GROUP;
+  __shared__ __attribute__((aligned(16))) uint16_t lqs[GROUP][64 * KP];
   __shared__ __attribute__((aligned(16))) uint16_t lk[2][BK * KP];
   __shared__ __attribute__((aligned(16))) uint16_t lv[2][BK * VP];
   __shared__ int mtok[2][BK], mdrop[2][BK];
@@ -110,203 +356,109 @@ __global__ __launch_bounds__(64 * GROUP) void seg_attn_bf16(
   const int nvt = (r + BK - 1) / BK;
   const float sl2 = scale * kLog2e;
 
-  // Q^T fragments (B operand): qf[qb][ds] = Q[q0 + 32qb + lq][h][16ds + 8lg .. +8]
-  bf16x8 qf[2][4];
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int tok = q0 + qb * 32 + lq;
-    const uint4* src = (const uint4*)(q + ((long long)tok * hq + h) * D);
-#pragma unroll
-    for (int ds = 0; ds < 4; ++ds) {
-      uint4 x = make_uint4(0, 0, 0, 0);
-      if (tok < q1) x = src[ds * 2 + lg];
-      qf[qb][ds] = __builtin_bit_cast(bf16x8, x);
-    }
-  }
-
-  // global -> register staging of one K/V tile (+ mask metadata), then -> LDS buffer
-  uint4 kx[CPT], vx[CPT];
-  int mt = INT_MAX, md = INT_MIN;
-  auto fetch = [&](int ent) {
-    const TileSrc ts = tile_src(ent, nvt, voff, r, tb, te, k, v, kver, vver);
-#pragma unroll
-    for (int j = 0; j < CPT; ++j) {
-      const int c = threadIdx.x + j * NT;
-      const int key = c >> 3, ch = c & 7;
-      kx[j] = make_uint4(0, 0, 0, 0);
-      vx[j] = make_uint4(0, 0, 0, 0);
-      if (c < BK * 8 && key < ts.nrows) {
-        const long long off = ((long long)(ts.row0 + key) * hkv + hk) * D + ch * 8;
-        kx[j] = *(const uint4*)(ts.k + off);
-        vx[j] = *(const uint4*)(ts.v + off);
-      }
-    }
-    if ((ent & 3) == AKV_TILE_PARTIAL && threadIdx.x < BK) {
-      const int key = threadIdx.x;
-      mt = INT_MAX;
-      md = INT_MIN;
-      if (key < ts.nrows) {
-        mt = ts.ver ? -1 : ts.row0 + key;
-        md = tok_drop[ts.ver ? ver_src[ts.row0 + key] : ts.row0 + key];
-      }
-    }
-  };
-  auto stash = [&](int buf, int ent) {
-#pragma unroll
-    for (int j = 0; j < CPT; ++j) {
-      const int c = threadIdx.x + j * NT;
-      if (c < BK * 8) {
-        const int key = c >> 3, ch = c & 7;
-        *(uint4*)(&lk[buf][key * KP + ch * 8]) = kx[j];
-        *(uint4*)(&lv[buf][key * VP + ch * 8]) = vx[j];
-      }
-    }
-    if ((ent & 3) == AKV_TILE_PARTIAL && threadIdx.x < BK) {
-      mtok[buf][threadIdx.x] = mt;
-      mdrop[buf][threadIdx.x] = md;
-    }
-  };
-
-  f32x16 o[2][2];
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-    for (int db = 0; db < 2; ++db)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) o[qb][db][i] = 0.f;
-  float ms[2] = {-INFINITY, -INFINITY};  // running max, already scaled to log2 units
-  float lrun[2] = {0.f, 0.f};
-
+  WaveState w;
+  load_q(w, lqs[wave], q, q0, q1, hq, h, lq, lg, sl2);
+  TileStage<NT> st;
   if (t0 < t1) {
-    fetch(tiles[t0]);
-    stash(0, tiles[t0]);
+    const int e = tiles[t0];
+    st.fetch(tile_src(e, nvt, voff, r, tb, te, k, v, kver, vver), (e & 3) == AKV_TILE_PARTIAL, hkv, hk,
+             tok_drop, ver_src);
+    st.stash(lk[0], lv[0], mtok[0], mdrop[0], (e & 3) == AKV_TILE_PARTIAL);
   }
   __syncthreads();
-
   for (int t = t0; t < t1; ++t) {
     const int buf = (t - t0) & 1;
     const int ent = tiles[t];
     const bool has_next = t + 1 < t1;
-    const int ent_next = has_next ? tiles[t + 1] : 0;
-    if (has_next) fetch(ent_next);  // in flight while this tile computes
-
-    const uint16_t* lkb = lk[buf];
-    const uint16_t* lvb = lv[buf];
-    // S^T[key][q]: s[kb][qb][i] is key 32kb + 8(i/4) + 4lg + i%4, query 32qb + lq
-    f32x16 s[2][2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) s[kb][qb][i] = 0.f;
-#pragma unroll
-    for (int ds = 0; ds < 4; ++ds) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 a = *(const bf16x8*)(lkb + (kb * 32 + lq) * KP + ds * 16 + lg * 8);
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-          s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qb][ds], s[kb][qb], 0, 0, 0);
-      }
-    }
-    if ((ent & 3) == AKV_TILE_PARTIAL) {
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        const int tok = q0 + qb * 32 + lq;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = kb * 32 + 8 * (i >> 2) + 4 * lg + (i & 3);
-            if (!(mtok[buf][key] <= tok && tok < mdrop[buf][key])) s[kb][qb][i] = -INFINITY;
-          }
-      }
-    }
-
-    // online softmax in log2 units with a lazily rescaled running max
-    bf16x8 pb[2][2][2];  // [kb][qb][half]: P^T B operand
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][qb][i]);
-      mx = xhalf_max(mx) * sl2;
-      const bool grow = mx > ms[qb] + kRescaleSlack;
-      if (__any(grow)) {
-        const float alpha = grow ? __builtin_amdgcn_exp2f(ms[qb] - mx) : 1.f;
-        ms[qb] = grow ? mx : ms[qb];
-        lrun[qb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < 2; ++db)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) o[qb][db][i] *= alpha;
-      }
-      const float msub = (ms[qb] == -INFINITY) ? 0.f : ms[qb];
-      float sum = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][qb][i], sl2, -msub));
-          s[kb][qb][i] = p;
-          sum += p;
-        }
-      lrun[qb] += xhalf_sum(sum);
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-          for (int j = 0; j < 8; ++j) pb[kb][qb][hf][j] = (__bf16)s[kb][qb][8 * hf + j];
-    }
-
-    // O^T[d][q] += V^T[d][key] P^T[key][q]
-    const int G = lane >> 4, i16 = lane & 15;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-        for (int db = 0; db < 2; ++db) {
-          const int key = kb * 32 + 16 * hf + 4 * (G >> 1) + (i16 >> 2);
-          const int dc = db * 32 + 16 * (G & 1) + 4 * (i16 & 3);
-          const s16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lvb + key * VP + dc));
-          const s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lvb + (key + 8) * VP + dc));
-          const bf16x8 a = cat4(r0, r1);
-#pragma unroll
-          for (int qb = 0; qb < 2; ++qb)
-            o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb][qb][hf], o[qb][db], 0, 0, 0);
-        }
-
-    if (has_next) stash(buf ^ 1, ent_next);
-    __syncthreads();  // next buffer written; this buffer's readers done
+    const int en = has_next ? tiles[t + 1] : 0;
+    if (has_next)
+      st.fetch(tile_src(en, nvt, voff, r, tb, te, k, v, kver, vver), (en & 3) == AKV_TILE_PARTIAL, hkv, hk,
+               tok_drop, ver_src);
+    tile_qk(w, lk[buf], lqs[wave], lq, lg);
+    tile_softmax(w, (ent & 3) == AKV_TILE_PARTIAL, mtok[buf], mdrop[buf], q0, lq, lg);
+    tile_pv(w, lv[buf], lane);
+    if (has_next) st.stash(lk[buf ^ 1], lv[buf ^ 1], mtok[buf ^ 1], mdrop[buf ^ 1], (en & 3) == AKV_TILE_PARTIAL);
+    lds_barrier();
   }
+  store_out(w, out, lse, q0, q1, hq, h, lq, lg);
+}
 
-  // epilogue: O^T[d][q] / l -> out[q][h][d]; o[qb][db][i] is d = 32db + 8(i/4) + 4lg + i%4
+// Ping-pong pipeline for 8 query heads per kv head (8 waves, two per SIMD).
+// Waves 0-3 (group A) and 4-7 (group B) run the same tile loop one phase apart,
+// separated by workgroup barriers, so while one wave of a SIMD issues MFMAs
+// (PV of tile t and QK of tile t+1) its partner runs the softmax of its tile on
+// the VALU.  Each K/V tile stays in LDS for four phases, so tiles rotate through
+// three LDS slots; tile t+2 is fetched to registers at the start of iteration t
+// and written to its slot one phase later, after its previous occupant's last
+// reader has passed a barrier.
+__global__ __launch_bounds__(512) void seg_attn_bf16_pp(AKV_ATTN_PARAMS) {
+  constexpr int GROUP = 8, NT = 512, NSLOT = 3;
+  __shared__ __attribute__((aligned(16))) uint16_t lqs[GROUP][64 * KP];
+  __shared__ __attribute__((aligned(16))) uint16_t lk[NSLOT][BK * KP];
+  __shared__ __attribute__((aligned(16))) uint16_t lv[NSLOT][BK * VP];
+  __shared__ int mtok[NSLOT][BK], mdrop[NSLOT][BK];
+
+  const int hk = blockIdx.x % hkv;
+  const int item = order[blockIdx.x / hkv];
+  const int* dsc = item_desc + item * ID_WORDS;
+  const int q0 = dsc[ID_QBEGIN], q1 = dsc[ID_QEND], tb = dsc[ID_TB], te = dsc[ID_TE];
+  const int r = dsc[ID_R], voff = dsc[ID_VEROFF], t0 = dsc[ID_TILE0], t1 = dsc[ID_TILE1];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int h = hk * GROUP + wave;
+  const int lq = lane & 31, lg = lane >> 5;
+  const bool lag = wave >= 4;  // group B
+  const int nvt = (r + BK - 1) / BK;
+  const float sl2 = scale * kLog2e;
+  const int n = t1 - t0;
+  if (n <= 0) return;  // uniform over the workgroup; every query sees at least itself
+
+  WaveState w;
+  load_q(w, lqs[wave], q, q0, q1, hq, h, lq, lg, sl2);
+  TileStage<NT> st;
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int tok = q0 + qb * 32 + lq;
-    if (tok >= q1) continue;
-    const float inv = 1.f / lrun[qb];
-    uint16_t* dst = out + ((long long)tok * hq + h) * D;
-#pragma unroll
-    for (int db = 0; db < 2; ++db)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int d0 = db * 32 + 8 * j + 4 * lg;
-        const __bf16 b0 = (__bf16)(o[qb][db][4 * j] * inv), b1 = (__bf16)(o[qb][db][4 * j + 1] * inv);
-        const __bf16 b2 = (__bf16)(o[qb][db][4 * j + 2] * inv), b3 = (__bf16)(o[qb][db][4 * j + 3] * inv);
-        uint2 w;
-        w.x = (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
-        w.y = (uint32_t)__builtin_bit_cast(uint16_t, b2) | ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
-        *(uint2*)(dst + d0) = w;
-      }
-    // natural-log sum of exp(scale * score) = (ms + log2 l) / log2 e
-    if (lse && lg == 0) lse[(long long)tok * hq + h] = (ms[qb] + __log2f(lrun[qb])) / kLog2e;
+  for (int j = 0; j < 2; ++j) {
+    if (j < n) {
+      const int e = tiles[t0 + j];
+      const bool pt = (e & 3) == AKV_TILE_PARTIAL;
+      st.fetch(tile_src(e, nvt, voff, r, tb, te, k, v, kver, vver), pt, hkv, hk, tok_drop, ver_src);
+      st.stash(lk[j], lv[j], mtok[j], mdrop[j], pt);
+    }
   }
+  __syncthreads();
+  if (lag) lds_barrier();
+  tile_qk(w, lk[0], lqs[wave], lq, lg);
+  lds_barrier();
+  int slot = 0;  // slot of tile i
+  // tile entries i, i+1, i+2 in hand; entry i+3 is requested one iteration ahead
+  int ent = tiles[t0], e1 = n > 1 ? tiles[t0 + 1] : 0, e2n = n > 2 ? tiles[t0 + 2] : 0;
+  for (int i = 0; i < n; ++i) {
+    const int e3n = i + 3 < n ? tiles[t0 + i + 3] : 0;
+    const bool fetch2 = i + 2 < n;
+    const int e2 = e2n;
+    const bool p2 = (e2 & 3) == AKV_TILE_PARTIAL;
+    const int slot1 = slot == NSLOT - 1 ? 0 : slot + 1;
+    const int slot2 = slot1 == NSLOT - 1 ? 0 : slot1 + 1;
+    if (fetch2) st.fetch(tile_src(e2, nvt, voff, r, tb, te, k, v, kver, vver), p2, hkv, hk, tok_drop, ver_src);
+    // phase 1 (VALU): softmax of tile i
+    tile_softmax(w, (ent & 3) == AKV_TILE_PARTIAL, mtok[slot], mdrop[slot], q0, lq, lg);
+    lds_barrier();
+    // phase 2 (MFMA): PV of tile i, QK of tile i+1; then tile i+2 goes to the slot
+    // freed by tile i-1 (its last reader finished before the barrier above)
+    __builtin_amdgcn_s_setprio(1);
+    tile_pv(w, lv[slot], lane);
+    // P of tile i dies here, before the scores of tile i+1 are born: they share registers
+    __builtin_amdgcn_sched_barrier(0);
+    if (i + 1 < n) tile_qk(w, lk[slot1], lqs[wave], lq, lg);
+    __builtin_amdgcn_s_setprio(0);
+    if (fetch2) st.stash(lk[slot2], lv[slot2], mtok[slot2], mdrop[slot2], p2);
+    lds_barrier();
+    slot = slot1;
+    ent = e1;
+    e1 = e2n;
+    e2n = e3n;
+  }
+  if (!lag) lds_barrier();
+  store_out(w, out, lse, q0, q1, hq, h, lq, lg);
 }
 
 // float32 path: one thread per (query token, head), keys walked one at a time
@@ -387,7 +539,12 @@ int launch_segment_attention(const AttnArgs& a, void* stream) {
       case 1: AKV_LAUNCH_BF16(1); break;
       case 2: AKV_LAUNCH_BF16(2); break;
       case 4: AKV_LAUNCH_BF16(4); break;
-      default: AKV_LAUNCH_BF16(8); break;
+      default:
+        hipLaunchKernelGGL(seg_attn_bf16_pp, dim3((unsigned)blocks), dim3(512), 0, s, (const uint16_t*)a.q,
+                           (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.k_ver,
+                           (const uint16_t*)a.v_ver, a.item_desc, a.tiles, a.order, a.tok_drop, a.ver_src,
+                           (uint16_t*)a.out, a.lse, a.hq, a.hkv, a.scale);
+        break;
     }
 #undef AKV_LAUNCH_BF16
   } else {
