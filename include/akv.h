@@ -204,7 +204,7 @@ int akv_segment_attention(const akv_plan* plan, const void* dev_plan,
  * pool rows indices[indptr[b] .. indptr[b+1]) (its active cache plus its own new
  * slot, gathered at page size 1).  q, k_pool, v_pool: bf16; indptr/indices: device
  * int32; max_n >= every request's key count (host-side bound, sets the split
- * count).  A request with zero keys is an error the kernel cannot report; callers
+ * count; at most 2^21).  A request with zero keys is an error the kernel cannot report; callers
  * must include the new token's own slot.  ws: device workspace of at least
  * akv_decode_workspace_bytes(...) bytes.  scale <= 0 means 1/sqrt(d).  d == 64.
  */

@@ -228,7 +228,7 @@ int akv_segment_attention(const akv_plan* p, const void* dev_plan, const void* q
 uint64_t akv_decode_workspace_bytes(int32_t batch, int32_t hq, int32_t hkv, int32_t d, int64_t max_n) {
   (void)hkv;
   int32_t splits = 0, chunk = 0;
-  if (batch < 1 || hq < 1 || d < 1 || akv::decode_split_plan(max_n, &splits, &chunk)) return 0;
+  if (batch < 1 || hq < 1 || d < 1 || akv::decode_split_plan(batch, max_n, &splits, &chunk)) return 0;
   return 4 * akv::decode_ws_floats(batch, hq, d, splits);
 }
 
@@ -245,7 +245,7 @@ int akv_decode_attention(const void* q, const void* k_pool, const void* v_pool, 
   if (!q || !k_pool || !v_pool || !indptr || !indices || !out || !ws)
     return fail(AKV_EINVAL, "NULL pointer argument");
   int32_t splits = 0, chunk = 0;
-  if (akv::decode_split_plan(max_n, &splits, &chunk)) return fail(AKV_EINVAL, "max_n must be in [1, 2^31)");
+  if (akv::decode_split_plan(batch, max_n, &splits, &chunk)) return fail(AKV_EINVAL, "max_n must be in [1, 2^21]");
   if (ws_bytes < 4 * akv::decode_ws_floats(batch, hq, d, splits))
     return fail(AKV_EINVAL, "decode workspace too small");
   if (!(scale > 0.0f)) scale = 1.0f / std::sqrt((float)d);

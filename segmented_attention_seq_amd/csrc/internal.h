@@ -79,7 +79,7 @@ struct DecodeArgs {
   float* lse;
   float* ws;
 };
-int decode_split_plan(int64_t max_n, int32_t* splits, int32_t* chunk);
+int decode_split_plan(int32_t batch, int64_t max_n, int32_t* splits, int32_t* chunk);
 uint64_t decode_ws_floats(int32_t batch, int32_t hq, int32_t d, int32_t splits);
 int launch_decode(const DecodeArgs& a, void* stream);
 
