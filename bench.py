@@ -49,8 +49,8 @@ def parse_args():
     ap.add_argument("--only", default="", help="comma list of stages to run (profiling aid): "
                                                "restore,repos,decode")
     ap.add_argument("--copy-mb", type=int, default=0,
-                    help="before timing, run a plain device copy of this many MiB (3 times) so hardware "
-                         "byte counters can be scaled against a transfer of known size")
+                    help="before timing, run an elementwise multiply reading and writing this many MiB "
+                         "(3 times) so hardware byte counters can be scaled against a known transfer")
     return ap.parse_args()
 
 
@@ -176,10 +176,11 @@ def main():
     decode_bytes = n_keys * db.hkv * db.d * 2 * 2 + 4 * n_keys + 2 * dq.numel() * 2
     torch.cuda.synchronize()
     if args.copy_mb:
-        src = torch.ones(args.copy_mb << 20, dtype=torch.uint8, device=dev)
+        # a plain elementwise kernel that reads and writes exactly copy_mb MiB each
+        src = torch.ones((args.copy_mb << 20) // 4, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         for _ in range(3):
-            dst.copy_(src)
+            torch.mul(src, 2.0, out=dst)
         torch.cuda.synchronize()
         del src, dst
 
