@@ -67,11 +67,6 @@ __device__ __forceinline__ bf16x8 cat4(s16x4 a, s16x4 b) {
   return __builtin_bit_cast(bf16x8, v);
 }
 
-// Running-max slack (log2 units): the accumulators are rescaled only when a new
-// score exceeds the running max by more than this, so exp2 arguments stay <= 8
-// (p <= 256, exact in fp32, no bf16 overflow) and most tiles skip the rescale.
-constexpr float kRescaleSlack = 8.0f;
-
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
 
 struct TileSrc {
@@ -94,39 +89,76 @@ __device__ __forceinline__ TileSrc tile_src(int ent, int nvt, int voff, int r, i
   return ts;
 }
 
-// Per-wave state: 64 query tokens of one head.  The wave's Q rows live in LDS
-// (see load_q), not in registers.
+// Per-wave state: 64 query tokens of one head.
 struct WaveState {
+  bf16x8 qf[2][4];        // Q'^T B operand: qf[qb][ds] = Q'[q0 + 32qb + lq][h][16ds + 8lg .. +8]
   f32x16 o[2][2];         // O^T accumulators [qb][db]: d = 32db + 8(i/4) + 4lg + i%4, query 32qb + lq
   f32x16 s[2][2];         // S^T [kb][qb]: key 32kb + 8(i/4) + 4lg + i%4, query 32qb + lq
   bf16x8 pb[2][2][2];     // P^T B operand [kb][qb][half]
-  f32x16 cm[2];           // QK accumulator seed per query block: -running max (0 while unset)
-  float ms[2], lrun[2];   // running max (log2 units; -inf while unset) and sum per query column
+  float ms[2], lrun[2];   // exponent offset (log2 units) and running sum per query column
+  bool shifted;           // some column of the wave has a non-zero offset
 };
 
-// S'^T = K Q'^T - m for one 64-key tile held in LDS (16 MFMAs).  Q' is Q scaled by
-// scale*log2(e), and each accumulation chain starts from the running max seed, so
-// the MFMA result is already the exp2 argument.
-__device__ __forceinline__ void tile_qk(WaveState& w, const uint16_t* lkb, const uint16_t* lqw, int lq, int lg) {
+// S^T = K Q'^T for one 64-key tile held in LDS (16 MFMAs).  Q' is Q scaled by
+// scale*log2(e), so the scores are already in log2 units.
+__device__ __forceinline__ void tile_qk(WaveState& w, const uint16_t* lkb, int lq, int lg) {
+  const f32x16 zero = {};
 #pragma unroll
   for (int ds = 0; ds < 4; ++ds) {
-    bf16x8 b[2];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) b[qb] = *(const bf16x8*)(lqw + (qb * 32 + lq) * KP + ds * 16 + lg * 8);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const bf16x8 a = *(const bf16x8*)(lkb + (kb * 32 + lq) * KP + ds * 16 + lg * 8);
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb)
-        w.s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b[qb], ds ? w.s[kb][qb] : w.cm[qb], 0, 0, 0);
+        w.s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, w.qf[qb][ds], ds ? w.s[kb][qb] : zero,
+                                                              0, 0, 0);
     }
   }
 }
 
-// Mask (PARTIAL tiles), online softmax in log2 units, P -> bf16 B operand.  The
-// scores arrive already shifted by the running max m (tile_qk).  m is raised only
-// when a score exceeds it by more than kRescaleSlack (or on the first visible
-// score); then the accumulators are rescaled and the tile's scores shifted.
+// Bounds on a query column's tile probability sum.  The exponent offset m starts
+// at 0, so p = exp2(s - m) is used as is while the sums stay in (2^-40, 2^40]:
+// fp32/bf16 keep full relative precision anywhere in that range.  A sum above it
+// (a score far above m) or a column with no mass below it (scores far under m)
+// moves m to the tile's max and redoes the tile.
+constexpr float kSumHi = 1099511627776.0f;        // 2^40
+constexpr float kSumLo = 9.094947017729282e-13f;  // 2^-40
+
+__device__ __forceinline__ void tile_exp(WaveState& w, int qb, float& tot) {
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  float sum = 0.f;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      bf16x8 p;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) p[j] = (__bf16)__builtin_amdgcn_exp2f(w.s[kb][qb][8 * hf + j]);
+      w.pb[kb][qb][hf] = p;
+      // row sum of the rounded probabilities (the values the PV product uses)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bf16x2 pr = {p[2 * j], p[2 * j + 1]};
+        sum = __builtin_amdgcn_fdot2_f32_bf16(pr, one, sum, false);
+      }
+    }
+  tot = xhalf_sum(sum);
+}
+
+__device__ __forceinline__ float col_max(const WaveState& w, int qb) {
+  float m = -INFINITY;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) m = fmaxf(m, w.s[kb][qb][i]);
+  return xhalf_max(m);
+}
+
+__device__ __forceinline__ bool out_of_range(float tot, float lrun) {
+  return !(tot <= kSumHi) || (lrun + tot < kSumLo);
+}
+
+// Mask (PARTIAL tiles), online softmax in log2 units, P -> bf16 B operand.
 __device__ __forceinline__ void tile_softmax(WaveState& w, bool partial, const int* mtok, const int* mdrop,
                                              int q0, int lq, int lg) {
   if (partial) {
@@ -145,27 +177,27 @@ __device__ __forceinline__ void tile_softmax(WaveState& w, bool partial, const i
         }
     }
   }
-  float mx[2];
-  bool grow[2];
+  if (w.shifted) {
+    asm volatile("");  // only after a rescale: apply the column offsets
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    float m = -INFINITY;
+    for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) m = fmaxf(m, w.s[kb][qb][i]);
-    mx[qb] = xhalf_max(m);
-    grow[qb] = (w.ms[qb] == -INFINITY) ? (mx[qb] > -INFINITY) : (mx[qb] > kRescaleSlack);
+        for (int i = 0; i < 16; ++i) w.s[kb][qb][i] -= w.ms[qb];
   }
-  if (__any(grow[0] || grow[1])) {
-    asm volatile("");  // rare path: keep it behind the branch
+  float tot[2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) tile_exp(w, qb, tot[qb]);
+  if (__any(out_of_range(tot[0], w.lrun[0]) || out_of_range(tot[1], w.lrun[1]))) {
+    asm volatile("");  // rare: scores far above or below the offset
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      const bool unset = w.ms[qb] == -INFINITY;
-      const float shift = grow[qb] ? mx[qb] : 0.f;
-      const float mnew = (unset ? 0.f : w.ms[qb]) + shift;
-      const float alpha = grow[qb] ? __builtin_amdgcn_exp2f(w.ms[qb] - mnew) : 1.f;  // 0 while unset
-      w.ms[qb] = grow[qb] ? mnew : w.ms[qb];
+      const float mx = col_max(w, qb);
+      const bool on = out_of_range(tot[qb], w.lrun[qb]) && mx > -INFINITY;
+      const float shift = on ? mx : 0.f;
+      const float alpha = __builtin_amdgcn_exp2f(-shift);
+      w.ms[qb] += shift;
       w.lrun[qb] *= alpha;
 #pragma unroll
       for (int db = 0; db < 2; ++db)
@@ -175,32 +207,12 @@ __device__ __forceinline__ void tile_softmax(WaveState& w, bool partial, const i
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) w.s[kb][qb][i] -= shift;
-      const float seed = w.ms[qb] == -INFINITY ? 0.f : -w.ms[qb];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) w.cm[qb][i] = seed;
+      if (on) tile_exp(w, qb, tot[qb]);
     }
+    w.shifted = __any((w.ms[0] != 0.f) || (w.ms[1] != 0.f));
   }
-  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    float sum = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        bf16x8 p;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) p[j] = (__bf16)__builtin_amdgcn_exp2f(w.s[kb][qb][8 * hf + j]);
-        w.pb[kb][qb][hf] = p;
-        // row sum of the rounded probabilities (the values the PV product uses)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const bf16x2 pr = {p[2 * j], p[2 * j + 1]};
-          sum = __builtin_amdgcn_fdot2_f32_bf16(pr, one, sum, false);
-        }
-      }
-    w.lrun[qb] += xhalf_sum(sum);
-  }
+  for (int qb = 0; qb < 2; ++qb) w.lrun[qb] += tot[qb];
 }
 
 // O^T += V^T P^T for one tile (16 MFMAs); V^T comes from the row-major V tile
@@ -224,11 +236,10 @@ __device__ __forceinline__ void tile_pv(WaveState& w, const uint16_t* lvb, int l
       }
 }
 
-// The wave's 64 Q rows, scaled by sl2 = scale * log2(e) (re-rounded to bf16) so
-// that QK products come out in log2 units, go to the wave's private LDS block
-// lqw[64][KP]; each lane writes exactly the fragments it reads back in tile_qk.
-__device__ __forceinline__ void load_q(WaveState& w, uint16_t* lqw, const uint16_t* q, int q0, int q1, int hq,
-                                       int h, int lq, int lg, float sl2) {
+// Q fragments scaled by sl2 = scale * log2(e) (re-rounded to bf16) so that QK
+// products come out in log2 units.
+__device__ __forceinline__ void load_q(WaveState& w, const uint16_t* q, int q0, int q1, int hq, int h, int lq,
+                                       int lg, float sl2) {
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const int tok = q0 + qb * 32 + lq;
@@ -240,19 +251,19 @@ __device__ __forceinline__ void load_q(WaveState& w, uint16_t* lqw, const uint16
       bf16x8 b = __builtin_bit_cast(bf16x8, x);
 #pragma unroll
       for (int j = 0; j < 8; ++j) b[j] = (__bf16)((float)b[j] * sl2);
-      *(bf16x8*)(lqw + (qb * 32 + lq) * KP + ds * 16 + lg * 8) = b;
+      w.qf[qb][ds] = b;
     }
-    for (int i = 0; i < 16; ++i) w.cm[qb][i] = 0.f;
   }
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    w.ms[qb] = -INFINITY;
+    w.ms[qb] = 0.f;
     w.lrun[qb] = 0.f;
 #pragma unroll
     for (int db = 0; db < 2; ++db)
 #pragma unroll
       for (int i = 0; i < 16; ++i) w.o[qb][db][i] = 0.f;
   }
+  w.shifted = false;
 }
 
 __device__ __forceinline__ void store_out(const WaveState& w, uint16_t* out, float* lse, int q0, int q1,
@@ -340,7 +351,6 @@ struct TileStage {
 template <int GROUP>
 __global__ __launch_bounds__(64 * GROUP) void seg_attn_bf16(AKV_ATTN_PARAMS) {
   constexpr int NT = 64 * GROUP;
-  __shared__ __attribute__((aligned(16))) uint16_t lqs[GROUP][64 * KP];
   __shared__ __attribute__((aligned(16))) uint16_t lk[2][BK * KP];
   __shared__ __attribute__((aligned(16))) uint16_t lv[2][BK * VP];
   __shared__ int mtok[2][BK], mdrop[2][BK];
@@ -357,7 +367,7 @@ __global__ __launch_bounds__(64 * GROUP) void seg_attn_bf16(AKV_ATTN_PARAMS) {
   const float sl2 = scale * kLog2e;
 
   WaveState w;
-  load_q(w, lqs[wave], q, q0, q1, hq, h, lq, lg, sl2);
+  load_q(w, q, q0, q1, hq, h, lq, lg, sl2);
   TileStage<NT> st;
   if (t0 < t1) {
     const int e = tiles[t0];
@@ -374,7 +384,7 @@ __global__ __launch_bounds__(64 * GROUP) void seg_attn_bf16(AKV_ATTN_PARAMS) {
     if (has_next)
       st.fetch(tile_src(en, nvt, voff, r, tb, te, k, v, kver, vver), (en & 3) == AKV_TILE_PARTIAL, hkv, hk,
                tok_drop, ver_src);
-    tile_qk(w, lk[buf], lqs[wave], lq, lg);
+    tile_qk(w, lk[buf], lq, lg);
     tile_softmax(w, (ent & 3) == AKV_TILE_PARTIAL, mtok[buf], mdrop[buf], q0, lq, lg);
     tile_pv(w, lv[buf], lane);
     if (has_next) st.stash(lk[buf ^ 1], lv[buf ^ 1], mtok[buf ^ 1], mdrop[buf ^ 1], (en & 3) == AKV_TILE_PARTIAL);
@@ -393,7 +403,6 @@ __global__ __launch_bounds__(64 * GROUP) void seg_attn_bf16(AKV_ATTN_PARAMS) {
 // reader has passed a barrier.
 __global__ __launch_bounds__(512) void seg_attn_bf16_pp(AKV_ATTN_PARAMS) {
   constexpr int GROUP = 8, NT = 512, NSLOT = 3;
-  __shared__ __attribute__((aligned(16))) uint16_t lqs[GROUP][64 * KP];
   __shared__ __attribute__((aligned(16))) uint16_t lk[NSLOT][BK * KP];
   __shared__ __attribute__((aligned(16))) uint16_t lv[NSLOT][BK * VP];
   __shared__ int mtok[NSLOT][BK], mdrop[NSLOT][BK];
@@ -413,7 +422,7 @@ __global__ __launch_bounds__(512) void seg_attn_bf16_pp(AKV_ATTN_PARAMS) {
   if (n <= 0) return;  // uniform over the workgroup; every query sees at least itself
 
   WaveState w;
-  load_q(w, lqs[wave], q, q0, q1, hq, h, lq, lg, sl2);
+  load_q(w, q, q0, q1, hq, h, lq, lg, sl2);
   TileStage<NT> st;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
@@ -426,7 +435,7 @@ __global__ __launch_bounds__(512) void seg_attn_bf16_pp(AKV_ATTN_PARAMS) {
   }
   __syncthreads();
   if (lag) lds_barrier();
-  tile_qk(w, lk[0], lqs[wave], lq, lg);
+  tile_qk(w, lk[0], lq, lg);
   lds_barrier();
   int slot = 0;  // slot of tile i
   // tile entries i, i+1, i+2 in hand; entry i+3 is requested one iteration ahead
@@ -448,7 +457,7 @@ __global__ __launch_bounds__(512) void seg_attn_bf16_pp(AKV_ATTN_PARAMS) {
     tile_pv(w, lv[slot], lane);
     // P of tile i dies here, before the scores of tile i+1 are born: they share registers
     __builtin_amdgcn_sched_barrier(0);
-    if (i + 1 < n) tile_qk(w, lk[slot1], lqs[wave], lq, lg);
+    if (i + 1 < n) tile_qk(w, lk[slot1], lq, lg);
     __builtin_amdgcn_s_setprio(0);
     if (fetch2) st.stash(lk[slot2], lv[slot2], mtok[slot2], mdrop[slot2], p2);
     lds_barrier();

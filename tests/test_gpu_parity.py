@@ -344,3 +344,40 @@ def test_decode_equals_last_prefill_row():
     akv.decode_attention(qn, kfin, vfin, torch.tensor([0, rows.size], dtype=torch.int32, device="cuda"),
                          torch.arange(rows.size, dtype=torch.int32, device="cuda"), rows.size, o)
     assert (o[0].float() - out[T - 1].float()).abs().max().item() <= 2e-2
+
+
+@pytest.mark.parametrize("offset", [300.0, -300.0])
+def test_score_jumps_past_running_max_bf16(offset):
+    """Scores of a block of keys shifted by a common offset of |C|/8 = 37.5 (54 in
+    log2 units): +C on the later half of the keys (scores jump far above the
+    running max set by earlier tiles) or -C on the first third (the running max
+    starts far below later scores).  Exercises the rare rescale path of the
+    softmax (exp2 would overflow fp32 without it).  The offset rides on the
+    lowest-frequency RoPE pair (i = 31, which turns ~1e-5 rad per position, so it
+    is position independent here) with q = 1 on that dimension, so it shifts
+    whole blocks of scores without sharpening the softmax within them."""
+    tr = workload.agent_trajectory(3, seed=111, total=1400, keep=1, repos="every", user_len=64,
+                                   assist_range=(30, 200), tool_range=(100, 500), name=f"jump{offset}")
+    plan = akv.build_visibility(akv.ops_from_messages(tr.msg_len, tr.drop, tr.reposition))
+    q, k, v = workload.prefill_tensors(tr.n_tokens, 16, 2, 64, seed=112)
+    qf, kf = workload.bf16_bits_to_f32(q), workload.bf16_bits_to_f32(k)
+    T = tr.n_tokens
+    qf[:, :, 31], qf[:, :, 63] = 1.0, 0.0
+    kf[:, :, 31], kf[:, :, 63] = 0.0, 0.0
+    if offset > 0:
+        kf[T // 2:, :, 31] = offset
+    else:
+        kf[: T // 3, :, 31] = offset
+    q, k = workload.f32_to_bf16_bits(qf), workload.f32_to_bf16_bits(kf)
+    bufs = {"out": nan_like((T, 16, 64), torch.bfloat16), "lse": nan_like((T, 16), torch.float32)}
+    out, lse = akv.restore(plan, dev_tensor(q, True), dev_tensor(k, True), dev_tensor(v, True), BASE,
+                           with_lse=True, bufs=bufs)
+    torch.cuda.synchronize()
+    ops = oracle.canonical_ops(tr.msg_len, tr.drop, tr.reposition)
+    o_ref, l_ref = oracle.segment_attention(Bf16Rows(q), Bf16Rows(k), Bf16Rows(v), ops, base=BASE)
+    err = np.abs(host_f64(out) - o_ref).max()
+    # lse carries the offset (|.| up to ~40); bf16 rounding of q*scale*log2(e) scales it by 1 +- 2^-9
+    lerr = np.abs(host_f64(lse) - l_ref).max()
+    print(f"[attn jump offset={offset}] max-abs {err:.3e} lse {lerr:.3e}")
+    assert np.isfinite(host_f64(out)).all()
+    assert err <= 2e-2 and lerr <= 0.2
