@@ -38,6 +38,7 @@ typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
 
 constexpr int D = 64;    // head dim
 constexpr int BQ = 64;   // query tokens per work item (= 2 MFMA column blocks)
@@ -67,7 +68,6 @@ __device__ __forceinline__ bf16x8 cat4(s16x4 a, s16x4 b) {
   return __builtin_bit_cast(bf16x8, v);
 }
 
-typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
 
 struct TileSrc {
   const uint16_t* k;
@@ -99,20 +99,61 @@ struct WaveState {
   bool shifted;           // some column of the wave has a non-zero offset
 };
 
-// S^T = K Q'^T for one 64-key tile held in LDS (16 MFMAs).  Q' is Q scaled by
-// scale*log2(e), so the scores are already in log2 units.
-__device__ __forceinline__ void tile_qk(WaveState& w, const uint16_t* lkb, int lq, int lg) {
+// Operand fragments of one tile, read from LDS ahead of the MFMAs that use them.
+struct KFrag { bf16x8 a[4][2]; };        // K rows: a[ds][kb] = K[32kb + lq][16ds + 8lg .. +8]
+struct VFrag { bf16x8 a[2][2][2]; };     // V^T: a[kb][hf][db] (rows d, columns keys of the half)
+
+// 16 bytes of row `row` at column 16ds + 8lg of a K-pitched LDS tile (K or Q').
+__device__ __forceinline__ bf16x8 row_frag(const uint16_t* base, int row, int ds, int lg) {
+  return *(const bf16x8*)(base + row * KP + ds * 16 + lg * 8);
+}
+
+// Q' operand of query block qb, d slice ds: from registers, or (QL) from the
+// wave's Q' rows in LDS.
+template <bool QL>
+__device__ __forceinline__ bf16x8 q_frag(const WaveState& w, const uint16_t* lqw, int qb, int ds, int lq, int lg) {
+  if (QL) return row_frag(lqw, qb * 32 + lq, ds, lg);
+  return w.qf[qb][ds];
+}
+
+// S^T = K Q'^T for one 64-key tile (16 MFMAs), operands read as they are used.
+// Q' is Q scaled by scale*log2(e), so the scores are already in log2 units.
+template <bool QL>
+__device__ __forceinline__ void tile_qk(WaveState& w, const uint16_t* lkb, const uint16_t* lqw, int lq, int lg) {
   const f32x16 zero = {};
 #pragma unroll
   for (int ds = 0; ds < 4; ++ds) {
+    const bf16x8 b0 = q_frag<QL>(w, lqw, 0, ds, lq, lg), b1 = q_frag<QL>(w, lqw, 1, ds, lq, lg);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const bf16x8 a = *(const bf16x8*)(lkb + (kb * 32 + lq) * KP + ds * 16 + lg * 8);
+      const bf16x8 a = row_frag(lkb, kb * 32 + lq, ds, lg);
+      w.s[kb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b0, ds ? w.s[kb][0] : zero, 0, 0, 0);
+      w.s[kb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b1, ds ? w.s[kb][1] : zero, 0, 0, 0);
+    }
+  }
+}
+
+// tile_qk with the K fragments and the first Q' slice (b0) already in registers;
+// the remaining Q' slices are read from LDS one d slice ahead of their MFMAs.
+__device__ __forceinline__ void mfma_qk_lq(WaveState& w, const KFrag& f, const bf16x8 (&b0)[2], const uint16_t* lqw,
+                                           int lq, int lg) {
+  const f32x16 zero = {};
+  bf16x8 b[2][2];
+  b[0][0] = b0[0];
+  b[0][1] = b0[1];
+#pragma unroll
+  for (int ds = 0; ds < 4; ++ds) {
+    if (ds < 3) {
+      b[(ds + 1) & 1][0] = row_frag(lqw, lq, ds + 1, lg);
+      b[(ds + 1) & 1][1] = row_frag(lqw, 32 + lq, ds + 1, lg);
+    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb)
-        w.s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, w.qf[qb][ds], ds ? w.s[kb][qb] : zero,
+        w.s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[ds][kb], b[ds & 1][qb], ds ? w.s[kb][qb] : zero,
                                                               0, 0, 0);
-    }
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -124,6 +165,9 @@ __device__ __forceinline__ void tile_qk(WaveState& w, const uint16_t* lkb, int l
 constexpr float kSumHi = 1099511627776.0f;        // 2^40
 constexpr float kSumLo = 9.094947017729282e-13f;  // 2^-40
 
+// P = exp2(S - m) rounded to bf16 into the PV B operand, and the column's tile
+// sum of those rounded values (the weights the PV product uses, so the output is
+// normalised by exactly their total), summed with bf16 dot2 against ones.
 __device__ __forceinline__ void tile_exp(WaveState& w, int qb, float& tot) {
   const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
   float sum = 0.f;
@@ -135,7 +179,7 @@ __device__ __forceinline__ void tile_exp(WaveState& w, int qb, float& tot) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) p[j] = (__bf16)__builtin_amdgcn_exp2f(w.s[kb][qb][8 * hf + j]);
       w.pb[kb][qb][hf] = p;
-      // row sum of the rounded probabilities (the values the PV product uses)
+      asm volatile("" ::"v"(p));  // pack here, not after the range check (fewer live registers)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const bf16x2 pr = {p[2 * j], p[2 * j + 1]};
@@ -158,9 +202,10 @@ __device__ __forceinline__ bool out_of_range(float tot, float lrun) {
   return !(tot <= kSumHi) || (lrun + tot < kSumLo);
 }
 
-// Mask (PARTIAL tiles), online softmax in log2 units, P -> bf16 B operand.
-__device__ __forceinline__ void tile_softmax(WaveState& w, bool partial, const int* mtok, const int* mdrop,
-                                             int q0, int lq, int lg) {
+// Scores of a tile made ready for exp2: hidden pairs of a PARTIAL tile set to
+// -inf, and the column offsets subtracted once any column has moved its offset.
+__device__ __forceinline__ void prep_scores(WaveState& w, bool partial, const int* mtok, const int* mdrop, int q0,
+                                            int lq, int lg) {
   if (partial) {
     asm volatile("");  // keep this rare path behind its branch (not speculated into every tile)
 #pragma unroll
@@ -186,15 +231,27 @@ __device__ __forceinline__ void tile_softmax(WaveState& w, bool partial, const i
 #pragma unroll
         for (int i = 0; i < 16; ++i) w.s[kb][qb][i] -= w.ms[qb];
   }
+}
+
+// Mask (PARTIAL tiles), online softmax in log2 units, P -> bf16 B operand.  The
+// scores die as P is formed; the rare path that moves a column's offset
+// recomputes them from the tile's K rows (still in LDS at lkb).
+template <bool QL>
+__device__ __forceinline__ void tile_softmax(WaveState& w, bool partial, const int* mtok, const int* mdrop,
+                                             const uint16_t* lkb, const uint16_t* lqw, int q0, int lq, int lg) {
+  prep_scores(w, partial, mtok, mdrop, q0, lq, lg);
   float tot[2];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) tile_exp(w, qb, tot[qb]);
-  if (__any(out_of_range(tot[0], w.lrun[0]) || out_of_range(tot[1], w.lrun[1]))) {
+  const bool bad0 = out_of_range(tot[0], w.lrun[0]), bad1 = out_of_range(tot[1], w.lrun[1]);
+  if (__any(bad0 || bad1)) {
     asm volatile("");  // rare: scores far above or below the offset
+    tile_qk<QL>(w, lkb, lqw, lq, lg);
+    prep_scores(w, partial, mtok, mdrop, q0, lq, lg);
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       const float mx = col_max(w, qb);
-      const bool on = out_of_range(tot[qb], w.lrun[qb]) && mx > -INFINITY;
+      const bool on = (qb ? bad1 : bad0) && mx > -INFINITY;
       const float shift = on ? mx : 0.f;
       const float alpha = __builtin_amdgcn_exp2f(-shift);
       w.ms[qb] += shift;
@@ -207,7 +264,7 @@ __device__ __forceinline__ void tile_softmax(WaveState& w, bool partial, const i
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) w.s[kb][qb][i] -= shift;
-      if (on) tile_exp(w, qb, tot[qb]);
+      tile_exp(w, qb, tot[qb]);  // unchanged for a column whose offset stays
     }
     w.shifted = __any((w.ms[0] != 0.f) || (w.ms[1] != 0.f));
   }
@@ -215,9 +272,10 @@ __device__ __forceinline__ void tile_softmax(WaveState& w, bool partial, const i
   for (int qb = 0; qb < 2; ++qb) w.lrun[qb] += tot[qb];
 }
 
-// O^T += V^T P^T for one tile (16 MFMAs); V^T comes from the row-major V tile
-// through the transposing LDS read.
-__device__ __forceinline__ void tile_pv(WaveState& w, const uint16_t* lvb, int lane) {
+// V^T fragments of one tile from the row-major V tile through the transposing LDS
+// read (lane i of a 16-lane group gets element i%4 of the 8-byte chunk that lane
+// 4k + i/4 addresses, for k = 0..3).
+__device__ __forceinline__ void read_vt(VFrag& f, const uint16_t* lvb, int lane) {
   const int G = lane >> 4, i16 = lane & 15;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
@@ -229,17 +287,61 @@ __device__ __forceinline__ void tile_pv(WaveState& w, const uint16_t* lvb, int l
         const int dc = db * 32 + 16 * (G & 1) + 4 * (i16 & 3);
         const s16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lvb + key * VP + dc));
         const s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lvb + (key + 8) * VP + dc));
-        const bf16x8 a = cat4(r0, r1);
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-          w.o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, w.pb[kb][qb][hf], w.o[qb][db], 0, 0, 0);
+        f.a[kb][hf][db] = cat4(r0, r1);
       }
 }
 
-// Q fragments scaled by sl2 = scale * log2(e) (re-rounded to bf16) so that QK
-// products come out in log2 units.
-__device__ __forceinline__ void load_q(WaveState& w, const uint16_t* q, int q0, int q1, int hq, int h, int lq,
-                                       int lg, float sl2) {
+// O^T += V^T P^T for one tile (16 MFMAs).
+__device__ __forceinline__ void mfma_pv(WaveState& w, const VFrag& f) {
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+          w.o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[kb][hf][db], w.pb[kb][qb][hf], w.o[qb][db], 0, 0, 0);
+}
+
+// mfma_pv with the next tile's K fragments read in between: after the 4 MFMAs of
+// each (kb, hf) quarter, whose V^T and P registers then die, the two K fragments
+// of one 16-wide d slice are read (and, after the last quarter, the first Q'
+// slice).  The reads' latency hides behind the MFMAs.
+__device__ __forceinline__ void mfma_pv_read_k(WaveState& w, const VFrag& f, KFrag& kf, bf16x8 (&q0f)[2],
+                                               const uint16_t* lkb, const uint16_t* lqw, int lq, int lg) {
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+          w.o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[kb][hf][db], w.pb[kb][qb][hf], w.o[qb][db], 0, 0, 0);
+      const int ds = kb * 2 + hf;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) kf.a[ds][kk] = row_frag(lkb, kk * 32 + lq, ds, lg);
+      if (ds == 3) {
+        q0f[0] = row_frag(lqw, lq, 0, lg);
+        q0f[1] = row_frag(lqw, 32 + lq, 0, lg);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+__device__ __forceinline__ void tile_pv(WaveState& w, const uint16_t* lvb, int lane) {
+  VFrag f;
+  read_vt(f, lvb, lane);
+  mfma_pv(w, f);
+}
+
+// Q' = Q scaled by sl2 = scale * log2(e) (re-rounded to bf16), so that QK
+// products come out in log2 units; kept in registers, or (QL) in the wave's LDS
+// rows lqw (64 rows, K pitch).
+template <bool QL>
+__device__ __forceinline__ void load_q(WaveState& w, uint16_t* lqw, const uint16_t* q, int q0, int q1, int hq, int h,
+                                       int lq, int lg, float sl2) {
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const int tok = q0 + qb * 32 + lq;
@@ -251,7 +353,8 @@ __device__ __forceinline__ void load_q(WaveState& w, const uint16_t* q, int q0, 
       bf16x8 b = __builtin_bit_cast(bf16x8, x);
 #pragma unroll
       for (int j = 0; j < 8; ++j) b[j] = (__bf16)((float)b[j] * sl2);
-      w.qf[qb][ds] = b;
+      if (QL) *(bf16x8*)(lqw + (qb * 32 + lq) * KP + ds * 16 + lg * 8) = b;
+      else w.qf[qb][ds] = b;
     }
   }
 #pragma unroll
@@ -367,7 +470,7 @@ __global__ __launch_bounds__(64 * GROUP) void seg_attn_bf16(AKV_ATTN_PARAMS) {
   const float sl2 = scale * kLog2e;
 
   WaveState w;
-  load_q(w, q, q0, q1, hq, h, lq, lg, sl2);
+  load_q<false>(w, nullptr, q, q0, q1, hq, h, lq, lg, sl2);
   TileStage<NT> st;
   if (t0 < t1) {
     const int e = tiles[t0];
@@ -384,8 +487,8 @@ __global__ __launch_bounds__(64 * GROUP) void seg_attn_bf16(AKV_ATTN_PARAMS) {
     if (has_next)
       st.fetch(tile_src(en, nvt, voff, r, tb, te, k, v, kver, vver), (en & 3) == AKV_TILE_PARTIAL, hkv, hk,
                tok_drop, ver_src);
-    tile_qk(w, lk[buf], lq, lg);
-    tile_softmax(w, (ent & 3) == AKV_TILE_PARTIAL, mtok[buf], mdrop[buf], q0, lq, lg);
+    tile_qk<false>(w, lk[buf], nullptr, lq, lg);
+    tile_softmax<false>(w, (ent & 3) == AKV_TILE_PARTIAL, mtok[buf], mdrop[buf], lk[buf], nullptr, q0, lq, lg);
     tile_pv(w, lv[buf], lane);
     if (has_next) st.stash(lk[buf ^ 1], lv[buf ^ 1], mtok[buf ^ 1], mdrop[buf ^ 1], (en & 3) == AKV_TILE_PARTIAL);
     lds_barrier();
@@ -406,6 +509,7 @@ __global__ __launch_bounds__(512) void seg_attn_bf16_pp(AKV_ATTN_PARAMS) {
   __shared__ __attribute__((aligned(16))) uint16_t lk[NSLOT][BK * KP];
   __shared__ __attribute__((aligned(16))) uint16_t lv[NSLOT][BK * VP];
   __shared__ int mtok[NSLOT][BK], mdrop[NSLOT][BK];
+  __shared__ __attribute__((aligned(16))) uint16_t lqs[GROUP][64 * KP];
 
   const int hk = blockIdx.x % hkv;
   const int item = order[blockIdx.x / hkv];
@@ -415,6 +519,7 @@ __global__ __launch_bounds__(512) void seg_attn_bf16_pp(AKV_ATTN_PARAMS) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int h = hk * GROUP + wave;
   const int lq = lane & 31, lg = lane >> 5;
+  uint16_t* lqw = lqs[wave];  // this wave's Q' rows (written and read by this wave only)
   const bool lag = wave >= 4;  // group B
   const int nvt = (r + BK - 1) / BK;
   const float sl2 = scale * kLog2e;
@@ -422,7 +527,7 @@ __global__ __launch_bounds__(512) void seg_attn_bf16_pp(AKV_ATTN_PARAMS) {
   if (n <= 0) return;  // uniform over the workgroup; every query sees at least itself
 
   WaveState w;
-  load_q(w, q, q0, q1, hq, h, lq, lg, sl2);
+  load_q<true>(w, lqw, q, q0, q1, hq, h, lq, lg, sl2);
   TileStage<NT> st;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
@@ -435,7 +540,7 @@ __global__ __launch_bounds__(512) void seg_attn_bf16_pp(AKV_ATTN_PARAMS) {
   }
   __syncthreads();
   if (lag) lds_barrier();
-  tile_qk(w, lk[0], lq, lg);
+  tile_qk<true>(w, lk[0], lqw, lq, lg);
   lds_barrier();
   int slot = 0;  // slot of tile i
   // tile entries i, i+1, i+2 in hand; entry i+3 is requested one iteration ahead
@@ -448,16 +553,23 @@ __global__ __launch_bounds__(512) void seg_attn_bf16_pp(AKV_ATTN_PARAMS) {
     const int slot1 = slot == NSLOT - 1 ? 0 : slot + 1;
     const int slot2 = slot1 == NSLOT - 1 ? 0 : slot1 + 1;
     if (fetch2) st.fetch(tile_src(e2, nvt, voff, r, tb, te, k, v, kver, vver), p2, hkv, hk, tok_drop, ver_src);
-    // phase 1 (VALU): softmax of tile i
-    tile_softmax(w, (ent & 3) == AKV_TILE_PARTIAL, mtok[slot], mdrop[slot], q0, lq, lg);
-    lds_barrier();
-    // phase 2 (MFMA): PV of tile i, QK of tile i+1; then tile i+2 goes to the slot
-    // freed by tile i-1 (its last reader finished before the barrier above)
-    __builtin_amdgcn_s_setprio(1);
-    tile_pv(w, lv[slot], lane);
-    // P of tile i dies here, before the scores of tile i+1 are born: they share registers
+    // phase 1 (VALU): softmax of tile i.  The V^T fragments for its PV product are
+    // read first, so their LDS latency hides behind the softmax.
+    VFrag vf;
+    read_vt(vf, lv[slot], lane);
     __builtin_amdgcn_sched_barrier(0);
-    if (i + 1 < n) tile_qk(w, lk[slot1], lq, lg);
+    tile_softmax<true>(w, (ent & 3) == AKV_TILE_PARTIAL, mtok[slot], mdrop[slot], lk[slot], lqw, q0, lq, lg);
+    lds_barrier();
+    // phase 2 (MFMA): PV of tile i, QK of tile i+1 (its K fragments are read before
+    // the PV MFMAs, which hide their latency); then tile i+2 goes to the slot freed
+    // by tile i-1 (its last reader finished before the barrier above)
+    __builtin_amdgcn_s_setprio(1);
+    // (after the last tile, slot1 holds an older tile: its K reads are harmless and unused)
+    KFrag kf;
+    bf16x8 q0f[2];
+    mfma_pv_read_k(w, vf, kf, q0f, lk[slot1], lqw, lq, lg);
+    // P of tile i is dead here, before the scores of tile i+1 are born: they share registers
+    if (i + 1 < n) mfma_qk_lq(w, kf, q0f, lqw, lq, lg);
     __builtin_amdgcn_s_setprio(0);
     if (fetch2) st.stash(lk[slot2], lv[slot2], mtok[slot2], mdrop[slot2], p2);
     lds_barrier();
