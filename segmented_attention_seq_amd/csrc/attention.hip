@@ -36,6 +36,7 @@ namespace {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
@@ -59,8 +60,13 @@ __device__ __forceinline__ float xhalf_sum(float x) {
 // Workgroup barrier that orders LDS only: waits for this wave's LDS accesses
 // (lgkmcnt) but lets global loads into registers stay in flight across it (a
 // __syncthreads release fence would drain them).  The memory clobber keeps the
-// compiler from moving LDS accesses across the barrier.
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+// compiler from moving LDS accesses across the barrier, the scheduling fences
+// keep it from moving register-only work (exp, MFMA) from one phase to the other.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
 
 __device__ __forceinline__ bf16x8 cat4(s16x4 a, s16x4 b) {
   typedef __attribute__((__vector_size__(8 * sizeof(short)))) short s16x8;
@@ -204,6 +210,7 @@ __device__ __forceinline__ bool out_of_range(float tot, float lrun) {
 
 // Scores of a tile made ready for exp2: hidden pairs of a PARTIAL tile set to
 // -inf, and the column offsets subtracted once any column has moved its offset.
+template <bool OFFSETS = true>
 __device__ __forceinline__ void prep_scores(WaveState& w, bool partial, const int* mtok, const int* mdrop, int q0,
                                             int lq, int lg) {
   if (partial) {
@@ -222,7 +229,7 @@ __device__ __forceinline__ void prep_scores(WaveState& w, bool partial, const in
         }
     }
   }
-  if (w.shifted) {
+  if (OFFSETS && w.shifted) {
     asm volatile("");  // only after a rescale: apply the column offsets
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
@@ -272,6 +279,42 @@ __device__ __forceinline__ void tile_softmax(WaveState& w, bool partial, const i
   for (int qb = 0; qb < 2; ++qb) w.lrun[qb] += tot[qb];
 }
 
+// Fast-pass softmax: the exponent offset stays 0 and nothing is summed here.
+// P = exp2(S) rounded to bf16 (hidden pairs of a PARTIAL tile give 0); the column
+// sums come from the matrix cores in the MFMA phase, and the range of the final
+// sums is checked once per work item.
+__device__ __forceinline__ void tile_softmax_fast(WaveState& w, bool partial, const int* mtok, const int* mdrop,
+                                                  int q0, int lq, int lg) {
+  prep_scores<false>(w, partial, mtok, mdrop, q0, lq, lg);
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        bf16x8 p;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) p[j] = (__bf16)__builtin_amdgcn_exp2f(w.s[kb][qb][8 * hf + j]);
+        w.pb[kb][qb][hf] = p;
+      }
+}
+
+// A operand of the column-sum MFMA (16x16x32): row m = lane%16, k = 8(lane/16) + i.
+// Element (m, k) is 1 where bit 2 of m equals bit 3 of k.  With a P^T slice of 16
+// keys x 32 queries as the B operand (query 32qb + lane%32, keys 8(lane/32) + i,
+// read as k = 8(lane/16) + i, column lane%16), result rows 0-3 and 8-11 sum the
+// query columns 0-15 and rows 4-7 and 12-15 the columns 16-31 over the 16 keys, so
+// every register of lane l holds the sum of query column 32qb + l%32, the column
+// that lane owns in the softmax.
+__device__ __forceinline__ bf16x8 colsum_selector(int lane) {
+  const bool on = (((lane & 15) >> 2) & 1) == ((lane >> 4) & 1);
+  const __bf16 x = on ? (__bf16)1.0f : (__bf16)0.0f;
+  bf16x8 a;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) a[j] = x;
+  return a;
+}
+
 // V^T fragments of one tile from the row-major V tile through the transposing LDS
 // read (lane i of a 16-lane group gets element i%4 of the 8-byte chunk that lane
 // 4k + i/4 addresses, for k = 0..3).
@@ -307,9 +350,12 @@ __device__ __forceinline__ void mfma_pv(WaveState& w, const VFrag& f) {
 // mfma_pv with the next tile's K fragments read in between: after the 4 MFMAs of
 // each (kb, hf) quarter, whose V^T and P registers then die, the two K fragments
 // of one 16-wide d slice are read (and, after the last quarter, the first Q'
-// slice).  The reads' latency hides behind the MFMAs.
+// slice).  The reads' latency hides behind the MFMAs.  With SUMS, each quarter
+// also adds its P slice into the column sums ls (colsum_selector).
+template <bool SUMS>
 __device__ __forceinline__ void mfma_pv_read_k(WaveState& w, const VFrag& f, KFrag& kf, bf16x8 (&q0f)[2],
-                                               const uint16_t* lkb, const uint16_t* lqw, int lq, int lg) {
+                                               f32x4 (&ls)[2], bf16x8 sel, const uint16_t* lkb,
+                                               const uint16_t* lqw, int lq, int lg) {
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -319,6 +365,11 @@ __device__ __forceinline__ void mfma_pv_read_k(WaveState& w, const VFrag& f, KFr
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
           w.o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[kb][hf][db], w.pb[kb][qb][hf], w.o[qb][db], 0, 0, 0);
+      if (SUMS) {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+          ls[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel, w.pb[kb][qb][hf], ls[qb], 0, 0, 0);
+      }
       const int ds = kb * 2 + hf;
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) kf.a[ds][kk] = row_frag(lkb, kk * 32 + lq, ds, lg);
@@ -504,31 +555,21 @@ __global__ __launch_bounds__(64 * GROUP) void seg_attn_bf16(AKV_ATTN_PARAMS) {
 // three LDS slots; tile t+2 is fetched to registers at the start of iteration t
 // and written to its slot one phase later, after its previous occupant's last
 // reader has passed a barrier.
-__global__ __launch_bounds__(512) void seg_attn_bf16_pp(AKV_ATTN_PARAMS) {
-  constexpr int GROUP = 8, NT = 512, NSLOT = 3;
-  __shared__ __attribute__((aligned(16))) uint16_t lk[NSLOT][BK * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t lv[NSLOT][BK * VP];
-  __shared__ int mtok[NSLOT][BK], mdrop[NSLOT][BK];
-  __shared__ __attribute__((aligned(16))) uint16_t lqs[GROUP][64 * KP];
+//
+// SAFE = false is the fast pass (offset 0, column sums on the matrix cores);
+// SAFE = true is the lazily-rescaled softmax with per-tile range checks.
+constexpr int kPPThreads = 512;
+constexpr int kPPSlots = 3;
 
-  const int hk = blockIdx.x % hkv;
-  const int item = order[blockIdx.x / hkv];
-  const int* dsc = item_desc + item * ID_WORDS;
-  const int q0 = dsc[ID_QBEGIN], q1 = dsc[ID_QEND], tb = dsc[ID_TB], te = dsc[ID_TE];
-  const int r = dsc[ID_R], voff = dsc[ID_VEROFF], t0 = dsc[ID_TILE0], t1 = dsc[ID_TILE1];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int h = hk * GROUP + wave;
-  const int lq = lane & 31, lg = lane >> 5;
-  uint16_t* lqw = lqs[wave];  // this wave's Q' rows (written and read by this wave only)
-  const bool lag = wave >= 4;  // group B
-  const int nvt = (r + BK - 1) / BK;
-  const float sl2 = scale * kLog2e;
-  const int n = t1 - t0;
-  if (n <= 0) return;  // uniform over the workgroup; every query sees at least itself
-
-  WaveState w;
-  load_q<true>(w, lqw, q, q0, q1, hq, h, lq, lg, sl2);
-  TileStage<NT> st;
+template <bool SAFE>
+__device__ __forceinline__ void pp_pipeline(WaveState& w, f32x4 (&ls)[2], bf16x8 sel, TileStage<kPPThreads>& st,
+                                            uint16_t (*lk)[BK * KP], uint16_t (*lv)[BK * VP], int (*mtok)[BK],
+                                            int (*mdrop)[BK], const uint16_t* lqw, const int* tiles, int t0, int n,
+                                            int nvt, int voff, int r, int tb, int te, const uint16_t* k,
+                                            const uint16_t* v, const uint16_t* kver, const uint16_t* vver, int hkv,
+                                            int hk, const int* tok_drop, const int* ver_src, int q0, int lq, int lg,
+                                            int lane, bool lag) {
+  constexpr int NSLOT = kPPSlots;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     if (j < n) {
@@ -558,7 +599,10 @@ __global__ __launch_bounds__(512) void seg_attn_bf16_pp(AKV_ATTN_PARAMS) {
     VFrag vf;
     read_vt(vf, lv[slot], lane);
     __builtin_amdgcn_sched_barrier(0);
-    tile_softmax<true>(w, (ent & 3) == AKV_TILE_PARTIAL, mtok[slot], mdrop[slot], lk[slot], lqw, q0, lq, lg);
+    if (SAFE)
+      tile_softmax<true>(w, (ent & 3) == AKV_TILE_PARTIAL, mtok[slot], mdrop[slot], lk[slot], lqw, q0, lq, lg);
+    else
+      tile_softmax_fast(w, (ent & 3) == AKV_TILE_PARTIAL, mtok[slot], mdrop[slot], q0, lq, lg);
     lds_barrier();
     // phase 2 (MFMA): PV of tile i, QK of tile i+1 (its K fragments are read before
     // the PV MFMAs, which hide their latency); then tile i+2 goes to the slot freed
@@ -567,7 +611,7 @@ __global__ __launch_bounds__(512) void seg_attn_bf16_pp(AKV_ATTN_PARAMS) {
     // (after the last tile, slot1 holds an older tile: its K reads are harmless and unused)
     KFrag kf;
     bf16x8 q0f[2];
-    mfma_pv_read_k(w, vf, kf, q0f, lk[slot1], lqw, lq, lg);
+    mfma_pv_read_k<!SAFE>(w, vf, kf, q0f, ls, sel, lk[slot1], lqw, lq, lg);
     // P of tile i is dead here, before the scores of tile i+1 are born: they share registers
     if (i + 1 < n) mfma_qk_lq(w, kf, q0f, lqw, lq, lg);
     __builtin_amdgcn_s_setprio(0);
@@ -579,6 +623,63 @@ __global__ __launch_bounds__(512) void seg_attn_bf16_pp(AKV_ATTN_PARAMS) {
     e2n = e3n;
   }
   if (!lag) lds_barrier();
+}
+
+// Largest final column sum the fast pass accepts: P <= 2^100 keeps every fp32
+// product and accumulation of the PV step far from overflow.
+constexpr float kFastHi = 1.2676506002282294e30f;  // 2^100
+
+__global__ __launch_bounds__(kPPThreads) void seg_attn_bf16_pp(AKV_ATTN_PARAMS) {
+  constexpr int GROUP = 8;
+  __shared__ __attribute__((aligned(16))) uint16_t lk[kPPSlots][BK * KP];
+  __shared__ __attribute__((aligned(16))) uint16_t lv[kPPSlots][BK * VP];
+  __shared__ int mtok[kPPSlots][BK], mdrop[kPPSlots][BK];
+  __shared__ __attribute__((aligned(16))) uint16_t lqs[GROUP][64 * KP];
+  __shared__ int redo;
+
+  const int hk = blockIdx.x % hkv;
+  const int item = order[blockIdx.x / hkv];
+  const int* dsc = item_desc + item * ID_WORDS;
+  const int q0 = dsc[ID_QBEGIN], q1 = dsc[ID_QEND], tb = dsc[ID_TB], te = dsc[ID_TE];
+  const int r = dsc[ID_R], voff = dsc[ID_VEROFF], t0 = dsc[ID_TILE0], t1 = dsc[ID_TILE1];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int h = hk * GROUP + wave;
+  const int lq = lane & 31, lg = lane >> 5;
+  uint16_t* lqw = lqs[wave];  // this wave's Q' rows (written and read by this wave only)
+  const bool lag = wave >= 4;  // group B
+  const int nvt = (r + BK - 1) / BK;
+  const float sl2 = scale * kLog2e;
+  const int n = t1 - t0;
+  if (n <= 0) return;  // uniform over the workgroup; every query sees at least itself
+  if (threadIdx.x == 0) redo = 0;  // published by the first barrier of the pipeline
+
+  WaveState w;
+  load_q<true>(w, lqw, q, q0, q1, hq, h, lq, lg, sl2);
+  TileStage<kPPThreads> st;
+  const bf16x8 sel = colsum_selector(lane);
+  f32x4 ls[2] = {};
+  pp_pipeline<false>(w, ls, sel, st, lk, lv, mtok, mdrop, lqw, tiles, t0, n, nvt, voff, r, tb, te, k, v, kver, vver,
+                     hkv, hk, tok_drop, ver_src, q0, lq, lg, lane, lag);
+  // Accept the fast pass when every real query column's sum lies in [2^-40, 2^100]
+  // (also false for inf/NaN); otherwise the workgroup redoes the item with the
+  // rescaling softmax.
+  bool bad = false;
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const float l = ls[qb][0];
+    bad |= (q0 + qb * 32 + lq < q1) && !(l >= kSumLo && l <= kFastHi);
+  }
+  if (__any(bad) && lane == 0) redo = 1;
+  lds_barrier();
+  if (__builtin_amdgcn_readfirstlane(redo)) {
+    asm volatile("");  // rare: keep the second pipeline out of the common path
+    load_q<false>(w, nullptr, q, q0, q0, hq, h, lq, lg, 0.f);  // resets O, offsets and sums (Q' stays in LDS)
+    pp_pipeline<true>(w, ls, sel, st, lk, lv, mtok, mdrop, lqw, tiles, t0, n, nvt, voff, r, tb, te, k, v, kver,
+                      vver, hkv, hk, tok_drop, ver_src, q0, lq, lg, lane, lag);
+  } else {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) w.lrun[qb] = ls[qb][0];
+  }
   store_out(w, out, lse, q0, q1, hq, h, lq, lg);
 }
 
