@@ -203,10 +203,14 @@ int akv_segment_attention(const akv_plan* plan, const void* dev_plan,
  * One query token per request b < batch: out[b][h] = attention of q[b][h] over the
  * pool rows indices[indptr[b] .. indptr[b+1]) (its active cache plus its own new
  * slot, gathered at page size 1).  q, k_pool, v_pool: bf16; indptr/indices: device
- * int32; max_n >= every request's key count (host-side bound, sets the split
- * count; at most 2^21).  A request with zero keys is an error the kernel cannot report; callers
- * must include the new token's own slot.  ws: device workspace of at least
- * akv_decode_workspace_bytes(...) bytes.  scale <= 0 means 1/sqrt(d).  d == 64.
+ * int32 (indptr[batch] = total gathered keys).  max_n: host-side bound on every
+ * request's key count, in [1, 2^31); it is checked but does not shape the launch,
+ * which cuts all the batch's gathered keys into equal ranges, one per CU, and merges
+ * each request's partials.  A request with zero keys is an error the kernel cannot
+ * report (its output is left unwritten); callers must include the new token's own
+ * slot.  ws: device workspace of at least akv_decode_workspace_bytes(...) bytes
+ * (about (256 + batch) * hq * 264 bytes), owned by the caller; its contents are
+ * scratch.  scale <= 0 means 1/sqrt(d).  d == 64.
  */
 uint64_t akv_decode_workspace_bytes(int32_t batch, int32_t hq, int32_t hkv, int32_t d, int64_t max_n);
 int akv_decode_attention(const void* q, const void* k_pool, const void* v_pool,

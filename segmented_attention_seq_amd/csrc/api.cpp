@@ -1,4 +1,5 @@
 // C ABI of libakv: argument validation, error reporting, dispatch.
+#include <cstdint>
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -227,9 +228,8 @@ int akv_segment_attention(const akv_plan* p, const void* dev_plan, const void* q
 
 uint64_t akv_decode_workspace_bytes(int32_t batch, int32_t hq, int32_t hkv, int32_t d, int64_t max_n) {
   (void)hkv;
-  int32_t splits = 0, chunk = 0;
-  if (batch < 1 || hq < 1 || d < 1 || akv::decode_split_plan(batch, max_n, &splits, &chunk)) return 0;
-  return 4 * akv::decode_ws_floats(batch, hq, d, splits);
+  if (batch < 1 || hq < 1 || d < 1 || max_n < 1 || max_n > INT32_MAX) return 0;
+  return 4 * akv::decode_ws_floats(batch, hq, d);
 }
 
 int akv_decode_attention(const void* q, const void* k_pool, const void* v_pool, const int32_t* indptr,
@@ -244,13 +244,10 @@ int akv_decode_attention(const void* q, const void* k_pool, const void* v_pool, 
   if (batch == 0) return AKV_OK;
   if (!q || !k_pool || !v_pool || !indptr || !indices || !out || !ws)
     return fail(AKV_EINVAL, "NULL pointer argument");
-  int32_t splits = 0, chunk = 0;
-  if (akv::decode_split_plan(batch, max_n, &splits, &chunk)) return fail(AKV_EINVAL, "max_n must be in [1, 2^21]");
-  if (ws_bytes < 4 * akv::decode_ws_floats(batch, hq, d, splits))
-    return fail(AKV_EINVAL, "decode workspace too small");
+  if (max_n < 1 || max_n > INT32_MAX) return fail(AKV_EINVAL, "max_n must be in [1, 2^31)");
+  if (ws_bytes < 4 * akv::decode_ws_floats(batch, hq, d)) return fail(AKV_EINVAL, "decode workspace too small");
   if (!(scale > 0.0f)) scale = 1.0f / std::sqrt((float)d);
-  akv::DecodeArgs a{q, k_pool, v_pool, indptr, indices, batch, hq, hkv, d, splits, chunk, scale,
-                    out, lse, (float*)ws};
+  akv::DecodeArgs a{q, k_pool, v_pool, indptr, indices, batch, hq, hkv, d, scale, out, lse, (float*)ws};
   return akv::launch_decode(a, stream);
 }
 

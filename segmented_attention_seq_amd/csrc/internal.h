@@ -69,18 +69,22 @@ struct AttnArgs {
 };
 int launch_segment_attention(const AttnArgs& a, void* stream);
 
+// Decode split workgroups: one per CU of the MI355X; the batch's gathered keys are
+// cut into this many equal ranges.
+constexpr int kDecodeWGs = 256;
+
 struct DecodeArgs {
   const void *q, *k, *v;
   const int32_t *indptr, *indices;
   int32_t batch, hq, hkv, d;
-  int32_t splits, chunk;
   float scale;
   void* out;
   float* lse;
   float* ws;
 };
-int decode_split_plan(int32_t batch, int64_t max_n, int32_t* splits, int32_t* chunk);
-uint64_t decode_ws_floats(int32_t batch, int32_t hq, int32_t d, int32_t splits);
+// Workspace floats: one partial (d outputs, max, sum) per query head for each of
+// the at most kDecodeWGs + batch - 1 (workgroup, request) overlaps.
+uint64_t decode_ws_floats(int32_t batch, int32_t hq, int32_t d);
 int launch_decode(const DecodeArgs& a, void* stream);
 
 }  // namespace akv

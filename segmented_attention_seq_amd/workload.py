@@ -253,8 +253,8 @@ def survivor_trajectory(n_active: int, seed: int, keep: int = KEEP_TOOLS):
             alive[2 + 2 * (r - keep)] = False
         r += 1
     starts = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64)
-    surv = np.concatenate([np.arange(s, s + n, dtype=np.int64)
-                           for s, n, a in zip(starts, lens, alive) if a and n > 0])
+    surv = np.concatenate([np.zeros(0, np.int64)] + [np.arange(s, s + n, dtype=np.int64)
+                                                     for s, n, a in zip(starts, lens, alive) if a and n > 0])
     assert surv.size == n_active
     return lens, surv
 

@@ -311,6 +311,17 @@ def test_decode_small(args):
     _decode_case(b, lo, hi, seed, hq, hkv)
 
 
+# The split kernel cuts all gathered keys of the batch into 256 equal ranges: more
+# requests than ranges (several requests per range), fewer keys than ranges (most
+# ranges empty), one request spread over every range (256 partials to merge), and
+# more than 8 kv heads (two head groups per range).
+@pytest.mark.parametrize("args", [(300, 1, 40, 95, 64, 8), (2, 1, 4, 96, 8, 8), (1, 9000, 9001, 97, 64, 8),
+                                  (3, 100, 2000, 98, 32, 16)])
+def test_decode_balanced_split_edges(args):
+    batch, lo, hi, seed, hq, hkv = args
+    _decode_case(batch, lo, hi, seed, hq=hq, hkv=hkv)
+
+
 def test_decode_workload_batch14():
     _decode_case(14, 32_000, 96_001, 1005)
 
