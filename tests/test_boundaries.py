@@ -1,0 +1,66 @@
+"""Structural checks of the product/oracle boundary (CPU only).
+
+The oracle is test infrastructure: the product package and its native sources
+never import or include it, the workload generator holds no attention arithmetic,
+and bench.py touches the oracle only inside its CPU-baseline leg.  The binding
+fails loudly when the native library is missing instead of falling back.
+"""
+import ast
+import pathlib
+import subprocess
+import sys
+
+ROOT = pathlib.Path(__file__).resolve().parents[1]
+PKG = ROOT / "segmented_attention_seq_amd"
+
+
+def _imports(tree):
+    for node in ast.walk(tree):
+        if isinstance(node, ast.Import):
+            for a in node.names:
+                yield node, a.name
+        elif isinstance(node, ast.ImportFrom):
+            yield node, node.module or ""
+
+
+def test_package_never_imports_oracle():
+    for path in PKG.rglob("*.py"):
+        tree = ast.parse(path.read_text())
+        for _, name in _imports(tree):
+            assert not name.split(".")[0] == "oracle", f"{path} imports {name}"
+
+
+def test_native_sources_never_reference_oracle():
+    for path in list(PKG.rglob("*.hip")) + list(PKG.rglob("*.cpp")) + list(PKG.rglob("*.h")) + \
+            list((ROOT / "include").rglob("*.h")):
+        text = path.read_text()
+        assert "oracle" not in text.lower(), f"{path} mentions the oracle"
+
+
+def test_bench_uses_oracle_only_in_cpu_baseline():
+    tree = ast.parse((ROOT / "bench.py").read_text())
+    funcs = {n.name: n for n in ast.walk(tree) if isinstance(n, ast.FunctionDef)}
+    for node, name in _imports(tree):
+        if name.split(".")[0] != "oracle":
+            continue
+        owner = [f for f, fn in funcs.items() if fn.lineno <= node.lineno <= fn.end_lineno]
+        assert owner == ["cpu_baseline"], f"oracle imported at bench.py line {node.lineno} in {owner}"
+
+
+def test_oracle_never_imports_the_product():
+    for path in (ROOT / "oracle").rglob("*.py"):
+        tree = ast.parse(path.read_text())
+        for _, name in _imports(tree):
+            assert name.split(".")[0] not in ("segmented_attention_seq_amd", "torch"), f"{path} imports {name}"
+
+
+def test_binding_fails_loudly_without_the_library(tmp_path):
+    # a copy of the package without libakv.so must raise on import, not fall back
+    dst = tmp_path / "segmented_attention_seq_amd"
+    dst.mkdir()
+    for f in ("__init__.py", "akv.py", "workload.py"):
+        (dst / f).write_text((PKG / f).read_text())
+    code = "import segmented_attention_seq_amd.akv"
+    r = subprocess.run([sys.executable, "-c", code], cwd=tmp_path, capture_output=True, text=True, timeout=120)
+    assert r.returncode != 0
+    assert "libakv" in (r.stderr + r.stdout)
