@@ -1,0 +1,98 @@
+"""Multi-layer restore on the GPU (GPU form of the history-dependence example).
+
+"Cache Engineering for Agents" review, history dependence (§3.4, Fig. 5) and
+single-prefill restore (§4.2, App. A.1.1): a restore runs segment-batch attention
+in every layer of one prefill, so layer l+1's K/V of every token (dropped ones
+included) come from layer l's outputs under the same visibility.  A two-layer
+attention-only residual toy with seeded weights runs each layer through the
+library's restore path (RoPE-apply, KV versions, segment attention); the
+projections are plain torch matmuls in this test.  Each layer's attention output
+is compared with the oracle fed the same inputs, and the three op orders of the
+example (read A,B / compute C / drop A; read A,B / drop A / compute C; start at B,
+append C) must leave B and C in the states the example describes.
+
+Tolerance: the residual stream is not normalised, so later layers see larger
+activations (outputs up to ~4.6 here, against ~3 for the unit-variance restore
+workloads).  The bf16 error terms (rotated Q/K stored in bf16, P and the output
+rounded to bf16) are relative, so the bf16 bound is the workloads' 2e-2 scaled by
+max(1, max|o| / 3).  A CPU emulation of those roundings on this toy's second layer
+gives 0.019 at max|o| = 4.56; the fp32 bound stays 1e-5.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import bf16 as obf
+from segmented_attention_seq_amd import akv, workload
+from tests.gpu_helpers import host_f64
+
+pytestmark = pytest.mark.gpu
+
+BASE = workload.ROPE_BASE
+
+
+def _paths(a, b, c):
+    return {
+        1: ([a, b, c], {2: [0]}, []),   # read A,B; compute C; drop A
+        2: ([a, b, c], {1: [0]}, []),   # read A,B; drop A; compute C
+        3: ([b, c], {}, []),            # start at B; append C
+    }
+
+
+def _weights(seed, dm, hq, hkv, d, layers=2):
+    rng = np.random.default_rng(seed)
+    return [[rng.standard_normal((dm, h * d)) / np.sqrt(dm) for h in (hq, hkv, hkv)] +
+            [rng.standard_normal((hq * d, dm)) / np.sqrt(hq * d)] for _ in range(layers)]
+
+
+def _run(lens, drop, repos, x, W, hq, hkv, d, bf16, tol):
+    """Layer loop on the GPU; each layer's attention output is checked against the
+    oracle on the same (host copies of the) layer inputs.  Returns the final
+    residual stream (float64, host)."""
+    ops = akv.ops_from_messages(lens, drop, repos)
+    plan = akv.build_visibility(ops)
+    ref_ops = oracle.canonical_ops(lens, drop, repos)
+    n = x.shape[0]
+    h = torch.from_numpy(x).float().cuda()
+    dt = torch.bfloat16 if bf16 else torch.float32
+    for wq, wk, wv, wo in W:
+        proj = [(h @ torch.from_numpy(w).float().cuda()).to(dt).contiguous() for w in (wq, wk, wv)]
+        q, k, v = proj[0].view(n, hq, d), proj[1].view(n, hkv, d), proj[2].view(n, hkv, d)
+        out, _ = akv.restore(plan, q, k, v, BASE)
+        torch.cuda.synchronize()
+        host = [t.float().cpu().numpy().astype(np.float64) for t in (q, k, v)]
+        o_ref, _ = oracle.segment_attention(*host, ref_ops, base=BASE)
+        err = np.abs(host_f64(out) - o_ref).max()
+        bound = tol * max(1.0, np.abs(o_ref).max() / 3.0) if bf16 else tol
+        print(f"[multilayer lens={lens} drop={drop} bf16={bf16}] layer max-abs {err:.3e} (bound {bound:.3e})")
+        assert err <= bound
+        h = h + out.float().reshape(n, hq * d) @ torch.from_numpy(wo).float().cuda()
+    return h.double().cpu().numpy()
+
+
+@pytest.mark.parametrize("bf16,hq,hkv,scale", [(False, 4, 2, 1), (True, 16, 2, 8)])
+def test_history_dependence_two_layers(bf16, hq, hkv, scale):
+    a, b, c = 16 * scale, 24 * scale, 40 * scale
+    d, dm = 64, 128
+    W = _weights(11, dm, hq, hkv, d)
+    x = np.random.default_rng(12).standard_normal((a + b + c, dm))
+    tol = 2e-2 if bf16 else 1e-5
+    h = {p: _run(l, dr, rp, x if p < 3 else x[a:], W, hq, hkv, d, bf16, tol)
+         for p, (l, dr, rp) in _paths(a, b, c).items()}
+    Cs = {1: h[1][a + b:], 2: h[2][a + b:], 3: h[3][b:]}
+    Bs = {1: h[1][a:a + b], 2: h[2][a:a + b], 3: h[3][:b]}
+    for p1, p2 in [(1, 2), (1, 3), (2, 3)]:
+        assert np.abs(Cs[p1] - Cs[p2]).max() > 1e-1, (p1, p2)   # C differs under every pair of orders
+    assert np.abs(Bs[1] - Bs[2]).max() <= (1e-5 if not bf16 else 5e-2)  # B saw A in both
+    assert np.abs(Bs[1] - Bs[3]).max() > 1e-1                    # ... but not in path 3
+
+
+def test_two_layer_restore_with_repos_matches_oracle_f32():
+    """Drops and a repos over two layers: the layer-2 keys of every token come from
+    layer-1 outputs under the same segment visibility."""
+    lens, drop, repos = [40, 70, 30, 90, 50], {2: [0], 3: [1], 4: [2]}, [2, 4]
+    hq, hkv, d, dm = 8, 2, 64, 128
+    W = _weights(13, dm, hq, hkv, d)
+    x = np.random.default_rng(14).standard_normal((sum(lens), dm))
+    _run(lens, drop, repos, x, W, hq, hkv, d, False, 1e-5)
