@@ -4,23 +4,36 @@
 #include <cstdint>
 #include <memory>
 #include <string>
+#include <utility>
 #include <vector>
 
 #include "akv.h"
+
+// std::vector whose resize() leaves new elements uninitialised (the plan builder
+// writes every element, in parallel, so the first touch of a large table is spread
+// over threads instead of a serial zero fill).
+template <class T>
+struct DefaultInitAlloc : std::allocator<T> {
+  using std::allocator<T>::allocator;
+  template <class U> struct rebind { using other = DefaultInitAlloc<U>; };
+  template <class U> void construct(U* p) noexcept { ::new (static_cast<void*>(p)) U; }
+  template <class U, class... A> void construct(U* p, A&&... a) { ::new (static_cast<void*>(p)) U(std::forward<A>(a)...); }
+};
+using I32Vec = std::vector<int32_t, DefaultInitAlloc<int32_t>>;
 
 struct akv_plan {
   int32_t bq = 0, bk = 0;
   int64_t T = 0;
   // host tables (layouts documented in akv.h)
-  std::vector<int32_t> tok_pos, tok_drop;
-  std::vector<int32_t> segments;    // 3 per segment
-  std::vector<int32_t> epochs;      // 4 per stretch
-  std::vector<int32_t> versions;    // 3 per version row
-  std::vector<int32_t> items;       // 2 per item
-  std::vector<int32_t> tile_ptr;    // n_items + 1
-  std::vector<int32_t> tiles;       // k_tile * 4 + class
-  std::vector<int32_t> item_order;
-  std::vector<int32_t> final_tok, final_pos;
+  I32Vec tok_pos, tok_drop;
+  I32Vec segments;    // 3 per segment
+  I32Vec epochs;      // 4 per stretch
+  I32Vec versions;    // 3 per version row
+  I32Vec items;       // 2 per item
+  I32Vec tile_ptr;    // n_items + 1
+  I32Vec tiles;       // k_tile * 4 + class
+  I32Vec item_order;
+  I32Vec final_tok, final_pos;
   int64_t visible_pairs = 0, p_next = 0, n_full = 0, n_partial = 0;
   // device image: contiguous int32 arrays at 256-byte aligned offsets
   std::unique_ptr<uint8_t[]> image;

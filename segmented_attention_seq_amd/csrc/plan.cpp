@@ -19,6 +19,7 @@
 #include <new>
 #include <numeric>
 #include <stdexcept>
+#include <thread>
 
 #include "internal.h"
 
@@ -28,7 +29,51 @@ namespace {
 
 struct Range { int64_t a, b; };
 
-struct Stretch { int64_t tb, te; std::vector<int32_t> src; };
+// A repos stretch: its own tokens [tb, te) and the keys active after its repos,
+// kept as the live range list (ascending) with their count r; version row v is
+// the v-th token of those ranges.
+struct Stretch {
+  int64_t tb, te;
+  std::vector<Range> src;
+  int64_t r;
+};
+
+// Host threads for the plan build (the tables are filled at precomputed offsets,
+// so the result does not depend on the split).
+int plan_threads() {
+  static const int n = [] {
+    const unsigned h = std::thread::hardware_concurrency();
+    return (int)std::max(1u, std::min(16u, h));
+  }();
+  return n;
+}
+
+// f(lo, hi) over [0, n) in contiguous chunks of at least `grain`, one per thread.
+template <class F>
+void par_for(int64_t n, int64_t grain, const F& f) {
+  if (n <= 0) return;
+  const int64_t P = std::min<int64_t>(plan_threads(), (n + grain - 1) / grain);
+  if (P <= 1) { f(0, n); return; }
+  std::vector<std::thread> th;
+  th.reserve(P - 1);
+  for (int64_t k = 1; k < P; ++k) th.emplace_back([&f, n, k, P] { f(n * k / P, n * (k + 1) / P); });
+  f(0, n / P);
+  for (auto& x : th) x.join();
+}
+
+// Source tokens of version rows [v0, v1) of a stretch, in order: cb(v, token).
+template <class CB>
+void for_version_rows(const Stretch& st, const std::vector<int64_t>& pre, int64_t v0, int64_t v1, const CB& cb) {
+  // pre[i] = number of version rows before range i
+  size_t i = std::upper_bound(pre.begin(), pre.end(), v0) - pre.begin() - 1;
+  int64_t v = v0;
+  while (v < v1) {
+    const Range& rg = st.src[i];
+    const int64_t end = std::min(v1, pre[i] + (rg.b - rg.a));
+    for (int64_t j = rg.a + (v - pre[i]); v < end; ++v, ++j) cb(v, j);
+    ++i;
+  }
+}
 
 // Per key-tile summary used to classify tiles in O(1): every key j of a stretch
 // is visible exactly to the queries in [start_j, drop_j), where start_j is j for
@@ -82,15 +127,8 @@ int build_plan(const akv_op* ops, int64_t n_ops, int32_t bq, int32_t bk, akv_pla
     int64_t n_live = 0, t = 0, next_pos = 0;
     std::vector<int64_t> cuts;          // token indices of op boundaries
     std::vector<Stretch> stretches;
-    Stretch cur{0, 0, {}};
+    Stretch cur{0, 0, {}, 0};
     int64_t pairs = 0;
-
-    auto live_tokens = [&](std::vector<int32_t>& dst) {
-      dst.clear();
-      dst.reserve(n_live);
-      for (const Range& r : live)
-        for (int64_t j = r.a; j < r.b; ++j) dst.push_back((int32_t)j);
-    };
 
     for (int64_t n = 0; n < n_ops; ++n) {
       const akv_op& op = ops[n];
@@ -121,8 +159,7 @@ int build_plan(const akv_op* ops, int64_t n_ops, int32_t bq, int32_t bk, akv_pla
       } else {  // REPOS
         cuts.push_back(t);
         if (t > cur.tb) { cur.te = t; stretches.push_back(std::move(cur)); }
-        cur = Stretch{t, t, {}};
-        live_tokens(cur.src);
+        cur = Stretch{t, t, live, n_live};
         next_pos = n_live;
       }
     }
@@ -132,20 +169,27 @@ int build_plan(const akv_op* ops, int64_t n_ops, int32_t bq, int32_t bk, akv_pla
 
     // T7: final live tokens with their current positions.  Tokens appended after
     // the last repos keep their append position; older ones hold their rank in
-    // that repos' renumbering (cur.src, ascending).
-    live_tokens(p->final_tok);
-    p->final_pos.resize(p->final_tok.size());
-    for (size_t n = 0; n < p->final_tok.size(); ++n) {
-      const int32_t j = p->final_tok[n];
-      if (j >= cur.tb) {
-        p->final_pos[n] = p->tok_pos[j];
-      } else {
-        auto it = std::lower_bound(cur.src.begin(), cur.src.end(), j);
-        p->final_pos[n] = (int32_t)(it - cur.src.begin());
-      }
+    // that repos' renumbering (the ranges of cur.src, ascending).
+    {
+      p->final_tok.resize(n_live);
+      p->final_pos.resize(n_live);
+      std::vector<int64_t> pre(cur.src.size() + 1, 0);
+      for (size_t i = 0; i < cur.src.size(); ++i) pre[i + 1] = pre[i] + (cur.src[i].b - cur.src[i].a);
+      int64_t n = 0;
+      size_t i = 0;
+      for (const Range& r : live)
+        for (int64_t j = r.a; j < r.b; ++j, ++n) {
+          p->final_tok[n] = (int32_t)j;
+          if (j >= cur.tb) {
+            p->final_pos[n] = p->tok_pos[j];
+          } else {
+            while (cur.src[i].b <= j) ++i;  // live tokens are ascending, so is i
+            p->final_pos[n] = (int32_t)(pre[i] + (j - cur.src[i].a));
+          }
+        }
     }
 
-    // T3: segments between op boundaries; T4/T5: stretches and version rows.
+    // T3: segments between op boundaries.
     std::sort(cuts.begin(), cuts.end());
     cuts.erase(std::unique(cuts.begin(), cuts.end()), cuts.end());
     {
@@ -159,122 +203,183 @@ int build_plan(const akv_op* ops, int64_t n_ops, int32_t bq, int32_t bk, akv_pla
         p->segments.insert(p->segments.end(), {(int32_t)c[n], (int32_t)c[n + 1], (int32_t)s});
       }
     }
-    int64_t ver_total = 0;
-    for (const Stretch& st : stretches) ver_total += (int64_t)st.src.size();
-    if (ver_total > INT32_MAX) throw std::length_error("more than 2^31-1 version rows");
-    p->versions.resize(3 * ver_total);
-    {
-      int64_t row = 0;
-      for (const Stretch& st : stretches) {
-        p->epochs.insert(p->epochs.end(), {(int32_t)st.tb, (int32_t)st.te, (int32_t)st.src.size(),
-                                           (int32_t)row});
-        int32_t* w = p->versions.data() + 3 * row;
-        for (size_t v = 0; v < st.src.size(); ++v, w += 3) {
-          w[0] = st.src[v];
-          w[1] = p->tok_pos[st.src[v]];
-          w[2] = (int32_t)v;
-        }
-        row += (int64_t)st.src.size();
-      }
-    }
 
-    // T6: tile classes per (stretch, q-tile).
-    std::vector<int32_t> desc;  // device item descriptors
-    p->tile_ptr.push_back(0);
-    std::vector<KeyTile> kts;
-    int64_t ver_off = 0;
-    for (size_t e = 0; e < stretches.size(); ++e) {
+    // Layout of everything per stretch: version rows, key tiles, items (q-tiles).
+    const int64_t S = (int64_t)stretches.size();
+    std::vector<int64_t> vrow(S + 1, 0), ktile(S + 1, 0), item(S + 1, 0);
+    std::vector<std::vector<int64_t>> rpre(S);  // per stretch: version rows before each range
+    for (int64_t e = 0; e < S; ++e) {
       const Stretch& st = stretches[e];
-      const int64_t r = (int64_t)st.src.size();
+      rpre[e].assign(st.src.size() + 1, 0);
+      for (size_t i = 0; i < st.src.size(); ++i) rpre[e][i + 1] = rpre[e][i] + (st.src[i].b - st.src[i].a);
       const int64_t own = st.te - st.tb;
-      const int64_t nvt = (r + bk - 1) / bk, not_ = (own + bk - 1) / bk;
-      kts.assign(nvt + not_, KeyTile{});
-      for (int64_t kt = 0; kt < nvt + not_; ++kt) {
-        KeyTile& K = kts[kt];
+      vrow[e + 1] = vrow[e] + st.r;
+      ktile[e + 1] = ktile[e] + (st.r + bk - 1) / bk + (own + bk - 1) / bk;
+      item[e + 1] = item[e] + (own + bq - 1) / bq;
+    }
+    const int64_t ver_total = vrow[S], n_ktiles = ktile[S], n_items = item[S];
+    if (ver_total > INT32_MAX) throw std::length_error("more than 2^31-1 version rows");
+    for (int64_t e = 0; e < S; ++e)
+      p->epochs.insert(p->epochs.end(), {(int32_t)stretches[e].tb, (int32_t)stretches[e].te,
+                                         (int32_t)stretches[e].r, (int32_t)vrow[e]});
+    auto stretch_of = [](const std::vector<int64_t>& off, int64_t x) {
+      return (int64_t)(std::upper_bound(off.begin(), off.end(), x) - off.begin()) - 1;
+    };
+
+    // T6, pass 1: per key tile, the interval summary (KeyTile).  Every key j of a
+    // stretch is visible exactly to the queries in [start_j, drop_j).
+    std::vector<KeyTile> kts(n_ktiles);
+    par_for(n_ktiles, 256, [&](int64_t lo, int64_t hi) {
+      int64_t e = stretch_of(ktile, lo);
+      for (int64_t g = lo; g < hi; ++g) {
+        while (ktile[e + 1] <= g) ++e;
+        const Stretch& st = stretches[e];
+        const int64_t nvt = (st.r + bk - 1) / bk, kt = g - ktile[e];
+        KeyTile& K = kts[g];
         K.max_drop = INT64_MIN;
         K.min_drop = INT64_MAX;
         int64_t k0, k1;
+        auto see = [&](int64_t, int64_t j) {
+          const int64_t dd = p->tok_drop[j];
+          K.max_drop = std::max(K.max_drop, dd);
+          K.min_drop = std::min(K.min_drop, dd);
+        };
         if (kt < nvt) {
           k0 = kt * bk;
-          k1 = std::min(r, k0 + bk);
-          for (int64_t v = k0; v < k1; ++v) {
-            const int64_t dd = p->tok_drop[st.src[v]];
-            K.max_drop = std::max(K.max_drop, dd);
-            K.min_drop = std::min(K.min_drop, dd);
-          }
+          k1 = std::min(st.r, k0 + bk);
+          for_version_rows(st, rpre[e], k0, k1, see);
           K.lo = st.tb;
           K.hi_start = st.tb;
         } else {
           k0 = st.tb + (kt - nvt) * bk;
           k1 = std::min(st.te, k0 + bk);
-          for (int64_t j = k0; j < k1; ++j) {
-            const int64_t dd = p->tok_drop[j];
-            K.max_drop = std::max(K.max_drop, dd);
-            K.min_drop = std::min(K.min_drop, dd);
-          }
+          for (int64_t j = k0; j < k1; ++j) see(0, j);
           K.lo = k0;
           K.hi_start = k1 - 1;
         }
         K.complete = (k1 - k0) == bk;
       }
-      const int64_t nqt = (own + bq - 1) / bq;
-      for (int64_t qt = 0; qt < nqt; ++qt) {
-        const int64_t i0 = st.tb + qt * bq, i1 = std::min(st.te, i0 + bq) - 1;
-        const int64_t first = (int64_t)p->tiles.size();
-        for (int64_t kt = 0; kt < nvt + not_; ++kt) {
-          const KeyTile& K = kts[kt];
-          if (K.lo > i1) break;                 // own tiles only grow from here on
-          if (K.max_drop <= i0) continue;       // every key dropped before this q-tile
-          const bool full = K.complete && K.hi_start <= i0 && K.min_drop > i1;
-          p->tiles.push_back((int32_t)(kt * 4 + (full ? AKV_TILE_FULL : AKV_TILE_PARTIAL)));
-          (full ? p->n_full : p->n_partial)++;
-        }
-        if ((int64_t)p->tiles.size() > INT32_MAX) throw std::length_error("too many tiles");
-        p->items.insert(p->items.end(), {(int32_t)e, (int32_t)qt});
-        p->tile_ptr.push_back((int32_t)p->tiles.size());
-        desc.insert(desc.end(), {(int32_t)i0, (int32_t)(i1 + 1), (int32_t)st.tb, (int32_t)st.te,
-                                 (int32_t)r, (int32_t)ver_off, (int32_t)first,
-                                 (int32_t)p->tiles.size()});
-      }
-      ver_off += r;
-    }
-    const int64_t n_items = (int64_t)p->items.size() / 2;
-    p->item_order.resize(n_items);
-    std::iota(p->item_order.begin(), p->item_order.end(), 0);
-    std::stable_sort(p->item_order.begin(), p->item_order.end(), [&](int32_t a, int32_t b) {
-      return p->tile_ptr[a + 1] - p->tile_ptr[a] > p->tile_ptr[b + 1] - p->tile_ptr[b];
     });
 
-    // Device image.  Version rows carry only (src, to); kernels read the source's
-    // append position and drop boundary through tok_pos / tok_drop.
-    const int64_t nv = ver_total;
+    // T6, pass 2: visit the non-empty key tiles of each item (stretch, q-tile);
+    // emit(kt, full) is called in key-tile order.
+    auto visit_item = [&](int64_t it, int64_t& e, const auto& emit) {
+      while (item[e + 1] <= it) ++e;
+      const Stretch& st = stretches[e];
+      const int64_t nk = ktile[e + 1] - ktile[e];
+      const int64_t qt = it - item[e];
+      const int64_t i0 = st.tb + qt * bq, i1 = std::min(st.te, i0 + bq) - 1;
+      const KeyTile* kk = kts.data() + ktile[e];
+      for (int64_t kt = 0; kt < nk; ++kt) {
+        const KeyTile& K = kk[kt];
+        if (K.lo > i1) break;                 // own tiles only grow from here on
+        if (K.max_drop <= i0) continue;       // every key dropped before this q-tile
+        emit(kt, K.complete && K.hi_start <= i0 && K.min_drop > i1);
+      }
+    };
+    std::vector<int64_t> cnt(n_items + 1, 0), nfull(n_items, 0);
+    par_for(n_items, 16, [&](int64_t lo, int64_t hi) {
+      int64_t e = stretch_of(item, lo);
+      for (int64_t it = lo; it < hi; ++it) {
+        int64_t c = 0, f = 0;
+        visit_item(it, e, [&](int64_t, bool full) { ++c; f += full; });
+        cnt[it + 1] = c;
+        nfull[it] = f;
+      }
+    });
+    p->n_full = 0;
+    for (int64_t it = 0; it < n_items; ++it) {
+      cnt[it + 1] += cnt[it];
+      p->n_full += nfull[it];
+    }
+    const int64_t n_tiles = cnt[n_items];
+    if (n_tiles > INT32_MAX) throw std::length_error("too many tiles");
+    p->n_partial = n_tiles - p->n_full;
+
+    // Device image layout.  Version rows carry only (src, to); kernels read the
+    // source's append position and drop boundary through tok_pos / tok_drop.
     uint64_t off = 0;
     auto place = [&](uint64_t bytes) { uint64_t o = off; off += (bytes + 255) & ~uint64_t(255); return o; };
     p->off_tok_pos = place(4 * T);
     p->off_tok_drop = place(4 * T);
-    p->off_ver_src = place(4 * nv);
-    p->off_ver_to = place(4 * nv);
-    p->off_item_desc = place(4 * desc.size());
-    p->off_tiles = place(4 * p->tiles.size());
-    p->off_order = place(4 * n_items);
+    p->off_ver_src = place(4 * ver_total);
+    p->off_ver_to = place(4 * ver_total);
+    p->off_item_desc = place(4 * (uint64_t)n_items * ID_WORDS);
+    p->off_tiles = place(4 * (uint64_t)n_tiles);
+    p->off_order = place(4 * (uint64_t)n_items);
     p->image_bytes = std::max<uint64_t>(off, 256);
     p->image.reset(new uint8_t[p->image_bytes]);   // padding between arrays is never read
-    auto put = [&](uint64_t o, const std::vector<int32_t>& v) {
-      if (!v.empty()) std::memcpy(p->image.get() + o, v.data(), 4 * v.size());
-    };
-    put(p->off_tok_pos, p->tok_pos);
-    put(p->off_tok_drop, p->tok_drop);
-    {
-      int32_t* src = (int32_t*)(p->image.get() + p->off_ver_src);
-      int32_t* to = (int32_t*)(p->image.get() + p->off_ver_to);
-      for (int64_t v = 0; v < nv; ++v) {
-        src[v] = p->versions[3 * v];
-        to[v] = p->versions[3 * v + 2];
+    int32_t* img_src = (int32_t*)(p->image.get() + p->off_ver_src);
+    int32_t* img_to = (int32_t*)(p->image.get() + p->off_ver_to);
+    int32_t* img_desc = (int32_t*)(p->image.get() + p->off_item_desc);
+    int32_t* img_tiles = (int32_t*)(p->image.get() + p->off_tiles);
+
+    // T5 version rows (src, its append position, row index) and their image columns.
+    p->versions.resize(3 * ver_total);
+    par_for(ver_total, 4096, [&](int64_t lo, int64_t hi) {
+      int64_t e = stretch_of(vrow, lo);
+      int64_t v = lo;
+      while (v < hi) {
+        while (vrow[e + 1] <= v) ++e;
+        const int64_t b = vrow[e], end = std::min(hi, vrow[e + 1]);
+        for_version_rows(stretches[e], rpre[e], v - b, end - b, [&](int64_t vv, int64_t j) {
+          int32_t* w = p->versions.data() + 3 * (b + vv);
+          w[0] = (int32_t)j;
+          w[1] = p->tok_pos[j];
+          w[2] = (int32_t)vv;
+          img_src[b + vv] = (int32_t)j;
+          img_to[b + vv] = (int32_t)vv;
+        });
+        v = end;
       }
-    }
-    put(p->off_item_desc, desc);
-    put(p->off_tiles, p->tiles);
-    put(p->off_order, p->item_order);
+    });
+
+    // T6 tile lists, items and item descriptors.
+    p->tiles.resize(n_tiles);
+    p->items.resize(2 * n_items);
+    p->tile_ptr.resize(n_items + 1);
+    par_for(n_items, 16, [&](int64_t lo, int64_t hi) {
+      int64_t e = stretch_of(item, lo);
+      for (int64_t it = lo; it < hi; ++it) {
+        int64_t w = cnt[it];
+        visit_item(it, e, [&](int64_t kt, bool f) {
+          const int32_t x = (int32_t)(kt * 4 + (f ? AKV_TILE_FULL : AKV_TILE_PARTIAL));
+          p->tiles[w] = x;
+          img_tiles[w] = x;
+          ++w;
+        });
+        const Stretch& st = stretches[e];
+        const int64_t qt = it - item[e];
+        const int64_t i0 = st.tb + qt * bq, i1 = std::min(st.te, i0 + bq);
+        p->items[2 * it] = (int32_t)e;
+        p->items[2 * it + 1] = (int32_t)qt;
+        p->tile_ptr[it] = (int32_t)cnt[it];
+        int32_t* d = img_desc + it * ID_WORDS;
+        d[ID_QBEGIN] = (int32_t)i0;
+        d[ID_QEND] = (int32_t)i1;
+        d[ID_TB] = (int32_t)st.tb;
+        d[ID_TE] = (int32_t)st.te;
+        d[ID_R] = (int32_t)st.r;
+        d[ID_VEROFF] = (int32_t)vrow[e];
+        d[ID_TILE0] = (int32_t)cnt[it];
+        d[ID_TILE1] = (int32_t)cnt[it + 1];
+      }
+    });
+    p->tile_ptr[n_items] = (int32_t)n_tiles;
+
+    // Work order: longest items first (stable, so ties keep item order).
+    p->item_order.resize(n_items);
+    std::iota(p->item_order.begin(), p->item_order.end(), 0);
+    std::stable_sort(p->item_order.begin(), p->item_order.end(), [&](int32_t a, int32_t b) {
+      return cnt[a + 1] - cnt[a] > cnt[b + 1] - cnt[b];
+    });
+
+    // Remaining image arrays.
+    par_for(T, 1 << 16, [&](int64_t lo, int64_t hi) {
+      std::memcpy(p->image.get() + p->off_tok_pos + 4 * lo, p->tok_pos.data() + lo, 4 * (hi - lo));
+      std::memcpy(p->image.get() + p->off_tok_drop + 4 * lo, p->tok_drop.data() + lo, 4 * (hi - lo));
+    });
+    if (n_items) std::memcpy(p->image.get() + p->off_order, p->item_order.data(), 4 * n_items);
   } catch (const std::bad_alloc&) {
     delete p;
     return fail(AKV_ENOMEM, "host allocation failed while building the plan");
