@@ -164,6 +164,23 @@ int akv_rope_repos(void* out, const void* in, int dtype, int64_t n_rows, int32_t
                    const int32_t* gather, const int32_t* pos_from, const int32_t* pos_to,
                    double rope_base, int rope_layout, akv_stream_t stream);
 
+/* akv_kv_reuse: the reuse path of a cache hit ("Cache Engineering for Agents"
+ * review, serving system: the extended radix tree with drop nodes, citing §4.2,
+ * App. A.1.2, Fig. 8; and the request flow: a hit copies the matched KV instead of
+ * re-prefilling).  A matched KV entry is copied into new rows, its key converted to
+ * the position version the request needs by rotation and its value copied as is:
+ *   k_out[n] = R((pos_to[n] - pos_from[n]) theta) * k_pool[gather[n]],
+ *   v_out[n] = v_pool[gather[n]]                            (bit-exact copy)
+ * for n < n_rows; rows hold `heads` vectors of length d (as akv_rope_repos).  A row
+ * whose position is unchanged (pos_from[n] == pos_to[n]) is copied bit for bit.
+ * gather, pos_from, pos_to: device int32 [n_rows], all required; gather values
+ * index rows of k_pool / v_pool (not checked on the device).  Outputs must not
+ * overlap the pools.  Caller-owned device memory; enqueued on `stream`.
+ */
+int akv_kv_reuse(void* k_out, void* v_out, const void* k_pool, const void* v_pool, int dtype, int64_t n_rows,
+                 int32_t heads, int32_t d, const int32_t* gather, const int32_t* pos_from,
+                 const int32_t* pos_to, double rope_base, int rope_layout, akv_stream_t stream);
+
 /* akv_rope_apply: rotate raw Q or K rows [n_tokens][heads][d] to their append
  * positions (plan T1), out of place or in place.  dev_plan = the uploaded image. */
 int akv_rope_apply(const akv_plan* plan, const void* dev_plan, void* out, const void* in,

@@ -75,6 +75,7 @@ _sig("akv_plan_tables_get", C.c_int, _vp, C.POINTER(akv_plan_tables))
 _sig("akv_plan_upload", C.c_int, _vp, _vp, _u64, _vp)
 _sig("akv_plan_destroy", None, _vp)
 _sig("akv_rope_repos", C.c_int, _vp, _vp, C.c_int, _i64, _i32, _i32, _vp, _vp, _vp, _f64, C.c_int, _vp)
+_sig("akv_kv_reuse", C.c_int, _vp, _vp, _vp, _vp, C.c_int, _i64, _i32, _i32, _vp, _vp, _vp, _f64, C.c_int, _vp)
 _sig("akv_rope_apply", C.c_int, _vp, _vp, _vp, _vp, C.c_int, _i32, _i32, _f64, C.c_int, _vp)
 _sig("akv_build_kv_versions", C.c_int, _vp, _vp, _vp, _vp, _vp, _vp, C.c_int, _i32, _i32, _f64, C.c_int, _vp)
 _sig("akv_segment_attention", C.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, C.c_int, _i32, _i32,
@@ -85,7 +86,7 @@ _sig("akv_decode_attention", C.c_int, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
 
 EXPORTED = ["akv_status_string", "akv_last_error", "akv_version", "akv_ops_from_messages",
             "akv_build_visibility", "akv_plan_info_get", "akv_plan_tables_get", "akv_plan_upload",
-            "akv_plan_destroy", "akv_rope_repos", "akv_rope_apply", "akv_build_kv_versions",
+            "akv_plan_destroy", "akv_rope_repos", "akv_kv_reuse", "akv_rope_apply", "akv_build_kv_versions",
             "akv_segment_attention", "akv_decode_workspace_bytes", "akv_decode_attention"]
 
 
@@ -251,6 +252,28 @@ def rope_repos(out, inp, pos_to, pos_from=None, gather=None, base: float = 15000
     _check(_lib.akv_rope_repos(out.data_ptr(), inp.data_ptr(), _dtype_code(out), n, H, d, g, p_from,
                                p_to, base, layout, _stream(dev)), "akv_rope_repos")
     return out
+
+
+def kv_reuse(k_out, v_out, k_pool, v_pool, gather, pos_from, pos_to, base: float = 150000.0,
+             layout: int = ROPE_HALF):
+    """Reuse path: k_out[n] = R((pos_to[n] - pos_from[n]) theta) k_pool[gather[n]],
+    v_out[n] = v_pool[gather[n]].  Pools [rows, H, d]; outputs [n, H, d]."""
+    import torch
+    n, H, d = k_out.shape
+    dev = k_out.device
+    _req(k_out, "k_out", k_pool.dtype, device=dev)
+    _req(v_out, "v_out", k_pool.dtype, (n, H, d), dev)
+    _req(k_pool, "k_pool", device=dev)
+    _req(v_pool, "v_pool", k_pool.dtype, tuple(k_pool.shape), dev)
+    if k_pool.shape[1:] != k_out.shape[1:]:
+        raise ValueError("pool/output head shapes differ")
+    g = _req(gather, "gather", torch.int32, (n,), dev)
+    p_from = _req(pos_from, "pos_from", torch.int32, (n,), dev)
+    p_to = _req(pos_to, "pos_to", torch.int32, (n,), dev)
+    _check(_lib.akv_kv_reuse(k_out.data_ptr(), v_out.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+                             _dtype_code(k_out), n, H, d, g, p_from, p_to, base, layout, _stream(dev)),
+           "akv_kv_reuse")
+    return k_out, v_out
 
 
 def rope_apply(plan: Plan, out, inp, base: float = 150000.0, layout: int = ROPE_HALF):

@@ -167,6 +167,21 @@ int akv_rope_repos(void* out, const void* in, int dtype, int64_t n_rows, int32_t
   return akv::launch_rope(a, stream);
 }
 
+int akv_kv_reuse(void* k_out, void* v_out, const void* k_pool, const void* v_pool, int dtype, int64_t n_rows,
+                 int32_t heads, int32_t d, const int32_t* gather, const int32_t* pos_from,
+                 const int32_t* pos_to, double rope_base, int rope_layout, akv_stream_t stream) {
+  int st = check_rope(dtype, heads, d, rope_layout, rope_base);
+  if (st) return st;
+  if (n_rows < 0) return fail(AKV_EINVAL, "n_rows < 0");
+  if (n_rows == 0) return AKV_OK;
+  if (!k_out || !v_out || !k_pool || !v_pool || !gather || !pos_from || !pos_to)
+    return fail(AKV_EINVAL, "NULL pointer argument");
+  if (k_out == k_pool || v_out == v_pool || k_out == v_out) return fail(AKV_EINVAL, "outputs must not alias the pools");
+  akv::RopeArgs a{k_out, k_pool, v_out, v_pool, n_rows, heads, d, gather, pos_from, false, pos_to,
+                  rope_base, rope_layout, dtype};
+  return akv::launch_rope(a, stream);
+}
+
 int akv_rope_apply(const akv_plan* p, const void* dev_plan, void* out, const void* in, int dtype,
                    int32_t heads, int32_t d, double rope_base, int rope_layout, akv_stream_t stream) {
   if (!p || !dev_plan) return fail(AKV_EINVAL, "NULL plan or device plan");

@@ -89,6 +89,47 @@ def test_repos_bf16_one_ulp_and_rne():
     assert mism < 0.01
 
 
+@pytest.mark.parametrize("bf16", [False, True])
+def test_kv_reuse_copies_and_converts_positions(bf16):
+    """Reuse path of a cache hit (review, serving system, extended radix tree:
+    same position index -> reuse as is, different -> convert by key rotation):
+    gathered keys are rotated to their new positions and values copied bit for bit;
+    rows whose position is unchanged come out bit-identical."""
+    rng = np.random.default_rng(31 + bf16)
+    rows, n, H, d = 6000, 4000, 8, 64
+    k = rng.standard_normal((rows, H, d)).astype(np.float32)
+    v = rng.standard_normal((rows, H, d)).astype(np.float32)
+    if bf16:
+        k, v = workload.f32_to_bf16_bits(k), workload.f32_to_bf16_bits(v)
+    g = rng.permutation(rows)[:n].astype(np.int32)
+    pf = rng.integers(0, 150_000, n).astype(np.int32)
+    pt = rng.integers(0, 150_000, n).astype(np.int32)
+    same = rng.random(n) < 0.25
+    pt[same] = pf[same]                      # a quarter of the rows keep their position
+    dt = torch.bfloat16 if bf16 else torch.float32
+    ko, vo = nan_like((n, H, d), dt), nan_like((n, H, d), dt)
+    kp, vp = dev_tensor(k, bf16), dev_tensor(v, bf16)
+    akv.kv_reuse(ko, vo, kp, vp, dev_int(g), dev_int(pf), dev_int(pt), BASE)
+    torch.cuda.synchronize()
+    exact = oracle.repos(as_f64(k, bf16)[g], pf, pt, BASE)
+    got = host_f64(ko)
+    if bf16:
+        assert np.all(np.abs(got - exact) <= _bf16_rot_bound(exact))
+        assert np.array_equal(host_bf16_bits(vo), v[g])
+        assert np.array_equal(host_bf16_bits(ko)[same], k[g][same])
+    else:
+        assert np.abs(got - exact).max() <= 1e-5
+        assert np.array_equal(vo.cpu().numpy(), v[g])
+        assert np.array_equal(ko.cpu().numpy()[same], k[g][same])
+
+
+def test_kv_reuse_rejects_bad_arguments():
+    x = torch.zeros((4, 8, 64), dtype=torch.bfloat16, device="cuda")
+    idx = torch.zeros(4, dtype=torch.int32, device="cuda")
+    with pytest.raises(akv.AkvError):
+        akv.kv_reuse(x, x.clone(), x, x.clone(), idx, idx, idx)   # k_out aliases k_pool
+
+
 @pytest.mark.parametrize("bf16", [True, False])
 def test_rope_apply_and_versions(bf16):
     tr = workload.agent_trajectory(4, seed=21, total=900, keep=2, repos="every",
