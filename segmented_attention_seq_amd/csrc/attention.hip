@@ -9,13 +9,12 @@
 // of the query's repos stretch are all earlier tokens), with keys at the positions
 // they hold in that stretch.
 //
-// bf16 kernel (gfx950, wave64, MFMA 32x32x16 bf16):
+// bf16 kernels (gfx950, wave64, MFMA 32x32x16 bf16):
 //   * one workgroup = one work item (stretch, 64-token q-tile) x one kv head; its
 //     GROUP waves are the GROUP query heads sharing that kv head, so each K/V tile
 //     staged in LDS feeds GROUP x 64 query rows;
-//   * per key tile of 64: S^T = K Q^T (keys on MFMA rows, queries on columns), so a
-//     lane holds 32 scores of one query column and the running max / sum are
-//     per-lane values plus one cross-half exchange (v_permlane32_swap);
+//   * per key tile of 64: S^T = K Q'^T (keys on MFMA rows, queries on columns, Q'
+//     = Q scaled by scale*log2 e), so a lane holds 32 scores of one query column;
 //   * P^T stays in registers in exactly the layout the second MFMA wants as its B
 //     operand; O^T = V^T P^T takes V^T from the row-major V tile through the
 //     transposing LDS read ds_read_b64_tr_b16 (lane i of a 16-lane group gets
@@ -23,7 +22,14 @@
 //   * the plan's tile list skips EMPTY tiles, FULL tiles run unmasked, PARTIAL
 //     tiles build the mask from per-key (token, drop) pairs staged in LDS;
 //   * blockIdx -> (item, kv head) puts consecutive workgroups on different kv heads,
-//     so with 8 kv heads each XCD's L2 streams a single head's K/V.
+//     so with 8 kv heads each XCD's L2 streams a single head's K/V;
+//   * 8 query heads per kv head (seg_attn_bf16_pp): two wave groups ping-pong
+//     between softmax and MFMA phases; the fast pass keeps the exponent offset at
+//     0 and takes the column sums from the matrix cores, with one range check per
+//     work item and a redo through the rescaling softmax when it fails;
+//   * 1, 2 or 4 query heads per kv head (seg_attn_bf16<GROUP>): one wave per query
+//     head, double-buffered tiles, the rescaling softmax (lazily moved exponent
+//     offset, bf16 dot2 row sums, per-tile range check).
 #include <hip/hip_runtime.h>
 
 #include <climits>
@@ -42,7 +48,6 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
 
 constexpr int D = 64;    // head dim
-constexpr int BQ = 64;   // query tokens per work item (= 2 MFMA column blocks)
 constexpr int BK = 64;   // keys per tile (= 2 MFMA row blocks)
 constexpr int KP = 72;   // K tile row pitch (bf16): 144 B, conflict-free 16-B row reads
 constexpr int VP = 80;   // V tile row pitch (bf16): 160 B, conflict-free transposing reads
