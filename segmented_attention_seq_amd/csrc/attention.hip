@@ -450,17 +450,29 @@ __device__ __forceinline__ void store_out(const WaveState& w, uint16_t* out, flo
   }
 }
 
+// threadIdx.x rebuilt from the lane id (v_mbcnt, a volatile asm so it is redone
+// where it is used) and the wave-uniform wave index: the staging addresses derived
+// from it are then recomputed each tile in a few VALU ops instead of being kept
+// in registers, which under the loop's register pressure meant spill reloads.
+__device__ __forceinline__ int local_tid(int wave_s) {
+  int lane;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
+  return wave_s * 64 + lane;
+}
+
 // Cooperative global -> register -> LDS staging of one K/V tile and its mask metadata.
 template <int NT>
 struct TileStage {
   static constexpr int CPT = (BK * 8 + NT - 1) / NT;  // 16-byte chunks of K (and V) per thread
   uint4 kx[CPT], vx[CPT];
   int mt, md;
+  int wave_s;  // this wave's index (uniform)
   __device__ __forceinline__ void fetch(const TileSrc& ts, bool partial, int hkv, int hk, const int* tok_drop,
                                         const int* ver_src) {
+    const int tid = local_tid(wave_s);
 #pragma unroll
     for (int j = 0; j < CPT; ++j) {
-      const int c = threadIdx.x + j * NT;
+      const int c = tid + j * NT;
       const int key = c >> 3, ch = c & 7;
       kx[j] = make_uint4(0, 0, 0, 0);
       vx[j] = make_uint4(0, 0, 0, 0);
@@ -470,8 +482,8 @@ struct TileStage {
         vx[j] = *(const uint4*)(ts.v + off);
       }
     }
-    if (partial && threadIdx.x < BK) {
-      const int key = threadIdx.x;
+    if (partial && tid < BK) {
+      const int key = tid;
       mt = INT_MAX;
       md = INT_MIN;
       if (key < ts.nrows) {
@@ -481,18 +493,19 @@ struct TileStage {
     }
   }
   __device__ __forceinline__ void stash(uint16_t* lkb, uint16_t* lvb, int* mtok, int* mdrop, bool partial) {
+    const int tid = local_tid(wave_s);
 #pragma unroll
     for (int j = 0; j < CPT; ++j) {
-      const int c = threadIdx.x + j * NT;
+      const int c = tid + j * NT;
       if (c < BK * 8) {
         const int key = c >> 3, ch = c & 7;
         *(uint4*)(lkb + key * KP + ch * 8) = kx[j];
         *(uint4*)(lvb + key * VP + ch * 8) = vx[j];
       }
     }
-    if (partial && threadIdx.x < BK) {
-      mtok[threadIdx.x] = mt;
-      mdrop[threadIdx.x] = md;
+    if (partial && tid < BK) {
+      mtok[tid] = mt;
+      mdrop[tid] = md;
     }
   }
 };
@@ -528,6 +541,7 @@ __global__ __launch_bounds__(64 * GROUP) void seg_attn_bf16(AKV_ATTN_PARAMS) {
   WaveState w;
   load_q<false>(w, nullptr, q, q0, q1, hq, h, lq, lg, sl2);
   TileStage<NT> st;
+  st.wave_s = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (t0 < t1) {
     const int e = tiles[t0];
     st.fetch(tile_src(e, nvt, voff, r, tb, te, k, v, kver, vver), (e & 3) == AKV_TILE_PARTIAL, hkv, hk,
@@ -661,6 +675,7 @@ __global__ __launch_bounds__(kPPThreads) void seg_attn_bf16_pp(AKV_ATTN_PARAMS) 
   WaveState w;
   load_q<true>(w, lqw, q, q0, q1, hq, h, lq, lg, sl2);
   TileStage<kPPThreads> st;
+  st.wave_s = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const bf16x8 sel = colsum_selector(lane);
   f32x4 ls[2] = {};
   pp_pipeline<false>(w, ls, sel, st, lk, lv, mtok, mdrop, lqw, tiles, t0, n, nvt, voff, r, tb, te, k, v, kver, vver,
