@@ -5,8 +5,10 @@ single-prefill restore (§4.2, App. A.1.1): a restore runs segment-batch attenti
 in every layer of one prefill, so layer l+1's K/V of every token (dropped ones
 included) come from layer l's outputs under the same visibility.  A two-layer
 attention-only residual toy with seeded weights runs each layer through the
-library's restore path (RoPE-apply, KV versions, segment attention); the
-projections are plain torch matmuls in this test.  Each layer's attention output
+library's restore path (RoPE-apply, KV versions, segment attention), and each
+layer ends with one FFN over all tokens of the restore as a single batch (only the
+attention is split by segment); the projections and the FFN are plain torch
+matmuls in this test.  Each layer's attention output
 is compared with the oracle fed the same inputs, and the three op orders of the
 example (read A,B / compute C / drop A; read A,B / drop A / compute C; start at B,
 append C) must leave B and C in the states the example describes.
@@ -41,9 +43,12 @@ def _paths(a, b, c):
 
 
 def _weights(seed, dm, hq, hkv, d, layers=2):
+    """Per layer: W_q, W_k, W_v, W_o, then the FFN's W_1 (dm x 2dm) and W_2."""
     rng = np.random.default_rng(seed)
     return [[rng.standard_normal((dm, h * d)) / np.sqrt(dm) for h in (hq, hkv, hkv)] +
-            [rng.standard_normal((hq * d, dm)) / np.sqrt(hq * d)] for _ in range(layers)]
+            [rng.standard_normal((hq * d, dm)) / np.sqrt(hq * d),
+             rng.standard_normal((dm, 2 * dm)) / np.sqrt(dm),
+             rng.standard_normal((2 * dm, dm)) / np.sqrt(4 * dm)] for _ in range(layers)]
 
 
 def _run(lens, drop, repos, x, W, hq, hkv, d, bf16, tol):
@@ -56,7 +61,8 @@ def _run(lens, drop, repos, x, W, hq, hkv, d, bf16, tol):
     n = x.shape[0]
     h = torch.from_numpy(x).float().cuda()
     dt = torch.bfloat16 if bf16 else torch.float32
-    for wq, wk, wv, wo in W:
+    gpu = lambda w: torch.from_numpy(w).float().cuda()
+    for wq, wk, wv, wo, w1, w2 in W:
         proj = [(h @ torch.from_numpy(w).float().cuda()).to(dt).contiguous() for w in (wq, wk, wv)]
         q, k, v = proj[0].view(n, hq, d), proj[1].view(n, hkv, d), proj[2].view(n, hkv, d)
         out, _ = akv.restore(plan, q, k, v, BASE)
@@ -67,7 +73,8 @@ def _run(lens, drop, repos, x, W, hq, hkv, d, bf16, tol):
         bound = tol * max(1.0, np.abs(o_ref).max() / 3.0) if bf16 else tol
         print(f"[multilayer lens={lens} drop={drop} bf16={bf16}] layer max-abs {err:.3e} (bound {bound:.3e})")
         assert err <= bound
-        h = h + out.float().reshape(n, hq * d) @ torch.from_numpy(wo).float().cuda()
+        h = h + out.float().reshape(n, hq * d) @ gpu(wo)
+        h = h + torch.relu(h @ gpu(w1)) @ gpu(w2)      # one FFN batch over every token
     return h.double().cpu().numpy()
 
 
