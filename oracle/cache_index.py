@@ -84,7 +84,8 @@ def history(tok, ops):
         if kind == APPEND:
             if op[1] < 0:
                 raise CacheError("negative append")
-            flush()
+            if op[1] > 0:               # an empty append is not a boundary
+                flush()
             for _ in range(op[1]):
                 if t >= T:
                     raise CacheError("ops append more tokens than given")

@@ -122,9 +122,10 @@ def test_canonical_form_drops_no_op_events():
     for ops in same:
         assert token_keys(history(tok, ops)) == kb
         assert _ident(tok, ops) == ib
-    split = [(APPEND, 3), (DROP, 0, 1), (DROP, 1, 2), (APPEND, 1)]
+    split = [(APPEND, 3), (DROP, 0, 1), (APPEND, 0), (DROP, 1, 2), (APPEND, 1)]
     merged = [(APPEND, 3), (DROP, 0, 2), (APPEND, 1)]
     assert token_keys(history(tok, split)) == token_keys(history(tok, merged))
+    assert _ident(tok, split) == _ident(tok, merged)
     # a repos after a drop moves positions: a real event
     moved = [(APPEND, 2), (DROP, 0, 1), (REPOS,), (APPEND, 2)]
     assert token_keys(history(tok, moved))[2] != kb[2]
