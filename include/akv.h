@@ -50,6 +50,7 @@ extern "C" {
 #define AKV_EUNSUPPORTED -3   /* valid but not implemented (e.g. head dim != 64) */
 #define AKV_EHIP         -4   /* HIP runtime / launch error */
 #define AKV_ENOMEM       -5   /* host allocation failed */
+#define AKV_ENOSPACE     -6   /* cache index: every slot asked for is locked */
 
 /* Element types. */
 #define AKV_F32  0
@@ -235,6 +236,97 @@ int akv_decode_attention(const void* q, const void* k_pool, const void* v_pool,
                          int32_t hq, int32_t hkv, int32_t d, int64_t max_n, float scale,
                          int dtype, void* out, float* lse, void* ws, uint64_t ws_bytes,
                          akv_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * KV cache index: which rows of a request are already held, where, and at which
+ * position; what has to be recomputed; which rows to give up under pressure.
+ * "Cache Engineering for Agents" review, AKV serving system (§4.2, App. A.1.2,
+ * Fig. 8) and the request flow (match in the extended radix tree, copy on a hit,
+ * one segment-batch prefill when the state was evicted); explainer §3.4 / Fig. 5
+ * (the same survivors reached by different op orders hold different KV).
+ *
+ * The index is host-only bookkeeping over the slots 0..n_slots-1 of a KV pool the
+ * caller owns (one slot = one token's K and V rows at one position, for however
+ * many layers and heads the caller stores there).  It never touches device memory.
+ *
+ * Sharing rule: a token's rows are identified by the canonical history up to and
+ * including its append: the token ids, one drop node per op boundary holding the
+ * logical ranges that boundary actually removed (drops of inactive tokens and empty
+ * appends change nothing), and a repos node for every repos that moves a position
+ * or the next position.  Requests share rows exactly where these histories agree.
+ * A token may hold several position versions; each sits in its own slot and is
+ * evicted on its own.  An evicted row leaves its tree node in place.
+ *
+ * Locks: every slot handed out (akv_cache_alloc, akv_cache_match with lock != 0)
+ * carries one lock per hand-out; akv_cache_unlock drops them.  Locked slots are
+ * never evicted; an allocated slot that never received a version goes back to the
+ * free list when its last lock is dropped.
+ *
+ * Eviction order among unlocked rows: first those no finished request holds
+ * ("dropped": not in the final state, at that position, of any completed request
+ * whose history no later completed request extends), then the rest; least recently
+ * used first within each class (one tick per call), then the lower slot.
+ *
+ * Not thread-safe: callers serialise calls on one index.  All arrays are host
+ * memory owned by the caller.  Tokens: tok[0..n_tok) must be exactly the tokens
+ * the op list appends (AKV_EINVAL otherwise); op errors as akv_build_visibility.
+ * ------------------------------------------------------------------------- */
+typedef struct akv_cache akv_cache;
+
+typedef struct {
+  int64_t n_tokens;      /* T */
+  int64_t n_matched;     /* leading tokens whose history is in the tree */
+  int64_t n_resident;    /* tokens with a resident version (slot_out >= 0) */
+  int64_t restore_from;  /* s: recompute tokens [s, T); T means reuse only */
+  int64_t n_final;       /* active tokens after the last op */
+  int64_t p_next;        /* position of the next appended token */
+} akv_cache_match_info;
+
+typedef struct {
+  int64_t n_slots, n_free, n_resident, n_locked;
+  int64_t n_nodes;        /* tree nodes, root included */
+  int64_t n_tree_tokens;  /* distinct token histories ever inserted */
+  int64_t n_marks;        /* distinct completed histories */
+  int64_t n_frontier;     /* of those, not extended by another */
+} akv_cache_stats;
+
+/* n_slots >= 1.  *out owned by the caller; free with akv_cache_destroy. */
+int  akv_cache_create(int32_t n_slots, akv_cache** out);
+void akv_cache_destroy(akv_cache* cache);
+
+/* For every token i of the request: slot_out[i] = slot of its preferred resident
+ * version (-1 if none) and pos_out[i] = that version's position.  Preferred: the
+ * version at the position the request needs (final position for tokens of the
+ * final state, else the append position), else the most recently used, then the
+ * lowest position.  A version at another position is usable after rotating its key
+ * by (needed - pos_out[i]) (akv_kv_reuse does the copy and the rotation).
+ * restore_from is the largest s in [0, T] such that every key seen by a query at or
+ * after s, and every final-state token below s, has a resident version.  Returned
+ * slots are touched (LRU) and, if lock != 0, locked once each.  info may be NULL. */
+int akv_cache_match(akv_cache* cache, const int32_t* tok, int64_t n_tok, const akv_op* ops,
+                    int64_t n_ops, int32_t lock, int32_t* slot_out, int32_t* pos_out,
+                    akv_cache_match_info* info);
+
+/* n slots, each locked once: free slots in ascending order, then evicted rows in
+ * eviction order.  AKV_ENOSPACE (nothing changes) if fewer than n are free or
+ * evictable. */
+int akv_cache_alloc(akv_cache* cache, int32_t n, int32_t* slots_out);
+
+/* Record the request's history (creating tree nodes) and the versions it computed:
+ * token ver_token[v] at position ver_pos[v] now sits in ver_slot[v], a slot from
+ * akv_cache_alloc that holds no version yet; its lock is kept.  Also records the
+ * request's final state as a completed request.  AKV_EINVAL (nothing changes) for an
+ * index out of range, a slot that is not allocated and empty, a version given twice
+ * or already resident. */
+int akv_cache_insert(akv_cache* cache, const int32_t* tok, int64_t n_tok, const akv_op* ops,
+                     int64_t n_ops, const int32_t* ver_token, const int32_t* ver_pos,
+                     const int32_t* ver_slot, int64_t n_ver);
+
+/* Drop one lock per listed slot (a slot may be listed as often as it is locked).
+ * AKV_EINVAL (nothing changes) if a slot holds fewer locks than listed. */
+int akv_cache_unlock(akv_cache* cache, const int32_t* slots, int64_t n);
+
+int akv_cache_stats_get(const akv_cache* cache, akv_cache_stats* out);
 
 #ifdef __cplusplus
 }

@@ -22,7 +22,7 @@ if not os.path.exists(LIB_PATH):
                       "`python -m segmented_attention_seq_amd.build` (no CPU fallback exists)")
 _lib = C.CDLL(LIB_PATH)
 
-OK, EINVAL, EOPSEQ, EUNSUPPORTED, EHIP, ENOMEM = 0, -1, -2, -3, -4, -5
+OK, EINVAL, EOPSEQ, EUNSUPPORTED, EHIP, ENOMEM, ENOSPACE = 0, -1, -2, -3, -4, -5, -6
 F32, BF16 = 0, 1
 ROPE_HALF, ROPE_INTERLEAVED = 0, 1
 OP_APPEND, OP_DROP, OP_REPOS = 0, 1, 2
@@ -48,6 +48,16 @@ class akv_plan_info(C.Structure):
 
 
 _P32 = C.POINTER(C.c_int32)
+
+
+class akv_cache_match_info(C.Structure):
+    _fields_ = [(n, C.c_int64) for n in ("n_tokens", "n_matched", "n_resident", "restore_from",
+                                         "n_final", "p_next")]
+
+
+class akv_cache_stats(C.Structure):
+    _fields_ = [(n, C.c_int64) for n in ("n_slots", "n_free", "n_resident", "n_locked", "n_nodes",
+                                         "n_tree_tokens", "n_marks", "n_frontier")]
 
 
 class akv_plan_tables(C.Structure):
@@ -83,11 +93,20 @@ _sig("akv_segment_attention", C.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _
 _sig("akv_decode_workspace_bytes", _u64, _i32, _i32, _i32, _i32, _i64)
 _sig("akv_decode_attention", C.c_int, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i64, _f32, C.c_int,
      _vp, _vp, _vp, _u64, _vp)
+_sig("akv_cache_create", C.c_int, _i32, C.POINTER(_vp))
+_sig("akv_cache_destroy", None, _vp)
+_sig("akv_cache_match", C.c_int, _vp, _vp, _i64, _vp, _i64, _i32, _vp, _vp, C.POINTER(akv_cache_match_info))
+_sig("akv_cache_alloc", C.c_int, _vp, _i32, _vp)
+_sig("akv_cache_insert", C.c_int, _vp, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _i64)
+_sig("akv_cache_unlock", C.c_int, _vp, _vp, _i64)
+_sig("akv_cache_stats_get", C.c_int, _vp, C.POINTER(akv_cache_stats))
 
 EXPORTED = ["akv_status_string", "akv_last_error", "akv_version", "akv_ops_from_messages",
             "akv_build_visibility", "akv_plan_info_get", "akv_plan_tables_get", "akv_plan_upload",
             "akv_plan_destroy", "akv_rope_repos", "akv_kv_reuse", "akv_rope_apply", "akv_build_kv_versions",
-            "akv_segment_attention", "akv_decode_workspace_bytes", "akv_decode_attention"]
+            "akv_segment_attention", "akv_decode_workspace_bytes", "akv_decode_attention",
+            "akv_cache_create", "akv_cache_destroy", "akv_cache_match", "akv_cache_alloc",
+            "akv_cache_insert", "akv_cache_unlock", "akv_cache_stats_get"]
 
 
 def _check(status: int, where: str):
@@ -129,6 +148,69 @@ def ops_array(ops) -> np.ndarray:
         out[i].a = op[1] if len(op) > 1 else 0
         out[i].b = op[2] if len(op) > 2 else 0
     return np.ctypeslib.as_array(out)[: len(ops)].copy()
+
+
+def _ops_arg(ops):
+    ops = ops if isinstance(ops, np.ndarray) else ops_array(ops)
+    ops = np.ascontiguousarray(ops)
+    return ops, (ops.ctypes.data if len(ops) else None), len(ops)
+
+
+def _i32_arg(x):
+    a = np.ascontiguousarray(x, np.int32)
+    return a, (a.ctypes.data if a.size else None), a.size
+
+
+class CacheIndex:
+    """KV cache index (akv_cache_*): extended radix tree over token + op histories,
+    position versions per token, drop-aware eviction over n_slots pool rows."""
+
+    def __init__(self, n_slots: int):
+        h = _vp()
+        _check(_lib.akv_cache_create(int(n_slots), C.byref(h)), "akv_cache_create")
+        self._h = h
+
+    def __del__(self):
+        if getattr(self, "_h", None):
+            _lib.akv_cache_destroy(self._h)
+            self._h = None
+
+    def match(self, tok, ops, lock: bool = False):
+        """-> (slot int32[T], pos int32[T], info dict)."""
+        tk, tp, n = _i32_arg(tok)
+        ops, op_p, n_ops = _ops_arg(ops)
+        slot = np.empty(n, np.int32)
+        pos = np.empty(n, np.int32)
+        info = akv_cache_match_info()
+        _check(_lib.akv_cache_match(self._h, tp, n, op_p, n_ops, int(bool(lock)),
+                                    slot.ctypes.data if n else None, pos.ctypes.data if n else None,
+                                    C.byref(info)), "akv_cache_match")
+        return slot, pos, {f: getattr(info, f) for f, _ in info._fields_}
+
+    def alloc(self, n: int) -> np.ndarray:
+        out = np.empty(max(int(n), 0), np.int32)
+        _check(_lib.akv_cache_alloc(self._h, int(n), out.ctypes.data if out.size else None),
+               "akv_cache_alloc")
+        return out
+
+    def insert(self, tok, ops, ver_token, ver_pos, ver_slot):
+        tk, tp, n = _i32_arg(tok)
+        ops, op_p, n_ops = _ops_arg(ops)
+        vt, vtp, nv = _i32_arg(ver_token)
+        vp, vpp, nv2 = _i32_arg(ver_pos)
+        vs, vsp, nv3 = _i32_arg(ver_slot)
+        if not nv == nv2 == nv3:
+            raise ValueError("version arrays differ in length")
+        _check(_lib.akv_cache_insert(self._h, tp, n, op_p, n_ops, vtp, vpp, vsp, nv), "akv_cache_insert")
+
+    def unlock(self, slots):
+        s, sp, n = _i32_arg(slots)
+        _check(_lib.akv_cache_unlock(self._h, sp, n), "akv_cache_unlock")
+
+    def stats(self) -> Dict[str, int]:
+        st = akv_cache_stats()
+        _check(_lib.akv_cache_stats_get(self._h, C.byref(st)), "akv_cache_stats_get")
+        return {f: getattr(st, f) for f, _ in st._fields_}
 
 
 class Plan:

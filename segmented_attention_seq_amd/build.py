@@ -18,7 +18,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libakv.so")
 BUILD = os.path.join(ROOT, "_build")
-SOURCES = ["plan.cpp", "api.cpp", "rope.hip", "attention.hip", "decode.hip"]
+SOURCES = ["plan.cpp", "cache_index.cpp", "api.cpp", "rope.hip", "attention.hip", "decode.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 CFLAGS = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-result",

@@ -36,6 +36,7 @@ const char* akv_status_string(int status) {
     case AKV_EUNSUPPORTED: return "unsupported configuration";
     case AKV_EHIP: return "HIP runtime error";
     case AKV_ENOMEM: return "out of host memory";
+    case AKV_ENOSPACE: return "cache index full: remaining slots are locked";
     default: return "unknown status";
   }
 }
