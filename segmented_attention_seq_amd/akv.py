@@ -14,6 +14,10 @@ import os
 from typing import Dict, Optional, Sequence
 
 import numpy as np
+# torch ships its own HIP runtime under the same soname as the system one.  Loading
+# it first makes libakv.so bind to that copy; loading libakv.so first would map a
+# second HIP runtime, whose launches then find no device for torch's allocations.
+import torch  # noqa: F401
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("AKV_LIB", os.path.join(_HERE, "libakv.so"))

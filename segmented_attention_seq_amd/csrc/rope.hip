@@ -6,11 +6,11 @@
 // matrix and leaves the value untouched; "single-prefill restore" (§4.2, App.
 // A.1.1): per-segment KV versions are made by key rotation and value copy.
 //
-// Bandwidth-bound.  One thread owns one 8-pair chunk of a row (pairs 8c..8c+7)
-// and walks every head of that row, so its 8 (cos, sin) values are computed once
-// and reused heads times.  Loads and stores are 16-byte vectors; a wave covers
-// 16 rows x 64 contiguous bytes per instruction (the partner half-chunk load
-// completes each 128-byte line).
+// Bandwidth-bound.  For head dims 16-128 one thread handles one 8-pair chunk of
+// one head of a row and the chunk's (cos, sin) values are shared across the
+// threads of 8 heads by cross-lane shuffle (rope_lane_kernel); other head dims use
+// one thread per chunk that walks every head of the row.  Loads and stores are
+// 16-byte vectors; a wave's two loads together read whole 128-byte lines.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -76,6 +76,19 @@ template <> struct Vec8<float> {
   }
 };
 
+// 8 consecutive elements moved bit for bit (value rows of versions and reuse)
+template <typename T> struct Raw8;
+template <> struct Raw8<uint16_t> {
+  uint4 u;
+  __device__ __forceinline__ void load(const uint16_t* p) { u = *(const uint4*)p; }
+  __device__ __forceinline__ void store(uint16_t* p) const { *(uint4*)p = u; }
+};
+template <> struct Raw8<float> {
+  float4 a, b;
+  __device__ __forceinline__ void load(const float* p) { a = *(const float4*)p; b = *(const float4*)(p + 4); }
+  __device__ __forceinline__ void store(float* p) const { *(float4*)p = a; *(float4*)(p + 4) = b; }
+};
+
 template <typename T, int LAYOUT>
 __global__ __launch_bounds__(256) void rope_kernel(T* __restrict__ out, const T* __restrict__ in,
                                                    T* __restrict__ vout, const T* __restrict__ vin,
@@ -132,8 +145,104 @@ __global__ __launch_bounds__(256) void rope_kernel(T* __restrict__ out, const T*
   }
 }
 
+// Lane-per-head form for d in {16, 32, 64, 128}: one thread per (row, head, chunk),
+// so every thread moves 16-32 bytes each way and the grid holds enough waves to keep
+// the memory system busy (one thread walking all heads of a row leaves a few
+// thousand waves, each waiting on one head after another).  The 8 threads that share
+// a (row, group of 8 heads, chunk) each compute one of the chunk's 8 (cos, sin) pairs
+// and fetch the other seven from their neighbours by cross-lane shuffle, so the angle
+// work stays one evaluation per thread.  Lane layout inside a wave: groups of
+// G = 8 * CPR lanes, lane = h8 * CPR + c, with G dividing 64.
+template <typename T, int LAYOUT, int CPR>
+__global__ __launch_bounds__(256) void rope_lane_kernel(T* __restrict__ out, const T* __restrict__ in,
+                                                        T* __restrict__ vout, const T* __restrict__ vin,
+                                                        long long n_rows, int heads, int n_hg,
+                                                        const int* __restrict__ gather,
+                                                        const int* __restrict__ pos_from, int from_by_src,
+                                                        const int* __restrict__ pos_to, Freqs fr) {
+  constexpr int G = 8 * CPR;
+  constexpr int D = 16 * CPR;
+  const long long tid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long long grp = tid / G;
+  const int l = (int)(tid - grp * G);
+  const long long row = grp / n_hg;
+  if (row >= n_rows) return;  // whole groups leave together: a group never spans two rows
+  const int hg = (int)(grp - row * n_hg);
+  const int h8 = l / CPR, c = l - h8 * CPR;
+  const int h = hg * 8 + h8;
+  const long long src = gather ? (long long)gather[row] : row;
+  // Position and frequency loads go first, then the row's data, so the angle work
+  // waits only for the former (loads complete in order) and overlaps the latter;
+  // lanes past the last head (heads % 8 != 0) read the last head and store nothing.
+  const long long delta =
+      (long long)pos_to[row] - (pos_from ? (long long)pos_from[from_by_src ? src : row] : 0LL);
+  const double th = fr.theta[c * 8 + h8];
+  const int hc = h < heads ? h : heads - 1;
+  const long long off_in = (src * heads + hc) * D, off_out = (row * heads + h) * D;
+  int oa, ob;
+  if (LAYOUT == AKV_ROPE_HALF) { oa = c * 8; ob = D / 2 + c * 8; }
+  else { oa = c * 16; ob = c * 16 + 8; }
+  float a[8], b[8];
+  Vec8<T>::load(in + off_in + oa, a);
+  Vec8<T>::load(in + off_in + ob, b);
+  Raw8<T> va, vb;
+  if (vout) {
+    va.load(vin + off_in + oa);
+    vb.load(vin + off_in + ob);
+  }
+  float mc, ms;
+  angle_cs(delta, th, mc, ms);
+  const int base = (int)(threadIdx.x & 63) - l;   // first lane of this group in the wave
+  float cs[8], sn[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    cs[i] = __shfl(mc, base + i * CPR + c, 64);
+    sn[i] = __shfl(ms, base + i * CPR + c, 64);
+  }
+  if (h >= heads) return;
+  float ya[8], yb[8];
+  if (LAYOUT == AKV_ROPE_HALF) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      ya[i] = a[i] * cs[i] - b[i] * sn[i];
+      yb[i] = a[i] * sn[i] + b[i] * cs[i];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ya[2 * i] = a[2 * i] * cs[i] - a[2 * i + 1] * sn[i];
+      ya[2 * i + 1] = a[2 * i] * sn[i] + a[2 * i + 1] * cs[i];
+      yb[2 * i] = b[2 * i] * cs[i + 4] - b[2 * i + 1] * sn[i + 4];
+      yb[2 * i + 1] = b[2 * i] * sn[i + 4] + b[2 * i + 1] * cs[i + 4];
+    }
+  }
+  Vec8<T>::store(out + off_out + oa, ya);
+  Vec8<T>::store(out + off_out + ob, yb);
+  if (vout) {
+    va.store(vout + off_out + oa);
+    vb.store(vout + off_out + ob);
+  }
+}
+
+template <typename T, int LAYOUT, int CPR>
+void launch_lane(const RopeArgs& a, const Freqs& fr, hipStream_t s) {
+  const int n_hg = (a.heads + 7) / 8;
+  const long long threads = a.n_rows * n_hg * (8LL * CPR);
+  const unsigned blocks = (unsigned)((threads + 255) / 256);
+  hipLaunchKernelGGL((rope_lane_kernel<T, LAYOUT, CPR>), dim3(blocks), dim3(256), 0, s, (T*)a.out,
+                     (const T*)a.in, (T*)a.v_out, (const T*)a.v_in, (long long)a.n_rows, a.heads, n_hg,
+                     a.gather, a.pos_from, a.pos_from_by_src ? 1 : 0, a.pos_to, fr);
+}
+
 template <typename T, int LAYOUT>
 void launch_t(const RopeArgs& a, const Freqs& fr, hipStream_t s) {
+  switch (a.d) {
+    case 16: return launch_lane<T, LAYOUT, 1>(a, fr, s);
+    case 32: return launch_lane<T, LAYOUT, 2>(a, fr, s);
+    case 64: return launch_lane<T, LAYOUT, 4>(a, fr, s);
+    case 128: return launch_lane<T, LAYOUT, 8>(a, fr, s);
+    default: break;
+  }
   const long long threads = a.n_rows * (a.d / 16);
   const unsigned blocks = (unsigned)((threads + 255) / 256);
   hipLaunchKernelGGL((rope_kernel<T, LAYOUT>), dim3(blocks), dim3(256), 0, s, (T*)a.out, (const T*)a.in,
@@ -147,7 +256,7 @@ int launch_rope(const RopeArgs& a, void* stream) {
   Freqs fr;
   for (int i = 0; i < a.d / 2; ++i) fr.theta[i] = std::pow(a.base, -2.0 * i / a.d);
   for (int i = a.d / 2; i < 128; ++i) fr.theta[i] = 0.0;
-  const long long threads = a.n_rows * (a.d / 16);
+  const long long threads = a.n_rows * ((a.heads + 7) / 8) * 8LL * (a.d / 16);   // the larger of the two forms
   if ((threads + 255) / 256 > 0x7fffffffLL) return fail(AKV_EINVAL, "too many rows for one launch");
   hipStream_t s = (hipStream_t)stream;
   (void)hipGetLastError();

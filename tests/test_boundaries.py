@@ -64,3 +64,18 @@ def test_binding_fails_loudly_without_the_library(tmp_path):
     r = subprocess.run([sys.executable, "-c", code], cwd=tmp_path, capture_output=True, text=True, timeout=120)
     assert r.returncode != 0
     assert "libakv" in (r.stderr + r.stdout)
+
+
+def test_binding_and_torch_share_one_hip_runtime():
+    """Importing the binding first (before torch) must still map a single HIP
+    runtime: the one torch loads, which libakv.so then binds to by soname."""
+    code = ("import os\n"
+            "from segmented_attention_seq_amd import akv\n"
+            "import torch\n"
+            "m = open(f'/proc/{os.getpid()}/maps').read()\n"
+            "libs = {l.split()[-1] for l in m.splitlines() if 'libamdhip64' in l}\n"
+            "print(len(libs), sorted(libs))\n")
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.split()[0] == "1", r.stdout
+

@@ -72,6 +72,27 @@ def test_repos_fp32_large_shifts(layout):
     assert err <= 1e-5
 
 
+# Head dims 16-128 run one thread per (row, head, 8-pair chunk) with the angles
+# shared by cross-lane shuffle among groups of 8 heads; other dims (48 here) walk all
+# heads per thread.  Head counts that are not multiples of 8 leave idle lanes in the
+# last head group.
+@pytest.mark.parametrize("d,H", [(16, 3), (32, 8), (48, 5), (64, 1), (64, 12), (128, 9)])
+@pytest.mark.parametrize("layout", [akv.ROPE_HALF, akv.ROPE_INTERLEAVED])
+def test_repos_fp32_head_dims_and_counts(d, H, layout):
+    rng = np.random.default_rng(1000 + d + H)
+    rows, n = 700, 513
+    k = rng.standard_normal((rows, H, d)).astype(np.float32)
+    g = rng.integers(0, rows, n).astype(np.int32)
+    pf = rng.integers(0, 1 << 20, n).astype(np.int32)
+    pt = rng.integers(0, 1 << 20, n).astype(np.int32)
+    out = nan_like((n, H, d), torch.float32)
+    akv.rope_repos(out, dev_tensor(k, False), dev_int(pt), dev_int(pf), dev_int(g), BASE, layout)
+    ref = oracle.repos(k[g], pf, pt, BASE, layout)
+    err = np.abs(host_f64(out) - ref).max()
+    print(f"[repos fp32 d={d} H={H} layout={layout}] max-abs {err:.2e}")
+    assert err <= 1e-5
+
+
 def test_repos_bf16_one_ulp_and_rne():
     rng = np.random.default_rng(12)
     n, H, d = 4000, 8, 64
