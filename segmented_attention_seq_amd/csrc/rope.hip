@@ -20,22 +20,19 @@
 namespace akv {
 namespace {
 
-// 2*pi split in two doubles for Cody & Waite's reduction (Cody, W. and Waite, W.,
-// "Software Manual for the Elementary Functions", 1980): x - k*2pi is evaluated as
-// (x - k*C1) - k*C2 with fma, so the reduced angle keeps ~1e-15 absolute accuracy
-// for |x| up to ~1e9.
-constexpr double kTwoPiHi = 6.283185307179586232;     // double nearest 2*pi
-constexpr double kTwoPiLo = 2.4492935982947064e-16;   // 2*pi - kTwoPiHi
-constexpr double kInvTwoPi = 0.15915494309189533577;
+// Frequencies are stored in revolutions per position, theta_i / (2 pi), in fp64.
+// The angle of a shift delta is reduced to its fractional revolution in fp64:
+// |delta| < 2^31 and theta_i / (2 pi) < 0.16 keep the product below 2^29, where the
+// fp64 spacing is 2^-23 revolutions or less (2^-35 for shifts up to 2^20), and the
+// fraction is rounded once to fp32.  The hardware sine and cosine take their
+// argument in revolutions; on [-0.5, 0.5] they are within 1.3e-7 of the exact value.
+struct Freqs { double rev[128]; };
 
-struct Freqs { double theta[128]; };
-
-__device__ __forceinline__ void angle_cs(long long delta, double th, float& c, float& s) {
-  const double x = (double)delta * th;
-  const double k = rint(x * kInvTwoPi);
-  double r = fma(-k, kTwoPiHi, x);
-  r = fma(-k, kTwoPiLo, r);
-  sincosf((float)r, &s, &c);
+__device__ __forceinline__ void angle_cs(long long delta, double rev, float& c, float& s) {
+  const double x = (double)delta * rev;
+  const float r = (float)(x - rint(x));
+  s = __builtin_amdgcn_sinf(r);
+  c = __builtin_amdgcn_cosf(r);
 }
 
 __device__ __forceinline__ float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
@@ -106,7 +103,7 @@ __global__ __launch_bounds__(256) void rope_kernel(T* __restrict__ out, const T*
       (long long)pos_to[row] - (pos_from ? (long long)pos_from[from_by_src ? src : row] : 0LL);
   float cs[8], sn[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) angle_cs(delta, fr.theta[c * 8 + i], cs[i], sn[i]);
+  for (int i = 0; i < 8; ++i) angle_cs(delta, fr.rev[c * 8 + i], cs[i], sn[i]);
 
   const long long stride = (long long)heads * d;
   const T* x = in + src * stride;
@@ -153,7 +150,13 @@ __global__ __launch_bounds__(256) void rope_kernel(T* __restrict__ out, const T*
 // and fetch the other seven from their neighbours by cross-lane shuffle, so the angle
 // work stays one evaluation per thread.  Lane layout inside a wave: groups of
 // G = 8 * CPR lanes, lane = h8 * CPR + c, with G dividing 64.
-template <typename T, int LAYOUT, int CPR>
+// Index forms of the lane kernel, fixed at compile time so that independent index
+// loads issue together: apply (no gather, rotation from position 0), repos and
+// reuse (gather, pos_from by output row), versions (gather, pos_from by source
+// row); anything else reads the pointers at run time.
+enum { IX_APPLY = 0, IX_GATHER_ROW = 1, IX_GATHER_SRC = 2, IX_ANY = 3 };
+
+template <typename T, int LAYOUT, int CPR, int IX>
 __global__ __launch_bounds__(256) void rope_lane_kernel(T* __restrict__ out, const T* __restrict__ in,
                                                         T* __restrict__ vout, const T* __restrict__ vin,
                                                         long long n_rows, int heads, int n_hg,
@@ -170,13 +173,26 @@ __global__ __launch_bounds__(256) void rope_lane_kernel(T* __restrict__ out, con
   const int hg = (int)(grp - row * n_hg);
   const int h8 = l / CPR, c = l - h8 * CPR;
   const int h = hg * 8 + h8;
-  const long long src = gather ? (long long)gather[row] : row;
   // Position and frequency loads go first, then the row's data, so the angle work
   // waits only for the former (loads complete in order) and overlaps the latter;
   // lanes past the last head (heads % 8 != 0) read the last head and store nothing.
-  const long long delta =
-      (long long)pos_to[row] - (pos_from ? (long long)pos_from[from_by_src ? src : row] : 0LL);
-  const double th = fr.theta[c * 8 + h8];
+  long long src, delta;
+  if constexpr (IX == IX_APPLY) {
+    src = row;
+    delta = pos_to[row];
+  } else if constexpr (IX == IX_GATHER_ROW) {
+    const int g = gather[row], pt = pos_to[row], pf = pos_from[row];
+    src = g;
+    delta = (long long)pt - pf;
+  } else if constexpr (IX == IX_GATHER_SRC) {
+    const int g = gather[row], pt = pos_to[row];
+    src = g;
+    delta = (long long)pt - pos_from[g];
+  } else {
+    src = gather ? (long long)gather[row] : row;
+    delta = (long long)pos_to[row] - (pos_from ? (long long)pos_from[from_by_src ? src : row] : 0LL);
+  }
+  const double th = fr.rev[c * 8 + h8];
   const int hc = h < heads ? h : heads - 1;
   const long long off_in = (src * heads + hc) * D, off_out = (row * heads + h) * D;
   int oa, ob;
@@ -224,14 +240,22 @@ __global__ __launch_bounds__(256) void rope_lane_kernel(T* __restrict__ out, con
   }
 }
 
-template <typename T, int LAYOUT, int CPR>
-void launch_lane(const RopeArgs& a, const Freqs& fr, hipStream_t s) {
+template <typename T, int LAYOUT, int CPR, int IX>
+void launch_lane_ix(const RopeArgs& a, const Freqs& fr, hipStream_t s) {
   const int n_hg = (a.heads + 7) / 8;
   const long long threads = a.n_rows * n_hg * (8LL * CPR);
   const unsigned blocks = (unsigned)((threads + 255) / 256);
-  hipLaunchKernelGGL((rope_lane_kernel<T, LAYOUT, CPR>), dim3(blocks), dim3(256), 0, s, (T*)a.out,
+  hipLaunchKernelGGL((rope_lane_kernel<T, LAYOUT, CPR, IX>), dim3(blocks), dim3(256), 0, s, (T*)a.out,
                      (const T*)a.in, (T*)a.v_out, (const T*)a.v_in, (long long)a.n_rows, a.heads, n_hg,
                      a.gather, a.pos_from, a.pos_from_by_src ? 1 : 0, a.pos_to, fr);
+}
+
+template <typename T, int LAYOUT, int CPR>
+void launch_lane(const RopeArgs& a, const Freqs& fr, hipStream_t s) {
+  if (!a.gather && !a.pos_from) return launch_lane_ix<T, LAYOUT, CPR, IX_APPLY>(a, fr, s);
+  if (a.gather && a.pos_from && !a.pos_from_by_src) return launch_lane_ix<T, LAYOUT, CPR, IX_GATHER_ROW>(a, fr, s);
+  if (a.gather && a.pos_from && a.pos_from_by_src) return launch_lane_ix<T, LAYOUT, CPR, IX_GATHER_SRC>(a, fr, s);
+  launch_lane_ix<T, LAYOUT, CPR, IX_ANY>(a, fr, s);
 }
 
 template <typename T, int LAYOUT>
@@ -254,8 +278,9 @@ void launch_t(const RopeArgs& a, const Freqs& fr, hipStream_t s) {
 
 int launch_rope(const RopeArgs& a, void* stream) {
   Freqs fr;
-  for (int i = 0; i < a.d / 2; ++i) fr.theta[i] = std::pow(a.base, -2.0 * i / a.d);
-  for (int i = a.d / 2; i < 128; ++i) fr.theta[i] = 0.0;
+  const double two_pi = 6.283185307179586476925286766559;
+  for (int i = 0; i < a.d / 2; ++i) fr.rev[i] = std::pow(a.base, -2.0 * i / a.d) / two_pi;
+  for (int i = a.d / 2; i < 128; ++i) fr.rev[i] = 0.0;
   const long long threads = a.n_rows * ((a.heads + 7) / 8) * 8LL * (a.d / 16);   // the larger of the two forms
   if ((threads + 255) / 256 > 0x7fffffffLL) return fail(AKV_EINVAL, "too many rows for one launch");
   hipStream_t s = (hipStream_t)stream;
