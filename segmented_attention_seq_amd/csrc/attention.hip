@@ -44,6 +44,7 @@ typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
 
@@ -425,14 +426,23 @@ __device__ __forceinline__ void load_q(WaveState& w, uint16_t* lqw, const uint16
   w.shifted = false;
 }
 
+// Normalised output rows as bf16, and the optional LSE.  STAGED: the wave's 64 x 64
+// output tile first goes to its own Q' rows of LDS (no longer read once the tile
+// loop and any rescaling pass are done), then every store instruction writes eight
+// whole 128-byte token rows with streaming stores.  The output (T x Hq x 128 B)
+// outgrows the last-level cache; cached stores would leave dirty lines there for
+// the next kernel to write back, and streaming stores of the 8-byte pieces the MFMA
+// layout holds per lane would reach HBM as partial-line writes.  Without staging the
+// pieces are stored directly (cached).
+template <bool STAGED>
 __device__ __forceinline__ void store_out(const WaveState& w, uint16_t* out, float* lse, int q0, int q1,
-                                          int hq, int h, int lq, int lg) {
+                                          int hq, int h, int lq, int lg, uint16_t* stage, int lane) {
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const int tok = q0 + qb * 32 + lq;
-    if (tok >= q1) continue;
+    if (!STAGED && tok >= q1) continue;
     const float inv = 1.f / w.lrun[qb];
-    uint16_t* dst = out + ((long long)tok * hq + h) * D;
+    uint16_t* dst = STAGED ? stage + (qb * 32 + lq) * KP : out + ((long long)tok * hq + h) * D;
 #pragma unroll
     for (int db = 0; db < 2; ++db)
 #pragma unroll
@@ -446,7 +456,20 @@ __device__ __forceinline__ void store_out(const WaveState& w, uint16_t* out, flo
         *(uint2*)(dst + d0) = u;
       }
     // natural-log sum of exp(scale * score) = (ms + log2 l) / log2 e
-    if (lse && lg == 0) lse[(long long)tok * hq + h] = (w.ms[qb] + __log2f(w.lrun[qb])) / kLog2e;
+    if (lse && lg == 0 && tok < q1) lse[(long long)tok * hq + h] = (w.ms[qb] + __log2f(w.lrun[qb])) / kLog2e;
+  }
+  if (STAGED) {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the tile is in LDS before this wave reads it back
+    const int c = lane & 7;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int row = 8 * i + (lane >> 3);
+      const int tok = q0 + row;
+      if (tok < q1) {
+        const u32x4 v = *(const u32x4*)(stage + row * KP + 8 * c);
+        __builtin_nontemporal_store(v, (u32x4*)(out + ((long long)tok * hq + h) * D + 8 * c));
+      }
+    }
   }
 }
 
@@ -563,7 +586,7 @@ __global__ __launch_bounds__(64 * GROUP) void seg_attn_bf16(AKV_ATTN_PARAMS) {
     if (has_next) st.stash(lk[buf ^ 1], lv[buf ^ 1], mtok[buf ^ 1], mdrop[buf ^ 1], (en & 3) == AKV_TILE_PARTIAL);
     lds_barrier();
   }
-  store_out(w, out, lse, q0, q1, hq, h, lq, lg);
+  store_out<false>(w, out, lse, q0, q1, hq, h, lq, lg, nullptr, lane);
 }
 
 // Ping-pong pipeline for 8 query heads per kv head (8 waves, two per SIMD).
@@ -700,7 +723,7 @@ __global__ __launch_bounds__(kPPThreads) void seg_attn_bf16_pp(AKV_ATTN_PARAMS) 
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) w.lrun[qb] = ls[qb][0];
   }
-  store_out(w, out, lse, q0, q1, hq, h, lq, lg);
+  store_out<true>(w, out, lse, q0, q1, hq, h, lq, lg, lqw, lane);
 }
 
 // float32 path: one thread per (query token, head), keys walked one at a time

@@ -73,17 +73,36 @@ template <> struct Vec8<float> {
   }
 };
 
+typedef unsigned rs_u32x4 __attribute__((ext_vector_type(4)));
+typedef float rs_f32x4 __attribute__((ext_vector_type(4)));
+
+// 8 elements stored as streaming (nontemporal) writes
+__device__ __forceinline__ void store8_nt(uint16_t* p, const float f[8]) {
+  const rs_u32x4 u = {pack_bf16(f[0], f[1]), pack_bf16(f[2], f[3]), pack_bf16(f[4], f[5]), pack_bf16(f[6], f[7])};
+  __builtin_nontemporal_store(u, (rs_u32x4*)p);
+}
+__device__ __forceinline__ void store8_nt(float* p, const float f[8]) {
+  const rs_f32x4 a = {f[0], f[1], f[2], f[3]}, b = {f[4], f[5], f[6], f[7]};
+  __builtin_nontemporal_store(a, (rs_f32x4*)p);
+  __builtin_nontemporal_store(b, (rs_f32x4*)(p + 4));
+}
+
 // 8 consecutive elements moved bit for bit (value rows of versions and reuse)
 template <typename T> struct Raw8;
 template <> struct Raw8<uint16_t> {
-  uint4 u;
-  __device__ __forceinline__ void load(const uint16_t* p) { u = *(const uint4*)p; }
-  __device__ __forceinline__ void store(uint16_t* p) const { *(uint4*)p = u; }
+  rs_u32x4 u;
+  __device__ __forceinline__ void load(const uint16_t* p) { u = *(const rs_u32x4*)p; }
+  __device__ __forceinline__ void store(uint16_t* p) const { *(rs_u32x4*)p = u; }
+  __device__ __forceinline__ void store_nt(uint16_t* p) const { __builtin_nontemporal_store(u, (rs_u32x4*)p); }
 };
 template <> struct Raw8<float> {
-  float4 a, b;
-  __device__ __forceinline__ void load(const float* p) { a = *(const float4*)p; b = *(const float4*)(p + 4); }
-  __device__ __forceinline__ void store(float* p) const { *(float4*)p = a; *(float4*)(p + 4) = b; }
+  rs_f32x4 a, b;
+  __device__ __forceinline__ void load(const float* p) { a = *(const rs_f32x4*)p; b = *(const rs_f32x4*)(p + 4); }
+  __device__ __forceinline__ void store(float* p) const { *(rs_f32x4*)p = a; *(rs_f32x4*)(p + 4) = b; }
+  __device__ __forceinline__ void store_nt(float* p) const {
+    __builtin_nontemporal_store(a, (rs_f32x4*)p);
+    __builtin_nontemporal_store(b, (rs_f32x4*)(p + 4));
+  }
 };
 
 template <typename T, int LAYOUT>
@@ -232,11 +251,25 @@ __global__ __launch_bounds__(256) void rope_lane_kernel(T* __restrict__ out, con
       yb[2 * i + 1] = b[2 * i] * sn[i + 4] + b[2 * i + 1] * cs[i + 4];
     }
   }
-  Vec8<T>::store(out + off_out + oa, ya);
-  Vec8<T>::store(out + off_out + ob, yb);
+  // Rows of a gathered form (repos, reuse, versions) are new copies written once:
+  // streaming stores keep them from leaving dirty lines in the last-level cache for
+  // the next kernel to write back.  RoPE-apply output is read right away by the
+  // attention, so it stays cached.
+  if constexpr (IX == IX_APPLY) {
+    Vec8<T>::store(out + off_out + oa, ya);
+    Vec8<T>::store(out + off_out + ob, yb);
+  } else {
+    store8_nt(out + off_out + oa, ya);
+    store8_nt(out + off_out + ob, yb);
+  }
   if (vout) {
-    va.store(vout + off_out + oa);
-    vb.store(vout + off_out + ob);
+    if constexpr (IX == IX_APPLY) {
+      va.store(vout + off_out + oa);
+      vb.store(vout + off_out + ob);
+    } else {
+      va.store_nt(vout + off_out + oa);
+      vb.store_nt(vout + off_out + ob);
+    }
   }
 }
 
