@@ -253,29 +253,49 @@ __global__ __launch_bounds__(64) void decode_merge(const float* __restrict__ ws,
   const int cnt = (int)(w1 - w0 + 1);
   const long long stride = (long long)hkv * grp * (D + 2);
   const float* base = ws + ((w0 + b) * hkv * grp + (long long)g * grp + j) * (D + 2);
+  const float* po = base + lane;
+  // The partial outputs of the first PF slots are requested first, so their latency
+  // overlaps the (max, sum) loads and reductions; lane s reads slot s's (max, sum).
+  constexpr int PF = 32;
+  float pv[PF];
+#pragma unroll
+  for (int s = 0; s < PF; ++s) pv[s] = s < cnt ? po[s * stride] : 0.f;
+  float ms[(kDecodeWGs + 64) / 64], lsv[(kDecodeWGs + 64) / 64];
   float M = -INFINITY;
-  for (int s = lane; s < cnt; s += 64) {
-    const long long w = w0 + s;
-    const bool has = range_begin(w, N, P) < range_begin(w + 1, N, P);  // empty ranges wrote nothing
-    if (has) M = fmaxf(M, base[s * stride + D]);
+#pragma unroll
+  for (int k = 0; k < (kDecodeWGs + 64) / 64; ++k) {
+    const int s = lane + 64 * k;
+    ms[k] = -INFINITY;
+    lsv[k] = 0.f;
+    if (s < cnt) {
+      const long long w = w0 + s;
+      if (range_begin(w, N, P) < range_begin(w + 1, N, P)) {  // empty ranges wrote nothing
+        ms[k] = base[s * stride + D];
+        lsv[k] = base[s * stride + D + 1];
+      }
+    }
+    M = fmaxf(M, ms[k]);
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
   float L = 0.f;
-  for (int s = lane; s < cnt; s += 64) {
-    const long long w = w0 + s;
-    const bool has = range_begin(w, N, P) < range_begin(w + 1, N, P);
-    const float wt = has ? exp2f((base[s * stride + D] - M) * sl2) : 0.f;
-    wgt[s] = wt;
-    if (has) L = fmaf(wt, base[s * stride + D + 1], L);
+#pragma unroll
+  for (int k = 0; k < (kDecodeWGs + 64) / 64; ++k) {
+    const int s = lane + 64 * k;
+    const float wt = ms[k] > -INFINITY ? exp2f((ms[k] - M) * sl2) : 0.f;
+    if (s < cnt) wgt[s] = wt;
+    L = fmaf(wt, lsv[k], L);
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) L += __shfl_xor(L, off);
   __syncthreads();
   float acc = 0.f;
-  const float* po = base + lane;
-#pragma unroll 8
-  for (int s = 0; s < cnt; ++s) {
+#pragma unroll
+  for (int s = 0; s < PF; ++s) {
+    const float wt = s < cnt ? wgt[s] : 0.f;
+    if (wt != 0.f) acc = fmaf(wt, pv[s], acc);  // stale slots (weight 0) may hold anything
+  }
+  for (int s = PF; s < cnt; ++s) {
     const float wt = wgt[s];
     if (wt != 0.f) acc = fmaf(wt, po[s * stride], acc);
   }
