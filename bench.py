@@ -189,9 +189,15 @@ def main():
     host_ms = []
     keep_plans = []
 
+    def mark():
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()
+        return e
+
     def step(i, timed):
         t0 = time.perf_counter()
         ev = {}
+        last = None
         if "restore" in only:
             plan = akv.build_visibility(akv.ops_from_messages(*req_ops))
             buf = dev_plans[i % 2]
@@ -204,31 +210,32 @@ def main():
             keep_plans.append(plan)
             del keep_plans[:-3]      # host images stay alive until their copies ran
             host_ms.append((time.perf_counter() - t0) * 1e3)
-            e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-            e[0].record()
+            # One event between consecutive stages (each record is a marker packet
+            # of a few microseconds on the GPU timeline): stage k runs from mark k to
+            # mark k+1.
+            m0 = mark()
             akv.rope_apply(plan, bufs["q_rot"], qd)
             akv.rope_apply(plan, bufs["k_rot"], kd)
-            e[1].record()
+            m1 = mark()
+            m2 = m1
             if nv:
                 akv.build_kv_versions(plan, bufs["k_rot"], vd, bufs["k_ver"], bufs["v_ver"])
-            e[2].record()
+                m2 = mark()
             akv.segment_attention(plan, bufs["q_rot"], bufs["k_rot"], vd, bufs["k_ver"], bufs["v_ver"],
                                   bufs["out"])
-            e[3].record()
-            ev.update(rope=(e[0], e[1]), versions=(e[1], e[2]), attn=(e[2], e[3]))
+            last = mark()
+            ev.update(rope=(m0, m1), versions=(m1, m2), attn=(m2, last))
         if "repos" in only:
             pool, out = repos_sets[i % len(repos_sets)]
-            e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-            e[0].record()
+            start = last if last is not None else mark()
             akv.rope_repos(out, pool, r_to, r_from, r_idx)
-            e[1].record()
-            ev["repos"] = (e[0], e[1])
+            last = mark()
+            ev["repos"] = (start, last)
         if "decode" in only:
-            e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-            e[0].record()
+            start = last if last is not None else mark()
             akv.decode_attention(dq, pool_k, pool_v, d_indptr, d_indices, max_n, dout, ws=dws)
-            e[1].record()
-            ev["decode"] = (e[0], e[1])
+            last = mark()
+            ev["decode"] = (start, last)
         return ev
 
     for i in range(args.warmup):

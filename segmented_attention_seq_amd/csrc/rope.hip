@@ -6,11 +6,10 @@
 // matrix and leaves the value untouched; "single-prefill restore" (§4.2, App.
 // A.1.1): per-segment KV versions are made by key rotation and value copy.
 //
-// Bandwidth-bound.  For head dims 16-128 one thread handles one 8-pair chunk of
-// one head of a row and the chunk's (cos, sin) values are shared across the
-// threads of 8 heads by cross-lane shuffle (rope_lane_kernel); other head dims use
-// one thread per chunk that walks every head of the row.  Loads and stores are
-// 16-byte vectors; a wave's two loads together read whole 128-byte lines.
+// Bandwidth-bound.  For head dims 16-128 one thread writes one 16-byte output chunk
+// of one head (rope_row_kernel), so stores cover whole 128-byte head rows, and the
+// (cos, sin) values are shared across a group of heads by cross-lane shuffle; other
+// head dims use one thread per 8-pair chunk that walks every head of the row.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -161,40 +160,39 @@ __global__ __launch_bounds__(256) void rope_kernel(T* __restrict__ out, const T*
   }
 }
 
-// Lane-per-head form for d in {16, 32, 64, 128}: one thread per (row, head, chunk),
-// so every thread moves 16-32 bytes each way and the grid holds enough waves to keep
-// the memory system busy (one thread walking all heads of a row leaves a few
-// thousand waves, each waiting on one head after another).  The 8 threads that share
-// a (row, group of 8 heads, chunk) each compute one of the chunk's 8 (cos, sin) pairs
-// and fetch the other seven from their neighbours by cross-lane shuffle, so the angle
-// work stays one evaluation per thread.  Lane layout inside a wave: groups of
-// G = 8 * CPR lanes, lane = h8 * CPR + c, with G dividing 64.
-// Index forms of the lane kernel, fixed at compile time so that independent index
+// Index forms of the row kernel, fixed at compile time so that independent index
 // loads issue together: apply (no gather, rotation from position 0), repos and
 // reuse (gather, pos_from by output row), versions (gather, pos_from by source
 // row); anything else reads the pointers at run time.
 enum { IX_APPLY = 0, IX_GATHER_ROW = 1, IX_GATHER_SRC = 2, IX_ANY = 3 };
 
+// Row form for d in {16, 32, 64, 128}: one thread per 16-byte output chunk of one
+// head, so each store instruction writes whole 128-byte head rows (a group of HG
+// heads x 2*CPR chunks, HG = min(8, 32 / CPR), fills G <= 64 lanes).  In the half
+// layout a chunk's pairs span both halves of the head vector: the two threads that
+// own chunk c of the first and of the second half both load the chunk's two input
+// pieces (the second load is a cache hit) and each writes its own half.  In the
+// interleaved layout a chunk holds four whole pairs.  Each thread evaluates one
+// angle, pair (lane in group) mod d/2, and fetches the ones it needs by shuffle.
 template <typename T, int LAYOUT, int CPR, int IX>
-__global__ __launch_bounds__(256) void rope_lane_kernel(T* __restrict__ out, const T* __restrict__ in,
-                                                        T* __restrict__ vout, const T* __restrict__ vin,
-                                                        long long n_rows, int heads, int n_hg,
-                                                        const int* __restrict__ gather,
-                                                        const int* __restrict__ pos_from, int from_by_src,
-                                                        const int* __restrict__ pos_to, Freqs fr) {
-  constexpr int G = 8 * CPR;
+__global__ __launch_bounds__(256) void rope_row_kernel(T* __restrict__ out, const T* __restrict__ in,
+                                                       T* __restrict__ vout, const T* __restrict__ vin,
+                                                       long long n_rows, int heads, int n_hg,
+                                                       const int* __restrict__ gather,
+                                                       const int* __restrict__ pos_from, int from_by_src,
+                                                       const int* __restrict__ pos_to, Freqs fr) {
+  constexpr int LPH = 2 * CPR;                      // lanes (16-byte chunks) per head
+  constexpr int HG = 32 / CPR < 8 ? 32 / CPR : 8;   // heads per group
+  constexpr int G = HG * LPH;
   constexpr int D = 16 * CPR;
   const long long tid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   const long long grp = tid / G;
   const int l = (int)(tid - grp * G);
   const long long row = grp / n_hg;
-  if (row >= n_rows) return;  // whole groups leave together: a group never spans two rows
+  if (row >= n_rows) return;  // whole groups leave together
   const int hg = (int)(grp - row * n_hg);
-  const int h8 = l / CPR, c = l - h8 * CPR;
-  const int h = hg * 8 + h8;
-  // Position and frequency loads go first, then the row's data, so the angle work
-  // waits only for the former (loads complete in order) and overlaps the latter;
-  // lanes past the last head (heads % 8 != 0) read the last head and store nothing.
+  const int hl = l / LPH, j = l - hl * LPH;
+  const int h = hg * HG + hl;
   long long src, delta;
   if constexpr (IX == IX_APPLY) {
     src = row;
@@ -211,93 +209,86 @@ __global__ __launch_bounds__(256) void rope_lane_kernel(T* __restrict__ out, con
     src = gather ? (long long)gather[row] : row;
     delta = (long long)pos_to[row] - (pos_from ? (long long)pos_from[from_by_src ? src : row] : 0LL);
   }
-  const double th = fr.rev[c * 8 + h8];
-  const int hc = h < heads ? h : heads - 1;
+  const double th = fr.rev[l % (D / 2)];
+  const int hc = h < heads ? h : heads - 1;   // lanes past the last head load a real row, store nothing
   const long long off_in = (src * heads + hc) * D, off_out = (row * heads + h) * D;
-  int oa, ob;
-  if (LAYOUT == AKV_ROPE_HALF) { oa = c * 8; ob = D / 2 + c * 8; }
-  else { oa = c * 16; ob = c * 16 + 8; }
+  const bool second = LAYOUT == AKV_ROPE_HALF && j >= CPR;
+  const int c = LAYOUT == AKV_ROPE_HALF ? (second ? j - CPR : j) : j;
   float a[8], b[8];
-  Vec8<T>::load(in + off_in + oa, a);
-  Vec8<T>::load(in + off_in + ob, b);
-  Raw8<T> va, vb;
-  if (vout) {
-    va.load(vin + off_in + oa);
-    vb.load(vin + off_in + ob);
+  if (LAYOUT == AKV_ROPE_HALF) {
+    Vec8<T>::load(in + off_in + 8 * c, a);
+    Vec8<T>::load(in + off_in + D / 2 + 8 * c, b);
+  } else {
+    Vec8<T>::load(in + off_in + 8 * j, a);
   }
+  Raw8<T> vv;
+  if (vout) vv.load(vin + off_in + 8 * j);
   float mc, ms;
   angle_cs(delta, th, mc, ms);
-  const int base = (int)(threadIdx.x & 63) - l;   // first lane of this group in the wave
-  float cs[8], sn[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    cs[i] = __shfl(mc, base + i * CPR + c, 64);
-    sn[i] = __shfl(ms, base + i * CPR + c, 64);
-  }
-  if (h >= heads) return;
-  float ya[8], yb[8];
+  const int base = (int)(threadIdx.x & 63) - l;
+  float y[8];
   if (LAYOUT == AKV_ROPE_HALF) {
+    float cs[8], sn[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      ya[i] = a[i] * cs[i] - b[i] * sn[i];
-      yb[i] = a[i] * sn[i] + b[i] * cs[i];
+      cs[i] = __shfl(mc, base + 8 * c + i, 64);
+      sn[i] = __shfl(ms, base + 8 * c + i, 64);
     }
+    if (h >= heads) return;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) y[i] = second ? a[i] * sn[i] + b[i] * cs[i] : a[i] * cs[i] - b[i] * sn[i];
   } else {
+    float cs[4], sn[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      ya[2 * i] = a[2 * i] * cs[i] - a[2 * i + 1] * sn[i];
-      ya[2 * i + 1] = a[2 * i] * sn[i] + a[2 * i + 1] * cs[i];
-      yb[2 * i] = b[2 * i] * cs[i + 4] - b[2 * i + 1] * sn[i + 4];
-      yb[2 * i + 1] = b[2 * i] * sn[i + 4] + b[2 * i + 1] * cs[i + 4];
+      cs[i] = __shfl(mc, base + 4 * j + i, 64);
+      sn[i] = __shfl(ms, base + 4 * j + i, 64);
+    }
+    if (h >= heads) return;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      y[2 * i] = a[2 * i] * cs[i] - a[2 * i + 1] * sn[i];
+      y[2 * i + 1] = a[2 * i] * sn[i] + a[2 * i + 1] * cs[i];
     }
   }
-  // Rows of a gathered form (repos, reuse, versions) are new copies written once:
-  // streaming stores keep them from leaving dirty lines in the last-level cache for
-  // the next kernel to write back.  RoPE-apply output is read right away by the
-  // attention, so it stays cached.
+  // Gathered forms write new copies once: streaming stores, so the next kernel finds
+  // no dirty lines to write back.  RoPE-apply output is read right away by the
+  // attention and stays cached.
   if constexpr (IX == IX_APPLY) {
-    Vec8<T>::store(out + off_out + oa, ya);
-    Vec8<T>::store(out + off_out + ob, yb);
+    Vec8<T>::store(out + off_out + 8 * j, y);
+    if (vout) vv.store(vout + off_out + 8 * j);
   } else {
-    store8_nt(out + off_out + oa, ya);
-    store8_nt(out + off_out + ob, yb);
-  }
-  if (vout) {
-    if constexpr (IX == IX_APPLY) {
-      va.store(vout + off_out + oa);
-      vb.store(vout + off_out + ob);
-    } else {
-      va.store_nt(vout + off_out + oa);
-      vb.store_nt(vout + off_out + ob);
-    }
+    store8_nt(out + off_out + 8 * j, y);
+    if (vout) vv.store_nt(vout + off_out + 8 * j);
   }
 }
 
 template <typename T, int LAYOUT, int CPR, int IX>
-void launch_lane_ix(const RopeArgs& a, const Freqs& fr, hipStream_t s) {
-  const int n_hg = (a.heads + 7) / 8;
-  const long long threads = a.n_rows * n_hg * (8LL * CPR);
+void launch_row_ix(const RopeArgs& a, const Freqs& fr, hipStream_t s) {
+  constexpr int HG = 32 / CPR < 8 ? 32 / CPR : 8;
+  const int n_hg = (a.heads + HG - 1) / HG;
+  const long long threads = a.n_rows * n_hg * (long long)(HG * 2 * CPR);
   const unsigned blocks = (unsigned)((threads + 255) / 256);
-  hipLaunchKernelGGL((rope_lane_kernel<T, LAYOUT, CPR, IX>), dim3(blocks), dim3(256), 0, s, (T*)a.out,
+  hipLaunchKernelGGL((rope_row_kernel<T, LAYOUT, CPR, IX>), dim3(blocks), dim3(256), 0, s, (T*)a.out,
                      (const T*)a.in, (T*)a.v_out, (const T*)a.v_in, (long long)a.n_rows, a.heads, n_hg,
                      a.gather, a.pos_from, a.pos_from_by_src ? 1 : 0, a.pos_to, fr);
 }
 
 template <typename T, int LAYOUT, int CPR>
-void launch_lane(const RopeArgs& a, const Freqs& fr, hipStream_t s) {
-  if (!a.gather && !a.pos_from) return launch_lane_ix<T, LAYOUT, CPR, IX_APPLY>(a, fr, s);
-  if (a.gather && a.pos_from && !a.pos_from_by_src) return launch_lane_ix<T, LAYOUT, CPR, IX_GATHER_ROW>(a, fr, s);
-  if (a.gather && a.pos_from && a.pos_from_by_src) return launch_lane_ix<T, LAYOUT, CPR, IX_GATHER_SRC>(a, fr, s);
-  launch_lane_ix<T, LAYOUT, CPR, IX_ANY>(a, fr, s);
+void launch_row(const RopeArgs& a, const Freqs& fr, hipStream_t s) {
+  if (!a.gather && !a.pos_from) return launch_row_ix<T, LAYOUT, CPR, IX_APPLY>(a, fr, s);
+  if (a.gather && a.pos_from && !a.pos_from_by_src) return launch_row_ix<T, LAYOUT, CPR, IX_GATHER_ROW>(a, fr, s);
+  if (a.gather && a.pos_from && a.pos_from_by_src) return launch_row_ix<T, LAYOUT, CPR, IX_GATHER_SRC>(a, fr, s);
+  launch_row_ix<T, LAYOUT, CPR, IX_ANY>(a, fr, s);
 }
 
 template <typename T, int LAYOUT>
 void launch_t(const RopeArgs& a, const Freqs& fr, hipStream_t s) {
   switch (a.d) {
-    case 16: return launch_lane<T, LAYOUT, 1>(a, fr, s);
-    case 32: return launch_lane<T, LAYOUT, 2>(a, fr, s);
-    case 64: return launch_lane<T, LAYOUT, 4>(a, fr, s);
-    case 128: return launch_lane<T, LAYOUT, 8>(a, fr, s);
+    case 16: return launch_row<T, LAYOUT, 1>(a, fr, s);
+    case 32: return launch_row<T, LAYOUT, 2>(a, fr, s);
+    case 64: return launch_row<T, LAYOUT, 4>(a, fr, s);
+    case 128: return launch_row<T, LAYOUT, 8>(a, fr, s);
     default: break;
   }
   const long long threads = a.n_rows * (a.d / 16);
@@ -314,7 +305,7 @@ int launch_rope(const RopeArgs& a, void* stream) {
   const double two_pi = 6.283185307179586476925286766559;
   for (int i = 0; i < a.d / 2; ++i) fr.rev[i] = std::pow(a.base, -2.0 * i / a.d) / two_pi;
   for (int i = a.d / 2; i < 128; ++i) fr.rev[i] = 0.0;
-  const long long threads = a.n_rows * ((a.heads + 7) / 8) * 8LL * (a.d / 16);   // the larger of the two forms
+  const long long threads = a.n_rows * (a.heads + 7LL) * (a.d / 8);   // bound for every form
   if ((threads + 255) / 256 > 0x7fffffffLL) return fail(AKV_EINVAL, "too many rows for one launch");
   hipStream_t s = (hipStream_t)stream;
   (void)hipGetLastError();
