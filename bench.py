@@ -141,7 +141,7 @@ def main():
     nv = int(plan0.info["n_versions"])
     pairs = int(plan0.info["visible_pairs"])
     attn_flop = 4.0 * d * hq * pairs
-    bufs = {"q_rot": torch.empty_like(qd), "k_rot": torch.empty_like(kd),
+    bufs = {"k_rot": torch.empty_like(kd),
             "k_ver": torch.empty((nv, hkv, d), dtype=torch.bfloat16, device=dev),
             "v_ver": torch.empty((nv, hkv, d), dtype=torch.bfloat16, device=dev),
             "out": torch.empty_like(qd)}
@@ -214,15 +214,14 @@ def main():
             # of a few microseconds on the GPU timeline): stage k runs from mark k to
             # mark k+1.
             m0 = mark()
-            akv.rope_apply(plan, bufs["q_rot"], qd)
-            akv.rope_apply(plan, bufs["k_rot"], kd)
+            akv.rope_apply(plan, bufs["k_rot"], kd)   # queries are rotated inside the attention
             m1 = mark()
             m2 = m1
             if nv:
                 akv.build_kv_versions(plan, bufs["k_rot"], vd, bufs["k_ver"], bufs["v_ver"])
                 m2 = mark()
-            akv.segment_attention(plan, bufs["q_rot"], bufs["k_rot"], vd, bufs["k_ver"], bufs["v_ver"],
-                                  bufs["out"])
+            akv.segment_attention(plan, qd, bufs["k_rot"], vd, bufs["k_ver"], bufs["v_ver"], bufs["out"],
+                                  rope_base=workload.ROPE_BASE)
             last = mark()
             ev.update(rope=(m0, m1), versions=(m1, m2), attn=(m2, last))
         if "repos" in only:
@@ -269,7 +268,7 @@ def main():
                            "frac": gbs / PEAK_HBM_GBS, "bytes_per_launch": decode_bytes,
                            "gathered_keys": n_keys, "requests": int(db.q.shape[0])}
     if avg["rope"]:
-        rope_bytes = 2 * (qd.numel() + kd.numel()) * 2 + 8 * T
+        rope_bytes = 2 * kd.numel() * 2 + 4 * T
         comps["rope_apply_gbs"] = rope_bytes / (avg["rope"] * 1e-3) / 1e9
     if avg["versions"] and nv:
         comps["versions_gbs"] = (nv * hkv * d * 2 * 4 + 12 * nv) / (avg["versions"] * 1e-3) / 1e9

@@ -208,13 +208,28 @@ int akv_build_kv_versions(const akv_plan* plan, const void* dev_plan, const void
  * q, k: rotated to append positions; out [n_tokens][hq][d]; lse (nullable, float32
  * [n_tokens][hq]) receives the natural-log sum of exp(scale * score).
  * scale <= 0 means 1/sqrt(d).  bf16 needs d == 64 and plan bq == bk == 64; f32
- * (a CUDA-core path for small problems) needs d <= 128.
+ * (a vector-ALU path for small problems) needs d <= 128.
  */
 int akv_segment_attention(const akv_plan* plan, const void* dev_plan,
                           const void* q, const void* k, const void* v,
                           const void* k_ver, const void* v_ver, void* out, float* lse,
                           int dtype, int32_t hq, int32_t hkv, int32_t d, float scale,
                           akv_stream_t stream);
+
+/* As akv_segment_attention, with the queries given raw (q_raw [n_tokens][hq][d],
+ * unrotated, "at position 0"): the attention rotates each query to its append
+ * position tok_pos (T1) as it loads it, in fp32 from the raw values, so no rotated
+ * copy of Q is written and read back (review §3.3: a vector at position p is the
+ * raw vector rotated pair by pair by p * theta_i).  k must still be rotated
+ * (akv_rope_apply); k_ver / v_ver as above.  rope_base > 1 and finite; rope_layout
+ * AKV_ROPE_HALF or AKV_ROPE_INTERLEAVED; d even and <= 128 (bf16: d == 64).
+ * Errors as akv_segment_attention, plus AKV_EINVAL for a bad base or layout.
+ */
+int akv_segment_attention_rope(const akv_plan* plan, const void* dev_plan,
+                               const void* q_raw, const void* k, const void* v,
+                               const void* k_ver, const void* v_ver, void* out, float* lse,
+                               int dtype, int32_t hq, int32_t hkv, int32_t d, float scale,
+                               double rope_base, int rope_layout, akv_stream_t stream);
 
 /* ---------------------------------------------------------------- A6: decode
  *

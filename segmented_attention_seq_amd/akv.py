@@ -94,6 +94,8 @@ _sig("akv_rope_apply", C.c_int, _vp, _vp, _vp, _vp, C.c_int, _i32, _i32, _f64, C
 _sig("akv_build_kv_versions", C.c_int, _vp, _vp, _vp, _vp, _vp, _vp, C.c_int, _i32, _i32, _f64, C.c_int, _vp)
 _sig("akv_segment_attention", C.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, C.c_int, _i32, _i32,
      _i32, _f32, _vp)
+_sig("akv_segment_attention_rope", C.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, C.c_int, _i32, _i32,
+     _i32, _f32, _f64, C.c_int, _vp)
 _sig("akv_decode_workspace_bytes", _u64, _i32, _i32, _i32, _i32, _i64)
 _sig("akv_decode_attention", C.c_int, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i64, _f32, C.c_int,
      _vp, _vp, _vp, _u64, _vp)
@@ -108,7 +110,7 @@ _sig("akv_cache_stats_get", C.c_int, _vp, C.POINTER(akv_cache_stats))
 EXPORTED = ["akv_status_string", "akv_last_error", "akv_version", "akv_ops_from_messages",
             "akv_build_visibility", "akv_plan_info_get", "akv_plan_tables_get", "akv_plan_upload",
             "akv_plan_destroy", "akv_rope_repos", "akv_kv_reuse", "akv_rope_apply", "akv_build_kv_versions",
-            "akv_segment_attention", "akv_decode_workspace_bytes", "akv_decode_attention",
+            "akv_segment_attention", "akv_segment_attention_rope", "akv_decode_workspace_bytes", "akv_decode_attention",
             "akv_cache_create", "akv_cache_destroy", "akv_cache_match", "akv_cache_alloc",
             "akv_cache_insert", "akv_cache_unlock", "akv_cache_stats_get"]
 
@@ -388,7 +390,11 @@ def build_kv_versions(plan: Plan, k, v, k_ver, v_ver, base: float = 150000.0, la
                                       layout, _stream(dev)), "akv_build_kv_versions")
 
 
-def segment_attention(plan: Plan, q, k, v, k_ver, v_ver, out, lse=None, scale: float = 0.0):
+def segment_attention(plan: Plan, q, k, v, k_ver, v_ver, out, lse=None, scale: float = 0.0,
+                      rope_base: Optional[float] = None, layout: int = ROPE_HALF):
+    """Segment attention (akv_segment_attention).  With rope_base set, q is raw and
+    is rotated to its append positions inside the attention
+    (akv_segment_attention_rope)."""
     import torch
     T, hq, d = q.shape
     hkv = k.shape[1]
@@ -405,9 +411,15 @@ def segment_attention(plan: Plan, q, k, v, k_ver, v_ver, out, lse=None, scale: f
         vvp = _req(v_ver, "v_ver", q.dtype, (nv, hkv, d), dev)
     _req(out, "out", q.dtype, (T, hq, d), dev)
     lp = _req(lse, "lse", torch.float32, (T, hq), dev) if lse is not None else None
-    _check(_lib.akv_segment_attention(plan.handle, plan.upload(dev).data_ptr(), q.data_ptr(), k.data_ptr(),
-                                      v.data_ptr(), kvp, vvp, out.data_ptr(), lp, _dtype_code(q), hq, hkv,
-                                      d, scale, _stream(dev)), "akv_segment_attention")
+    if rope_base is None:
+        _check(_lib.akv_segment_attention(plan.handle, plan.upload(dev).data_ptr(), q.data_ptr(), k.data_ptr(),
+                                          v.data_ptr(), kvp, vvp, out.data_ptr(), lp, _dtype_code(q), hq, hkv,
+                                          d, scale, _stream(dev)), "akv_segment_attention")
+    else:
+        _check(_lib.akv_segment_attention_rope(plan.handle, plan.upload(dev).data_ptr(), q.data_ptr(),
+                                               k.data_ptr(), v.data_ptr(), kvp, vvp, out.data_ptr(), lp,
+                                               _dtype_code(q), hq, hkv, d, scale, float(rope_base), layout,
+                                               _stream(dev)), "akv_segment_attention_rope")
     return out
 
 
@@ -440,18 +452,21 @@ def decode_attention(q, k_pool, v_pool, indptr, indices, max_n: int, out, lse=No
 
 
 def restore(plan: Plan, q_raw, k_raw, v, base: float = 150000.0, layout: int = ROPE_HALF,
-            with_lse: bool = False, scale: float = 0.0, bufs: Optional[dict] = None):
-    """Restore prefill: RoPE-apply Q and K to their append positions, build the
-    per-stretch KV versions, run segment attention.  Returns (out, lse or None).
-    `bufs` may hold preallocated q_rot/k_rot/k_ver/v_ver/out/lse tensors."""
+            with_lse: bool = False, scale: float = 0.0, bufs: Optional[dict] = None, fuse_q: bool = True):
+    """Restore prefill: RoPE-apply K to its append positions, build the per-stretch
+    KV versions, run segment attention, which rotates the raw queries as it loads
+    them (fuse_q=False: RoPE-apply Q into a rotated copy first).  Returns (out, lse
+    or None).  `bufs` may hold preallocated q_rot/k_rot/k_ver/v_ver/out/lse tensors."""
     import torch
     T, hq, d = q_raw.shape
     hkv = k_raw.shape[1]
     dev, dt = q_raw.device, q_raw.dtype
     nv = int(plan.info["n_versions"])
     b = {} if bufs is None else bufs
-    qr = b.get("q_rot")
-    qr = torch.empty_like(q_raw) if qr is None else qr
+    qr = None
+    if not fuse_q:
+        qr = b.get("q_rot")
+        qr = torch.empty_like(q_raw) if qr is None else qr
     kr = b.get("k_rot")
     kr = torch.empty_like(k_raw) if kr is None else kr
     kv = b.get("k_ver")
@@ -463,9 +478,12 @@ def restore(plan: Plan, q_raw, k_raw, v, base: float = 150000.0, layout: int = R
     lse = b.get("lse")
     if with_lse and lse is None:
         lse = torch.empty((T, hq), dtype=torch.float32, device=dev)
-    rope_apply(plan, qr, q_raw, base, layout)
     rope_apply(plan, kr, k_raw, base, layout)
     if nv:
         build_kv_versions(plan, kr, v, kv, vv, base, layout)
-    segment_attention(plan, qr, kr, v, kv, vv, out, lse if with_lse else None, scale)
+    if fuse_q:
+        segment_attention(plan, q_raw, kr, v, kv, vv, out, lse if with_lse else None, scale, base, layout)
+    else:
+        rope_apply(plan, qr, q_raw, base, layout)
+        segment_attention(plan, qr, kr, v, kv, vv, out, lse if with_lse else None, scale)
     return out, (lse if with_lse else None)

@@ -212,10 +212,11 @@ int akv_build_kv_versions(const akv_plan* p, const void* dev_plan, const void* k
   return akv::launch_rope(a, stream);
 }
 
-int akv_segment_attention(const akv_plan* p, const void* dev_plan, const void* q, const void* k,
-                          const void* v, const void* k_ver, const void* v_ver, void* out, float* lse,
-                          int dtype, int32_t hq, int32_t hkv, int32_t d, float scale,
-                          akv_stream_t stream) {
+namespace {
+
+int segment_attention(const akv_plan* p, const void* dev_plan, const void* q, const void* k, const void* v,
+                      const void* k_ver, const void* v_ver, void* out, float* lse, int dtype, int32_t hq,
+                      int32_t hkv, int32_t d, float scale, const akv::RopeQ& rq, akv_stream_t stream) {
   if (!p || !dev_plan) return fail(AKV_EINVAL, "NULL plan or device plan");
   if (dtype != AKV_F32 && dtype != AKV_BF16) return fail(AKV_EINVAL, "dtype must be AKV_F32 or AKV_BF16");
   if (hq < 1 || hkv < 1 || hq % hkv) return fail(AKV_EINVAL, "hq must be a positive multiple of hkv");
@@ -237,9 +238,36 @@ int akv_segment_attention(const akv_plan* p, const void* dev_plan, const void* q
   akv::AttnArgs a{q, k, v, k_ver, v_ver, out, lse,
                   (const int32_t*)(base + p->off_item_desc), (const int32_t*)(base + p->off_tiles),
                   (const int32_t*)(base + p->off_order), (const int32_t*)(base + p->off_tok_drop),
-                  (const int32_t*)(base + p->off_ver_src), (int64_t)p->items.size() / 2,
-                  hq, hkv, d, p->bq, p->bk, scale, dtype};
+                  (const int32_t*)(base + p->off_ver_src), (const int32_t*)(base + p->off_tok_pos),
+                  (int64_t)p->items.size() / 2, hq, hkv, d, p->bq, p->bk, scale, dtype, rq};
   return akv::launch_segment_attention(a, stream);
+}
+
+}  // namespace
+
+int akv_segment_attention(const akv_plan* p, const void* dev_plan, const void* q, const void* k,
+                          const void* v, const void* k_ver, const void* v_ver, void* out, float* lse,
+                          int dtype, int32_t hq, int32_t hkv, int32_t d, float scale,
+                          akv_stream_t stream) {
+  akv::RopeQ rq{};
+  rq.on = 0;
+  return segment_attention(p, dev_plan, q, k, v, k_ver, v_ver, out, lse, dtype, hq, hkv, d, scale, rq, stream);
+}
+
+int akv_segment_attention_rope(const akv_plan* p, const void* dev_plan, const void* q_raw, const void* k,
+                               const void* v, const void* k_ver, const void* v_ver, void* out, float* lse,
+                               int dtype, int32_t hq, int32_t hkv, int32_t d, float scale, double rope_base,
+                               int rope_layout, akv_stream_t stream) {
+  if (!(rope_base > 1.0) || !std::isfinite(rope_base)) return fail(AKV_EINVAL, "RoPE base must be finite and > 1");
+  if (rope_layout != AKV_ROPE_HALF && rope_layout != AKV_ROPE_INTERLEAVED)
+    return fail(AKV_EINVAL, "rope_layout must be AKV_ROPE_HALF or AKV_ROPE_INTERLEAVED");
+  if (d < 2 || d > 128 || d % 2) return fail(AKV_EUNSUPPORTED, "query rotation needs an even d <= 128");
+  akv::RopeQ rq{};
+  const double two_pi = 6.283185307179586476925286766559;
+  for (int i = 0; i < d / 2; ++i) rq.rev[i] = std::pow(rope_base, -2.0 * i / d) / two_pi;
+  rq.on = 1;
+  rq.layout = rope_layout;
+  return segment_attention(p, dev_plan, q_raw, k, v, k_ver, v_ver, out, lse, dtype, hq, hkv, d, scale, rq, stream);
 }
 
 uint64_t akv_decode_workspace_bytes(int32_t batch, int32_t hq, int32_t hkv, int32_t d, int64_t max_n) {

@@ -36,6 +36,7 @@
 #include <cmath>
 
 #include "internal.h"
+#include "rope_angle.h"
 
 namespace akv {
 namespace {
@@ -396,20 +397,58 @@ __device__ __forceinline__ void tile_pv(WaveState& w, const uint16_t* lvb, int l
 // Q' = Q scaled by sl2 = scale * log2(e) (re-rounded to bf16), so that QK
 // products come out in log2 units; kept in registers, or (QL) in the wave's LDS
 // rows lqw (64 rows, K pitch).
+// Q of the wave's head for its 64 query rows, times scale * log2(e), in bf16: in LDS
+// (QL) or registers.  With rq.on the raw rows are first rotated to their append
+// positions tok_pos[tok] in fp32 (the lane holds both members of each of its pairs:
+// chunk ds pairs with ds + 2 in the half layout, neighbours within a chunk in the
+// interleaved one), so the query is rounded to bf16 once.
 template <bool QL>
 __device__ __forceinline__ void load_q(WaveState& w, uint16_t* lqw, const uint16_t* q, int q0, int q1, int hq, int h,
-                                       int lq, int lg, float sl2) {
+                                       int lq, int lg, float sl2, const int* tok_pos, const RopeQ& rq) {
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const int tok = q0 + qb * 32 + lq;
     const uint4* src = (const uint4*)(q + ((long long)tok * hq + h) * D);
+    float f[4][8];
 #pragma unroll
     for (int ds = 0; ds < 4; ++ds) {
       uint4 x = make_uint4(0, 0, 0, 0);
       if (tok < q1) x = src[ds * 2 + lg];
-      bf16x8 b = __builtin_bit_cast(bf16x8, x);
+      const bf16x8 b = __builtin_bit_cast(bf16x8, x);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) b[j] = (__bf16)((float)b[j] * sl2);
+      for (int j = 0; j < 8; ++j) f[ds][j] = (float)b[j];
+    }
+    if (rq.on) {
+      const double pos = tok < q1 ? (double)tok_pos[tok] : 0.0;
+      if (rq.layout == AKV_ROPE_HALF) {
+#pragma unroll
+        for (int ds = 0; ds < 2; ++ds)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            float c, s;
+            rope_angle_cs(pos, rq.rev[ds * 16 + lg * 8 + j], c, s);
+            const float a = f[ds][j], bb = f[ds + 2][j];
+            f[ds][j] = a * c - bb * s;
+            f[ds + 2][j] = a * s + bb * c;
+          }
+      } else {
+#pragma unroll
+        for (int ds = 0; ds < 4; ++ds)
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            float c, s;
+            rope_angle_cs(pos, rq.rev[ds * 8 + lg * 4 + m], c, s);
+            const float a = f[ds][2 * m], bb = f[ds][2 * m + 1];
+            f[ds][2 * m] = a * c - bb * s;
+            f[ds][2 * m + 1] = a * s + bb * c;
+          }
+      }
+    }
+#pragma unroll
+    for (int ds = 0; ds < 4; ++ds) {
+      bf16x8 b;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) b[j] = (__bf16)(f[ds][j] * sl2);
       if (QL) *(bf16x8*)(lqw + (qb * 32 + lq) * KP + ds * 16 + lg * 8) = b;
       else w.qf[qb][ds] = b;
     }
@@ -539,7 +578,7 @@ struct TileStage {
       const int *__restrict__ item_desc, const int *__restrict__ tiles,                            \
       const int *__restrict__ order, const int *__restrict__ tok_drop,                             \
       const int *__restrict__ ver_src, uint16_t *__restrict__ out, float *__restrict__ lse,       \
-      int hq, int hkv, float scale
+      int hq, int hkv, float scale, const int *__restrict__ tok_pos, RopeQ rq
 
 // Double-buffered pipeline: tile t+1 is loaded while tile t computes.  Used when
 // the query-head group is smaller than 8 (fewer than two waves per SIMD).
@@ -562,7 +601,7 @@ __global__ __launch_bounds__(64 * GROUP) void seg_attn_bf16(AKV_ATTN_PARAMS) {
   const float sl2 = scale * kLog2e;
 
   WaveState w;
-  load_q<false>(w, nullptr, q, q0, q1, hq, h, lq, lg, sl2);
+  load_q<false>(w, nullptr, q, q0, q1, hq, h, lq, lg, sl2, tok_pos, rq);
   TileStage<NT> st;
   st.wave_s = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (t0 < t1) {
@@ -696,7 +735,7 @@ __global__ __launch_bounds__(kPPThreads) void seg_attn_bf16_pp(AKV_ATTN_PARAMS) 
   if (threadIdx.x == 0) redo = 0;  // published by the first barrier of the pipeline
 
   WaveState w;
-  load_q<true>(w, lqw, q, q0, q1, hq, h, lq, lg, sl2);
+  load_q<true>(w, lqw, q, q0, q1, hq, h, lq, lg, sl2, tok_pos, rq);
   TileStage<kPPThreads> st;
   st.wave_s = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const bf16x8 sel = colsum_selector(lane);
@@ -716,7 +755,7 @@ __global__ __launch_bounds__(kPPThreads) void seg_attn_bf16_pp(AKV_ATTN_PARAMS) 
   lds_barrier();
   if (__builtin_amdgcn_readfirstlane(redo)) {
     asm volatile("");  // rare: keep the second pipeline out of the common path
-    load_q<false>(w, nullptr, q, q0, q0, hq, h, lq, lg, 0.f);  // resets O, offsets and sums (Q' stays in LDS)
+    load_q<false>(w, nullptr, q, q0, q0, hq, h, lq, lg, 0.f, tok_pos, rq);  // resets O, offsets and sums (Q' stays in LDS)
     pp_pipeline<true>(w, ls, sel, st, lk, lv, mtok, mdrop, lqw, tiles, t0, n, nvt, voff, r, tb, te, k, v, kver,
                       vver, hkv, hk, tok_drop, ver_src, q0, lq, lg, lane, lag);
   } else {
@@ -734,7 +773,7 @@ __global__ __launch_bounds__(256) void seg_attn_f32(
     const float* __restrict__ kver, const float* __restrict__ vver, const int* __restrict__ item_desc,
     const int* __restrict__ tiles, const int* __restrict__ order, const int* __restrict__ tok_drop,
     const int* __restrict__ ver_src, float* __restrict__ out, float* __restrict__ lse, int hq,
-    int hkv, int bk, float scale) {
+    int hkv, int bk, float scale, const int* __restrict__ tok_pos, RopeQ rq) {
   const int h = blockIdx.x % hq;
   const int item = order[blockIdx.x / hq];
   const int g = h / (hq / hkv);
@@ -748,6 +787,18 @@ __global__ __launch_bounds__(256) void seg_attn_f32(
   const float* qp = q + ((long long)tok * hq + h) * DD;
 #pragma unroll
   for (int i = 0; i < DD; ++i) { qv[i] = qp[i]; acc[i] = 0.f; }
+  if (rq.on) {  // raw query: rotate to its append position
+    const double pos = (double)tok_pos[tok];
+#pragma unroll
+    for (int i = 0; i < DD / 2; ++i) {
+      float c, s;
+      rope_angle_cs(pos, rq.rev[i], c, s);
+      const int ia = rq.layout == AKV_ROPE_HALF ? i : 2 * i, ib = rq.layout == AKV_ROPE_HALF ? i + DD / 2 : 2 * i + 1;
+      const float a = qv[ia], b = qv[ib];
+      qv[ia] = a * c - b * s;
+      qv[ib] = a * s + b * c;
+    }
+  }
   float m = -INFINITY, l = 0.f;
   for (int t = t0; t < t1; ++t) {
     const int kt = tiles[t] >> 2;
@@ -799,7 +850,8 @@ int launch_segment_attention(const AttnArgs& a, void* stream) {
   hipLaunchKernelGGL(seg_attn_bf16<G>, dim3((unsigned)blocks), dim3(64 * G), 0, s,                  \
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,              \
                      (const uint16_t*)a.k_ver, (const uint16_t*)a.v_ver, a.item_desc, a.tiles,      \
-                     a.order, a.tok_drop, a.ver_src, (uint16_t*)a.out, a.lse, a.hq, a.hkv, a.scale)
+                     a.order, a.tok_drop, a.ver_src, (uint16_t*)a.out, a.lse, a.hq, a.hkv, a.scale,    \
+                     a.tok_pos, a.rq)
     switch (grp) {
       case 1: AKV_LAUNCH_BF16(1); break;
       case 2: AKV_LAUNCH_BF16(2); break;
@@ -808,7 +860,7 @@ int launch_segment_attention(const AttnArgs& a, void* stream) {
         hipLaunchKernelGGL(seg_attn_bf16_pp, dim3((unsigned)blocks), dim3(512), 0, s, (const uint16_t*)a.q,
                            (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.k_ver,
                            (const uint16_t*)a.v_ver, a.item_desc, a.tiles, a.order, a.tok_drop, a.ver_src,
-                           (uint16_t*)a.out, a.lse, a.hq, a.hkv, a.scale);
+                           (uint16_t*)a.out, a.lse, a.hq, a.hkv, a.scale, a.tok_pos, a.rq);
         break;
     }
 #undef AKV_LAUNCH_BF16
@@ -820,7 +872,8 @@ int launch_segment_attention(const AttnArgs& a, void* stream) {
   hipLaunchKernelGGL(seg_attn_f32<DD>, dim3((unsigned)blocks), dim3(threads), 0, s,                 \
                      (const float*)a.q, (const float*)a.k, (const float*)a.v,                       \
                      (const float*)a.k_ver, (const float*)a.v_ver, a.item_desc, a.tiles, a.order,   \
-                     a.tok_drop, a.ver_src, (float*)a.out, a.lse, a.hq, a.hkv, a.bk, a.scale)
+                     a.tok_drop, a.ver_src, (float*)a.out, a.lse, a.hq, a.hkv, a.bk, a.scale,       \
+                     a.tok_pos, a.rq)
     switch (a.d) {
       case 32: AKV_LAUNCH_F32(32); break;
       case 64: AKV_LAUNCH_F32(64); break;

@@ -70,15 +70,24 @@ struct RopeArgs {
 };
 int launch_rope(const RopeArgs& a, void* stream);
 
+// Query rotation inside the attention (queries given raw, rotated to their append
+// positions on load); off when the queries arrive rotated.
+struct RopeQ {
+  double rev[64];  // theta_i / (2 pi) for i < d / 2 (d <= 128)
+  int on;
+  int layout;      // AKV_ROPE_HALF or AKV_ROPE_INTERLEAVED
+};
+
 struct AttnArgs {
   const void *q, *k, *v, *k_ver, *v_ver;
   void* out;
   float* lse;
-  const int32_t *item_desc, *tiles, *order, *tok_drop, *ver_src;
+  const int32_t *item_desc, *tiles, *order, *tok_drop, *ver_src, *tok_pos;
   int64_t n_items;
   int32_t hq, hkv, d, bq, bk;
   float scale;
   int dtype;
+  RopeQ rq;
 };
 int launch_segment_attention(const AttnArgs& a, void* stream);
 

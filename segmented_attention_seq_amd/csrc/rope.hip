@@ -15,23 +15,17 @@
 #include <cmath>
 
 #include "internal.h"
+#include "rope_angle.h"
 
 namespace akv {
 namespace {
 
-// Frequencies are stored in revolutions per position, theta_i / (2 pi), in fp64.
-// The angle of a shift delta is reduced to its fractional revolution in fp64:
-// |delta| < 2^31 and theta_i / (2 pi) < 0.16 keep the product below 2^29, where the
-// fp64 spacing is 2^-23 revolutions or less (2^-35 for shifts up to 2^20), and the
-// fraction is rounded once to fp32.  The hardware sine and cosine take their
-// argument in revolutions; on [-0.5, 0.5] they are within 1.3e-7 of the exact value.
+// Frequencies are stored in revolutions per position, theta_i / (2 pi), in fp64; the
+// angle evaluation is shared with the attention's query load (rope_angle.h).
 struct Freqs { double rev[128]; };
 
 __device__ __forceinline__ void angle_cs(long long delta, double rev, float& c, float& s) {
-  const double x = (double)delta * rev;
-  const float r = (float)(x - rint(x));
-  s = __builtin_amdgcn_sinf(r);
-  c = __builtin_amdgcn_cosf(r);
+  rope_angle_cs((double)delta, rev, c, s);
 }
 
 __device__ __forceinline__ float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }

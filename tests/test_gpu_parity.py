@@ -233,6 +233,33 @@ def _check_rows(tr, qkv, out, lse, bf16, rows=None, layout=akv.ROPE_HALF, tol=No
     assert lerr <= (2e-2 if bf16 else 1e-5)
 
 
+# The restore path rotates the raw queries inside the attention (akv.restore default);
+# the separate RoPE-apply of Q into a rotated copy is the other form.  Both must meet
+# the oracle, and the fused form rounds Q to bf16 once instead of twice, so its error
+# is no larger (a small margin covers summation-order noise).
+@pytest.mark.parametrize("bf16,hq,hkv,layout", [(True, 64, 8, akv.ROPE_HALF), (True, 16, 4, akv.ROPE_INTERLEAVED),
+                                                (False, 4, 2, akv.ROPE_HALF), (False, 6, 2, akv.ROPE_INTERLEAVED)])
+def test_query_rotation_inside_attention(bf16, hq, hkv, layout):
+    tr = workload.agent_trajectory(4, seed=61, total=1400, keep=2, repos="every", user_len=40,
+                                   assist_range=(20, 120), tool_range=(80, 300))
+    plan = akv.build_visibility(akv.ops_from_messages(tr.msg_len, tr.drop, tr.reposition))
+    q, k, v = workload.prefill_tensors(tr.n_tokens, hq, hkv, 64, seed=62, bf16=bf16)
+    ops = oracle.canonical_ops(tr.msg_len, tr.drop, tr.reposition)
+    view = (lambda a: Bf16Rows(a)) if bf16 else (lambda a: a)
+    o_ref, l_ref = oracle.segment_attention(view(q), view(k), view(v), ops, base=BASE, layout=layout)
+    errs = {}
+    for fuse in (True, False):
+        out, lse = akv.restore(plan, dev_tensor(q, bf16), dev_tensor(k, bf16), dev_tensor(v, bf16), BASE, layout,
+                               with_lse=True, fuse_q=fuse)
+        torch.cuda.synchronize()
+        errs[fuse] = (np.abs(host_f64(out) - o_ref).max(), np.abs(host_f64(lse) - l_ref).max())
+    print(f"[q rotation in attention bf16={bf16} layout={layout}] fused {errs[True]} separate {errs[False]}")
+    tol = 2e-2 if bf16 else 1e-5
+    for e, le in errs.values():
+        assert e <= tol and le <= tol
+    assert errs[True][0] <= errs[False][0] * 1.25 + (1e-4 if bf16 else 1e-7)
+
+
 def test_tiny_request_example_fp32():
     tr = workload.config_trajectory(1)
     plan, qkv, out, lse = _run_restore(tr, 1, 1, 64, bf16=False, seed=1)
