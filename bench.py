@@ -54,46 +54,6 @@ def parse_args():
     return ap.parse_args()
 
 
-class KernelTimer:
-    """Kernel-exact durations: a pair of HIP events handed to the library's next call
-    (akv_time_next_call), which records them at its first kernel's start and its last
-    kernel's end.  The events come from the HIP runtime torch has loaded."""
-
-    def __init__(self, akv):
-        import ctypes
-        self._akv = akv
-        self._c = ctypes
-        self._hip = ctypes.CDLL("libamdhip64.so.7")   # resolves to the copy already loaded
-        self._hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
-        self._hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
-                                                  ctypes.c_void_p]
-        self._hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
-        self._events = []
-
-    def _create(self):
-        ev = self._c.c_void_p()
-        if self._hip.hipEventCreate(self._c.byref(ev)) != 0:
-            raise RuntimeError("hipEventCreate failed")
-        self._events.append(ev)
-        return ev
-
-    def arm(self):
-        pair = (self._create(), self._create())
-        self._akv.time_next_call(pair[0].value, pair[1].value)
-        return pair
-
-    def elapsed_ms(self, pair):
-        ms = self._c.c_float()
-        if self._hip.hipEventElapsedTime(self._c.byref(ms), pair[0], pair[1]) != 0:
-            raise RuntimeError("hipEventElapsedTime failed")
-        return ms.value
-
-    def close(self):
-        for ev in self._events:
-            self._hip.hipEventDestroy(ev)
-        self._events = []
-
-
 def attn_src_hash():
     with open(ATTN_SRC, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
@@ -229,11 +189,15 @@ def main():
     host_ms = []
     keep_plans = []
 
-    timer = KernelTimer(akv)
+    def mark():
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()
+        return e
 
     def step(i, timed):
         t0 = time.perf_counter()
         ev = {}
+        last = None
         if "restore" in only:
             plan = akv.build_visibility(akv.ops_from_messages(*req_ops))
             buf = dev_plans[i % 2]
@@ -246,23 +210,31 @@ def main():
             keep_plans.append(plan)
             del keep_plans[:-3]      # host images stay alive until their copies ran
             host_ms.append((time.perf_counter() - t0) * 1e3)
-            # kernel-exact stage times: the library records the pair at its kernels'
-            # dispatches (akv_time_next_call), no marker packets in the step
-            ev["rope"] = timer.arm()
+            # One event between consecutive stages (each record is a marker packet
+            # of a few microseconds on the GPU timeline): stage k runs from mark k to
+            # mark k+1.
+            m0 = mark()
             akv.rope_apply(plan, bufs["k_rot"], kd)   # queries are rotated inside the attention
+            m1 = mark()
+            m2 = m1
             if nv:
-                ev["versions"] = timer.arm()
                 akv.build_kv_versions(plan, bufs["k_rot"], vd, bufs["k_ver"], bufs["v_ver"])
-            ev["attn"] = timer.arm()
+                m2 = mark()
             akv.segment_attention(plan, qd, bufs["k_rot"], vd, bufs["k_ver"], bufs["v_ver"], bufs["out"],
                                   rope_base=workload.ROPE_BASE)
+            last = mark()
+            ev.update(rope=(m0, m1), versions=(m1, m2), attn=(m2, last))
         if "repos" in only:
             pool, out = repos_sets[i % len(repos_sets)]
-            ev["repos"] = timer.arm()
+            start = last if last is not None else mark()
             akv.rope_repos(out, pool, r_to, r_from, r_idx)
+            last = mark()
+            ev["repos"] = (start, last)
         if "decode" in only:
-            ev["decode"] = timer.arm()
+            start = last if last is not None else mark()
             akv.decode_attention(dq, pool_k, pool_v, d_indptr, d_indices, max_n, dout, ws=dws)
+            last = mark()
+            ev["decode"] = (start, last)
         return ev
 
     for i in range(args.warmup):
@@ -275,9 +247,8 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     for evs in pending:
-        for n, pair in evs.items():
-            stage_ms[n].append(timer.elapsed_ms(pair))
-    timer.close()
+        for n, (a, b) in evs.items():
+            stage_ms[n].append(a.elapsed_time(b))
     ms_per_step = wall * 1e3 / args.steps
     avg = {n: (float(np.mean(v)) if v else None) for n, v in stage_ms.items()}
 

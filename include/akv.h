@@ -76,18 +76,6 @@ typedef struct akv_plan akv_plan;   /* opaque, host-owned, immutable once built 
 typedef void* akv_stream_t;         /* a hipStream_t (NULL = the null stream) */
 
 const char* akv_status_string(int status);
-
-/* Kernel-exact timing of the next call on this thread that launches kernels
- * (akv_rope_repos, akv_kv_reuse, akv_rope_apply, akv_build_kv_versions,
- * akv_segment_attention[_rope], akv_decode_attention): start_event (a hipEvent_t
- * created by the caller) takes the time its first kernel starts and stop_event the
- * time its last kernel ends.  The events travel with the kernel dispatches, so the
- * interval holds no launch gaps or marker packets; read it with
- * hipEventElapsedTime after the stream has passed the call.  The pair is spent by
- * that next call, also when it fails or launches nothing (then the events are not
- * recorded).  Both NULL cancels; one NULL is AKV_EINVAL.  Not a reading of the
- * pages: a measuring aid. */
-int akv_time_next_call(void* start_event, void* stop_event);
 const char* akv_last_error(void);
 const char* akv_version(void);
 

@@ -81,7 +81,6 @@ _vp, _i32, _i64, _u64, _f32, _f64 = C.c_void_p, C.c_int32, C.c_int64, C.c_uint64
 _sig("akv_status_string", C.c_char_p, C.c_int)
 _sig("akv_last_error", C.c_char_p)
 _sig("akv_version", C.c_char_p)
-_sig("akv_time_next_call", C.c_int, _vp, _vp)
 _sig("akv_ops_from_messages", C.c_int, _i32, _vp, _i32, _vp, _vp, _i32, _vp, C.POINTER(akv_op), _i64,
      C.POINTER(_i64))
 _sig("akv_build_visibility", C.c_int, C.POINTER(akv_op), _i64, _i32, _i32, C.POINTER(_vp))
@@ -108,7 +107,7 @@ _sig("akv_cache_insert", C.c_int, _vp, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _i64
 _sig("akv_cache_unlock", C.c_int, _vp, _vp, _i64)
 _sig("akv_cache_stats_get", C.c_int, _vp, C.POINTER(akv_cache_stats))
 
-EXPORTED = ["akv_status_string", "akv_last_error", "akv_version", "akv_time_next_call", "akv_ops_from_messages",
+EXPORTED = ["akv_status_string", "akv_last_error", "akv_version", "akv_ops_from_messages",
             "akv_build_visibility", "akv_plan_info_get", "akv_plan_tables_get", "akv_plan_upload",
             "akv_plan_destroy", "akv_rope_repos", "akv_kv_reuse", "akv_rope_apply", "akv_build_kv_versions",
             "akv_segment_attention", "akv_segment_attention_rope", "akv_decode_workspace_bytes", "akv_decode_attention",
@@ -123,11 +122,6 @@ def _check(status: int, where: str):
 
 def version() -> str:
     return _lib.akv_version().decode()
-
-
-def time_next_call(start_event, stop_event):
-    """akv_time_next_call: raw hipEvent_t handles (ints) or None, None."""
-    _check(_lib.akv_time_next_call(start_event, stop_event), "akv_time_next_call")
 
 
 def lib_path() -> str:

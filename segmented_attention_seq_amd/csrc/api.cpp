@@ -26,27 +26,7 @@ int fail(int status, const std::string& msg) {
 
 using akv::fail;
 
-namespace akv {
-namespace {
-thread_local LaunchEvents t_pending, t_active;
-}  // namespace
-void set_pending_events(void* start, void* stop) { t_pending = LaunchEvents{start, stop}; }
-const LaunchEvents& active_events() { return t_active; }
-EventScope::EventScope() {
-  t_active = t_pending;
-  t_pending = LaunchEvents{};
-}
-EventScope::~EventScope() { t_active = LaunchEvents{}; }
-}  // namespace akv
-
 extern "C" {
-
-int akv_time_next_call(void* start_event, void* stop_event) {
-  if ((start_event == nullptr) != (stop_event == nullptr))
-    return fail(AKV_EINVAL, "akv_time_next_call: give both events or neither");
-  akv::set_pending_events(start_event, stop_event);
-  return AKV_OK;
-}
 
 const char* akv_status_string(int status) {
   switch (status) {
@@ -177,7 +157,6 @@ static int check_rope(int dtype, int32_t heads, int32_t d, int layout, double ba
 int akv_rope_repos(void* out, const void* in, int dtype, int64_t n_rows, int32_t heads, int32_t d,
                    const int32_t* gather, const int32_t* pos_from, const int32_t* pos_to,
                    double rope_base, int rope_layout, akv_stream_t stream) {
-  akv::EventScope timing;  // spends the events of akv_time_next_call
   int st = check_rope(dtype, heads, d, rope_layout, rope_base);
   if (st) return st;
   if (n_rows < 0) return fail(AKV_EINVAL, "n_rows < 0");
@@ -192,7 +171,6 @@ int akv_rope_repos(void* out, const void* in, int dtype, int64_t n_rows, int32_t
 int akv_kv_reuse(void* k_out, void* v_out, const void* k_pool, const void* v_pool, int dtype, int64_t n_rows,
                  int32_t heads, int32_t d, const int32_t* gather, const int32_t* pos_from,
                  const int32_t* pos_to, double rope_base, int rope_layout, akv_stream_t stream) {
-  akv::EventScope timing;  // spends the events of akv_time_next_call
   int st = check_rope(dtype, heads, d, rope_layout, rope_base);
   if (st) return st;
   if (n_rows < 0) return fail(AKV_EINVAL, "n_rows < 0");
@@ -207,7 +185,6 @@ int akv_kv_reuse(void* k_out, void* v_out, const void* k_pool, const void* v_poo
 
 int akv_rope_apply(const akv_plan* p, const void* dev_plan, void* out, const void* in, int dtype,
                    int32_t heads, int32_t d, double rope_base, int rope_layout, akv_stream_t stream) {
-  akv::EventScope timing;  // spends the events of akv_time_next_call
   if (!p || !dev_plan) return fail(AKV_EINVAL, "NULL plan or device plan");
   int st = check_rope(dtype, heads, d, rope_layout, rope_base);
   if (st) return st;
@@ -222,7 +199,6 @@ int akv_rope_apply(const akv_plan* p, const void* dev_plan, void* out, const voi
 int akv_build_kv_versions(const akv_plan* p, const void* dev_plan, const void* k, const void* v,
                           void* k_ver, void* v_ver, int dtype, int32_t hkv, int32_t d,
                           double rope_base, int rope_layout, akv_stream_t stream) {
-  akv::EventScope timing;  // spends the events of akv_time_next_call
   if (!p || !dev_plan) return fail(AKV_EINVAL, "NULL plan or device plan");
   int st = check_rope(dtype, hkv, d, rope_layout, rope_base);
   if (st) return st;
@@ -241,7 +217,6 @@ namespace {
 int segment_attention(const akv_plan* p, const void* dev_plan, const void* q, const void* k, const void* v,
                       const void* k_ver, const void* v_ver, void* out, float* lse, int dtype, int32_t hq,
                       int32_t hkv, int32_t d, float scale, const akv::RopeQ& rq, akv_stream_t stream) {
-  akv::EventScope timing;  // spends the events of akv_time_next_call
   if (!p || !dev_plan) return fail(AKV_EINVAL, "NULL plan or device plan");
   if (dtype != AKV_F32 && dtype != AKV_BF16) return fail(AKV_EINVAL, "dtype must be AKV_F32 or AKV_BF16");
   if (hq < 1 || hkv < 1 || hq % hkv) return fail(AKV_EINVAL, "hq must be a positive multiple of hkv");
@@ -305,7 +280,6 @@ int akv_decode_attention(const void* q, const void* k_pool, const void* v_pool, 
                          const int32_t* indices, int32_t batch, int32_t hq, int32_t hkv, int32_t d,
                          int64_t max_n, float scale, int dtype, void* out, float* lse, void* ws,
                          uint64_t ws_bytes, akv_stream_t stream) {
-  akv::EventScope timing;  // spends the events of akv_time_next_call
   if (dtype != AKV_BF16) return fail(AKV_EUNSUPPORTED, "decode attention is bf16 only");
   if (d != 64) return fail(AKV_EUNSUPPORTED, "decode attention needs d == 64");
   if (hq < 1 || hkv < 1 || hq % hkv || hq / hkv > 16)

@@ -37,7 +37,6 @@
 
 #include "internal.h"
 #include "rope_angle.h"
-#include "launch.h"
 
 namespace akv {
 namespace {
@@ -848,7 +847,7 @@ int launch_segment_attention(const AttnArgs& a, void* stream) {
     if (blocks > 0x7fffffffLL) return fail(AKV_EINVAL, "too many work items");
     const int grp = a.hq / a.hkv;
 #define AKV_LAUNCH_BF16(G)                                                                           \
-  launch_timed(seg_attn_bf16<G>, dim3((unsigned)blocks), dim3(64 * G), s, true, true,                \
+  hipLaunchKernelGGL(seg_attn_bf16<G>, dim3((unsigned)blocks), dim3(64 * G), 0, s,                  \
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,              \
                      (const uint16_t*)a.k_ver, (const uint16_t*)a.v_ver, a.item_desc, a.tiles,      \
                      a.order, a.tok_drop, a.ver_src, (uint16_t*)a.out, a.lse, a.hq, a.hkv, a.scale,    \
@@ -858,7 +857,7 @@ int launch_segment_attention(const AttnArgs& a, void* stream) {
       case 2: AKV_LAUNCH_BF16(2); break;
       case 4: AKV_LAUNCH_BF16(4); break;
       default:
-        launch_timed(seg_attn_bf16_pp, dim3((unsigned)blocks), dim3(512), s, true, true, (const uint16_t*)a.q,
+        hipLaunchKernelGGL(seg_attn_bf16_pp, dim3((unsigned)blocks), dim3(512), 0, s, (const uint16_t*)a.q,
                            (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.k_ver,
                            (const uint16_t*)a.v_ver, a.item_desc, a.tiles, a.order, a.tok_drop, a.ver_src,
                            (uint16_t*)a.out, a.lse, a.hq, a.hkv, a.scale, a.tok_pos, a.rq);
@@ -870,7 +869,7 @@ int launch_segment_attention(const AttnArgs& a, void* stream) {
     if (blocks > 0x7fffffffLL) return fail(AKV_EINVAL, "too many work items");
     const int threads = ((a.bq + 63) / 64) * 64;
 #define AKV_LAUNCH_F32(DD)                                                                           \
-  launch_timed(seg_attn_f32<DD>, dim3((unsigned)blocks), dim3(threads), s, true, true,               \
+  hipLaunchKernelGGL(seg_attn_f32<DD>, dim3((unsigned)blocks), dim3(threads), 0, s,                 \
                      (const float*)a.q, (const float*)a.k, (const float*)a.v,                       \
                      (const float*)a.k_ver, (const float*)a.v_ver, a.item_desc, a.tiles, a.order,   \
                      a.tok_drop, a.ver_src, (float*)a.out, a.lse, a.hq, a.hkv, a.bk, a.scale,       \

@@ -27,7 +27,6 @@
 #include <cmath>
 
 #include "internal.h"
-#include "launch.h"
 
 namespace akv {
 namespace {
@@ -315,10 +314,10 @@ int launch_decode(const DecodeArgs& a, void* stream) {
   (void)hipGetLastError();
   const float sl2 = a.scale * kLog2e;
   const int waves = a.hkv < HG ? a.hkv : HG;
-  launch_timed(decode_split, dim3(kDecodeWGs, (a.hkv + HG - 1) / HG), dim3(64 * waves), s, true, false,
+  hipLaunchKernelGGL(decode_split, dim3(kDecodeWGs, (a.hkv + HG - 1) / HG), dim3(64 * waves), 0, s,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.indptr, a.indices,
                      a.batch, a.hq, a.hkv, sl2, a.ws);
-  launch_timed(decode_merge, dim3(a.batch * a.hq), dim3(64), s, false, true, (const float*)a.ws, a.indptr,
+  hipLaunchKernelGGL(decode_merge, dim3(a.batch * a.hq), dim3(64), 0, s, (const float*)a.ws, a.indptr,
                      (uint16_t*)a.out, a.lse, a.batch, a.hq, a.hkv, kDecodeWGs, a.scale, sl2);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(AKV_EHIP, std::string("decode launch: ") + hipGetErrorString(e));

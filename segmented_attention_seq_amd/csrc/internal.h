@@ -48,23 +48,6 @@ namespace akv {
 enum { ID_QBEGIN = 0, ID_QEND, ID_TB, ID_TE, ID_R, ID_VEROFF, ID_TILE0, ID_TILE1, ID_WORDS };
 
 void set_error(const std::string& msg);
-
-// Timing events of akv_time_next_call (hipEvent_t handles, or null).  Every entry
-// point that launches kernels holds an EventScope: it takes the pending pair, its
-// launchers read active_events(), and the pair is spent when the scope ends, whether
-// or not anything was launched.
-struct LaunchEvents {
-  void* start = nullptr;
-  void* stop = nullptr;
-};
-void set_pending_events(void* start, void* stop);
-const LaunchEvents& active_events();
-struct EventScope {
-  EventScope();
-  ~EventScope();
-  EventScope(const EventScope&) = delete;
-  EventScope& operator=(const EventScope&) = delete;
-};
 int fail(int status, const std::string& msg);
 
 int build_plan(const akv_op* ops, int64_t n_ops, int32_t bq, int32_t bk, akv_plan** out);

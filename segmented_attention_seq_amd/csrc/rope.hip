@@ -16,7 +16,6 @@
 
 #include "internal.h"
 #include "rope_angle.h"
-#include "launch.h"
 
 namespace akv {
 namespace {
@@ -264,7 +263,7 @@ void launch_row_ix(const RopeArgs& a, const Freqs& fr, hipStream_t s) {
   const int n_hg = (a.heads + HG - 1) / HG;
   const long long threads = a.n_rows * n_hg * (long long)(HG * 2 * CPR);
   const unsigned blocks = (unsigned)((threads + 255) / 256);
-  launch_timed(rope_row_kernel<T, LAYOUT, CPR, IX>, dim3(blocks), dim3(256), s, true, true, (T*)a.out,
+  hipLaunchKernelGGL((rope_row_kernel<T, LAYOUT, CPR, IX>), dim3(blocks), dim3(256), 0, s, (T*)a.out,
                      (const T*)a.in, (T*)a.v_out, (const T*)a.v_in, (long long)a.n_rows, a.heads, n_hg,
                      a.gather, a.pos_from, a.pos_from_by_src ? 1 : 0, a.pos_to, fr);
 }
@@ -288,7 +287,7 @@ void launch_t(const RopeArgs& a, const Freqs& fr, hipStream_t s) {
   }
   const long long threads = a.n_rows * (a.d / 16);
   const unsigned blocks = (unsigned)((threads + 255) / 256);
-  launch_timed(rope_kernel<T, LAYOUT>, dim3(blocks), dim3(256), s, true, true, (T*)a.out, (const T*)a.in,
+  hipLaunchKernelGGL((rope_kernel<T, LAYOUT>), dim3(blocks), dim3(256), 0, s, (T*)a.out, (const T*)a.in,
                      (T*)a.v_out, (const T*)a.v_in, (long long)a.n_rows, a.heads, a.d, a.gather,
                      a.pos_from, a.pos_from_by_src ? 1 : 0, a.pos_to, fr);
 }

@@ -93,41 +93,6 @@ def test_repos_fp32_head_dims_and_counts(d, H, layout):
     assert err <= 1e-5
 
 
-def test_time_next_call_brackets_the_kernel():
-    """akv_time_next_call: the event pair recorded at the kernel's dispatch spans the
-    kernel alone, so it is positive and no longer than an event pair recorded around
-    the same call (plus a little clock slack)."""
-    import ctypes
-    hip = ctypes.CDLL("libamdhip64.so.7")
-    hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
-    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
-    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
-    rb = workload.repos_batch(n_keys=20000)
-    pool = nan_like((rb.pool_slots, rb.hkv, rb.d), torch.bfloat16)
-    pool[torch.from_numpy(rb.slots.astype(np.int64)).cuda()] = dev_tensor(rb.k_rows, True)
-    out = nan_like((rb.slots.size, rb.hkv, rb.d), torch.bfloat16)
-    args = (dev_int(rb.pos_to), dev_int(rb.pos_from), dev_int(rb.slots))
-    ev = [ctypes.c_void_p() for _ in range(2)]
-    for e in ev:
-        assert hip.hipEventCreate(ctypes.byref(e)) == 0
-    try:
-        for rep in range(3):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            akv.time_next_call(ev[0].value, ev[1].value)
-            akv.rope_repos(out, pool, *args)
-            e1.record()
-            torch.cuda.synchronize()
-            ms = ctypes.c_float()
-            assert hip.hipEventElapsedTime(ctypes.byref(ms), ev[0], ev[1]) == 0
-            outer = e0.elapsed_time(e1)
-            print(f"[time_next_call] kernel {ms.value * 1e3:.1f} us, events around the call {outer * 1e3:.1f} us")
-            assert 0.0 < ms.value <= outer + 0.005
-    finally:
-        for e in ev:
-            hip.hipEventDestroy(e)
-
-
 def test_repos_bf16_one_ulp_and_rne():
     rng = np.random.default_rng(12)
     n, H, d = 4000, 8, 64
