@@ -176,9 +176,11 @@ class CacheIndex:
         _check(_lib.akv_cache_create(int(n_slots), C.byref(h)), "akv_cache_create")
         self._h = h
 
-    def __del__(self):
+    def __del__(self, _destroy=_lib.akv_cache_destroy):
+        # the library function is bound at definition time: module globals may
+        # already be cleared when this runs at interpreter exit
         if getattr(self, "_h", None):
-            _lib.akv_cache_destroy(self._h)
+            _destroy(self._h)
             self._h = None
 
     def match(self, tok, ops, lock: bool = False):
@@ -237,10 +239,11 @@ class Plan:
     def handle(self):
         return self._h
 
-    def __del__(self):
+    def __del__(self, _destroy=_lib.akv_plan_destroy):
+        # bound at definition time, as in CacheIndex.__del__
         h = getattr(self, "_h", None)
         if h is not None and h.value:
-            _lib.akv_plan_destroy(h)
+            _destroy(h)
             self._h = None
 
     def tables(self) -> Dict[str, np.ndarray]:

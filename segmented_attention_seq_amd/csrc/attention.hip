@@ -29,7 +29,17 @@
 //     work item and a redo through the rescaling softmax when it fails;
 //   * 1, 2 or 4 query heads per kv head (seg_attn_bf16<GROUP>): one wave per query
 //     head, double-buffered tiles, the rescaling softmax (lazily moved exponent
-//     offset, bf16 dot2 row sums, per-tile range check).
+//     offset, bf16 dot2 row sums, per-tile range check);
+//   * queries arrive either rotated or raw; raw ones are rotated to their append
+//     positions (tok_pos) in fp32 as they are loaded, before the scale and the one
+//     bf16 rounding (review §3.3: a vector at position p is the raw vector rotated
+//     pair by pair by p * theta_i);
+//   * the ping-pong kernel writes its output tile through the wave's LDS rows as
+//     whole 128-byte rows with streaming stores, so no dirty output lines are left
+//     in the last-level cache for the next kernel to write back.
+//
+// fp32 kernel (seg_attn_f32): one thread per (query token, head), keys one at a
+// time with an exact online softmax; for small problems and fp32 checks.
 #include <hip/hip_runtime.h>
 
 #include <climits>
@@ -394,14 +404,13 @@ __device__ __forceinline__ void tile_pv(WaveState& w, const uint16_t* lvb, int l
   mfma_pv(w, f);
 }
 
-// Q' = Q scaled by sl2 = scale * log2(e) (re-rounded to bf16), so that QK
-// products come out in log2 units; kept in registers, or (QL) in the wave's LDS
-// rows lqw (64 rows, K pitch).
-// Q of the wave's head for its 64 query rows, times scale * log2(e), in bf16: in LDS
-// (QL) or registers.  With rq.on the raw rows are first rotated to their append
-// positions tok_pos[tok] in fp32 (the lane holds both members of each of its pairs:
-// chunk ds pairs with ds + 2 in the half layout, neighbours within a chunk in the
-// interleaved one), so the query is rounded to bf16 once.
+// Q' = Q scaled by sl2 = scale * log2(e) and rounded to bf16, so that QK products
+// come out in log2 units: the wave's head, its 64 query rows, kept in registers or
+// (QL) in the wave's LDS rows lqw (64 rows, K pitch).  With rq.on the raw rows are
+// first rotated to their append positions tok_pos[tok] in fp32 (the lane holds both
+// members of each of its pairs: chunk ds pairs with ds + 2 in the half layout,
+// neighbours within a chunk in the interleaved one), so the query is rounded to
+// bf16 once.
 template <bool QL>
 __device__ __forceinline__ void load_q(WaveState& w, uint16_t* lqw, const uint16_t* q, int q0, int q1, int hq, int h,
                                        int lq, int lg, float sl2, const int* tok_pos, const RopeQ& rq) {
