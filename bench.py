@@ -31,7 +31,8 @@ sys.path.insert(0, ROOT)
 METRIC = "segment-attn restore TFLOP/s (% MFMA peak); repos+decode HBM GB/s (% peak)"
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
-ATTN_SRC = os.path.join(ROOT, "segmented_attention_seq_amd", "csrc", "attention.hip")
+ATTN_SRCS = [os.path.join(ROOT, "segmented_attention_seq_amd", "csrc", f)
+             for f in ("attention.hip", "internal.h", "rope_angle.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "segment_attention_48k_traffic.md")
 
 
@@ -55,8 +56,16 @@ def parse_args():
 
 
 def attn_src_hash():
-    with open(ATTN_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the attention kernel's code: its source and the two local headers it
+    includes, with comments removed and whitespace collapsed, so an edit of the
+    comments alone keeps the counters that were taken on the same code."""
+    h = hashlib.sha256()
+    for path in ATTN_SRCS:
+        with open(path) as f:
+            code = re.sub(r"/\*.*?\*/", " ", f.read(), flags=re.S)
+        code = re.sub(r"//[^\n]*", " ", code)
+        h.update(" ".join(code.split()).encode() + b"\0")
+    return h.hexdigest()[:16]
 
 
 def read_traffic(cfg):
@@ -65,7 +74,7 @@ def read_traffic(cfg):
     if cfg != 2 or not os.path.exists(TRAFFIC_FILE):
         return None
     txt = open(TRAFFIC_FILE).read()
-    h = re.search(r"kernel source sha256\[:16\]:\s*([0-9a-f]{16})", txt)
+    h = re.search(r"kernel code sha256\[:16\]:\s*([0-9a-f]{16})", txt)
     b = re.search(r"HBM bytes per launch \(scaled\):\s*([0-9.e+]+)", txt)
     if not h or not b or h.group(1) != attn_src_hash():
         return None
