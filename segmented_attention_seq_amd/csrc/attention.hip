@@ -672,6 +672,8 @@ __device__ __forceinline__ void pp_pipeline(WaveState& w, f32x4 (&ls)[2], bf16x8
   __syncthreads();
   if (lag) lds_barrier();
   tile_qk<true>(w, lk[0], lqw, lq, lg);
+  VFrag vf;
+  read_vt(vf, lv[0], lane);
   lds_barrier();
   int slot = 0;  // slot of tile i
   // tile entries i, i+1, i+2 in hand; entry i+3 is requested one iteration ahead
@@ -684,26 +686,29 @@ __device__ __forceinline__ void pp_pipeline(WaveState& w, f32x4 (&ls)[2], bf16x8
     const int slot1 = slot == NSLOT - 1 ? 0 : slot + 1;
     const int slot2 = slot1 == NSLOT - 1 ? 0 : slot1 + 1;
     if (fetch2) st.fetch(tile_src(e2, nvt, voff, r, tb, te, k, v, kver, vver), p2, hkv, hk, tok_drop, ver_src);
-    // phase 1 (VALU): softmax of tile i.  The V^T fragments for its PV product are
-    // read first, so their LDS latency hides behind the softmax.
-    VFrag vf;
-    read_vt(vf, lv[slot], lane);
+    // phase 1 (VALU): softmax of tile i.  Its V^T fragments were read at the end of
+    // the previous MFMA phase: LDS reads issued here would hold up the exp stream
+    // while the partner wave's K and Q' reads occupy the LDS.
     __builtin_amdgcn_sched_barrier(0);
     if (SAFE)
       tile_softmax<true>(w, (ent & 3) == AKV_TILE_PARTIAL, mtok[slot], mdrop[slot], lk[slot], lqw, q0, lq, lg);
     else
       tile_softmax_fast(w, (ent & 3) == AKV_TILE_PARTIAL, mtok[slot], mdrop[slot], q0, lq, lg);
     lds_barrier();
-    // phase 2 (MFMA): PV of tile i, QK of tile i+1 (its K fragments are read before
-    // the PV MFMAs, which hide their latency); then tile i+2 goes to the slot freed
-    // by tile i-1 (its last reader finished before the barrier above)
+    // phase 2 (MFMA): PV of tile i, QK of tile i+1 (its K fragments are read between
+    // the PV MFMAs, which hide their latency), the V^T fragments of tile i+1 (both
+    // halves of it were stashed before the barrier above); then tile i+2 goes to the
+    // slot freed by tile i-1 (its last reader finished before the barrier above)
     __builtin_amdgcn_s_setprio(1);
     // (after the last tile, slot1 holds an older tile: its K reads are harmless and unused)
     KFrag kf;
     bf16x8 q0f[2];
     mfma_pv_read_k<!SAFE>(w, vf, kf, q0f, ls, sel, lk[slot1], lqw, lq, lg);
     // P of tile i is dead here, before the scores of tile i+1 are born: they share registers
-    if (i + 1 < n) mfma_qk_lq(w, kf, q0f, lqw, lq, lg);
+    if (i + 1 < n) {
+      mfma_qk_lq(w, kf, q0f, lqw, lq, lg);
+      read_vt(vf, lv[slot1], lane);
+    }
     __builtin_amdgcn_s_setprio(0);
     if (fetch2) st.stash(lk[slot2], lv[slot2], mtok[slot2], mdrop[slot2], p2);
     lds_barrier();
