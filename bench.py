@@ -125,6 +125,11 @@ def cpu_baseline(tr, q, k, v, target_s):
                       f"NumPy oracle, {secs:.1f} s"}
 
 
+def _back_to_back(ms, nbytes):
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"b2b_us": ms * 1e3, "b2b_achieved": gbs, "b2b_frac": gbs / PEAK_HBM_GBS}
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
@@ -261,6 +266,29 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     avg = {n: (float(np.mean(v)) if v else None) for n, v in stage_ms.items()}
 
+    # The short kernels once more, back to back between one pair of events, so the
+    # marker packets of the per-stage events (a few microseconds each) do not count
+    # against them: repos over the rotating buffer sets (together larger than the
+    # last-level cache), decode over its 1.9 GB of gathered rows.
+    b2b = {}
+    if "repos" in only:
+        n_b2b = 4 * len(repos_sets)
+        e0 = mark()
+        for j in range(n_b2b):
+            pool, out = repos_sets[j % len(repos_sets)]
+            akv.rope_repos(out, pool, r_to, r_from, r_idx)
+        e1 = mark()
+        torch.cuda.synchronize()
+        b2b["repos"] = e0.elapsed_time(e1) / n_b2b
+    if "decode" in only:
+        n_b2b = 8
+        e0 = mark()
+        for _ in range(n_b2b):
+            akv.decode_attention(dq, pool_k, pool_v, d_indptr, d_indices, max_n, dout, ws=dws)
+        e1 = mark()
+        torch.cuda.synchronize()
+        b2b["decode"] = e0.elapsed_time(e1) / n_b2b
+
     value = attn_flop / (ms_per_step * 1e-3) / 1e12 if "restore" in only else 0.0
     attn_tflops = attn_flop / (avg["attn"] * 1e-3) / 1e12 if avg["attn"] else None
     traffic = read_traffic(args.config)
@@ -271,11 +299,13 @@ def main():
         gbs = repos_bytes / (avg["repos"] * 1e-3) / 1e9
         comps["repos"] = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                           "frac": gbs / PEAK_HBM_GBS, "bytes_per_launch": repos_bytes, "keys": nrep}
+        comps["repos"].update(_back_to_back(b2b["repos"], repos_bytes))
     if avg["decode"]:
         gbs = decode_bytes / (avg["decode"] * 1e-3) / 1e9
         comps["decode"] = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                            "frac": gbs / PEAK_HBM_GBS, "bytes_per_launch": decode_bytes,
                            "gathered_keys": n_keys, "requests": int(db.q.shape[0])}
+        comps["decode"].update(_back_to_back(b2b["decode"], decode_bytes))
     if avg["rope"]:
         rope_bytes = 2 * kd.numel() * 2 + 4 * T
         comps["rope_apply_gbs"] = rope_bytes / (avg["rope"] * 1e-3) / 1e9

@@ -79,3 +79,22 @@ def test_binding_and_torch_share_one_hip_runtime():
     assert r.returncode == 0, r.stderr
     assert r.stdout.split()[0] == "1", r.stdout
 
+
+
+def test_traffic_key_ignores_comments_only(tmp_path, monkeypatch):
+    """bench.py reports the attention's HBM traffic only for the kernel code the
+    counters were taken on: a comment edit keeps the key, a code edit changes it."""
+    sys.path.insert(0, str(ROOT))
+    import bench
+    src = ["// header\n__global__ void k(int* p) { /* store */ p[0] = 1; }\n", "#define X 2 // two\n"]
+    paths = []
+    for i, text in enumerate(src):
+        p = tmp_path / f"f{i}.h"
+        p.write_text(text)
+        paths.append(str(p))
+    monkeypatch.setattr(bench, "ATTN_SRCS", paths)
+    h0 = bench.attn_src_hash()
+    (tmp_path / "f0.h").write_text("// other words\n__global__ void k(int* p) {\n  p[0] = 1;  // one\n}\n")
+    assert bench.attn_src_hash() == h0
+    (tmp_path / "f1.h").write_text("#define X 3 // two\n")
+    assert bench.attn_src_hash() != h0
