@@ -85,12 +85,19 @@ template <typename T> struct Raw8;
 template <> struct Raw8<uint16_t> {
   rs_u32x4 u;
   __device__ __forceinline__ void load(const uint16_t* p) { u = *(const rs_u32x4*)p; }
+  __device__ __forceinline__ void get(float f[8]) const {
+    f[0] = bf_lo(u.x); f[1] = bf_hi(u.x); f[2] = bf_lo(u.y); f[3] = bf_hi(u.y);
+    f[4] = bf_lo(u.z); f[5] = bf_hi(u.z); f[6] = bf_lo(u.w); f[7] = bf_hi(u.w);
+  }
   __device__ __forceinline__ void store(uint16_t* p) const { *(rs_u32x4*)p = u; }
   __device__ __forceinline__ void store_nt(uint16_t* p) const { __builtin_nontemporal_store(u, (rs_u32x4*)p); }
 };
 template <> struct Raw8<float> {
   rs_f32x4 a, b;
   __device__ __forceinline__ void load(const float* p) { a = *(const rs_f32x4*)p; b = *(const rs_f32x4*)(p + 4); }
+  __device__ __forceinline__ void get(float f[8]) const {
+    f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w; f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+  }
   __device__ __forceinline__ void store(float* p) const { *(rs_f32x4*)p = a; *(rs_f32x4*)(p + 4) = b; }
   __device__ __forceinline__ void store_nt(float* p) const {
     __builtin_nontemporal_store(a, (rs_f32x4*)p);
@@ -167,8 +174,14 @@ enum { IX_APPLY = 0, IX_GATHER_ROW = 1, IX_GATHER_SRC = 2, IX_ANY = 3 };
 // own chunk c of the first and of the second half both load the chunk's two input
 // pieces (the second load is a cache hit) and each writes its own half.  In the
 // interleaved layout a chunk holds four whole pairs.  Each thread evaluates one
-// angle, pair (lane in group) mod d/2, and fetches the ones it needs by shuffle.
-template <typename T, int LAYOUT, int CPR, int IX>
+// angle per row, pair (lane in group) mod d/2, and fetches the ones it needs by
+// shuffle.
+//
+// A group handles RPW consecutive rows: the index loads of all of them are issued
+// together, then all their data loads, so a wave keeps RPW rows of reads in flight
+// instead of paying an index-then-data round trip per row.  Rows past the end
+// repeat the last row and store nothing.
+template <typename T, int LAYOUT, int CPR, int IX, int RPW>
 __global__ __launch_bounds__(256) void rope_row_kernel(T* __restrict__ out, const T* __restrict__ in,
                                                        T* __restrict__ vout, const T* __restrict__ vin,
                                                        long long n_rows, int heads, int n_hg,
@@ -182,88 +195,104 @@ __global__ __launch_bounds__(256) void rope_row_kernel(T* __restrict__ out, cons
   const long long tid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   const long long grp = tid / G;
   const int l = (int)(tid - grp * G);
-  const long long row = grp / n_hg;
-  if (row >= n_rows) return;  // whole groups leave together
-  const int hg = (int)(grp - row * n_hg);
+  const long long rb = grp / n_hg;
+  if (rb * RPW >= n_rows) return;  // whole groups leave together
+  const int hg = (int)(grp - rb * n_hg);
   const int hl = l / LPH, j = l - hl * LPH;
   const int h = hg * HG + hl;
-  long long src, delta;
-  if constexpr (IX == IX_APPLY) {
-    src = row;
-    delta = pos_to[row];
-  } else if constexpr (IX == IX_GATHER_ROW) {
-    const int g = gather[row], pt = pos_to[row], pf = pos_from[row];
-    src = g;
-    delta = (long long)pt - pf;
-  } else if constexpr (IX == IX_GATHER_SRC) {
-    const int g = gather[row], pt = pos_to[row];
-    src = g;
-    delta = (long long)pt - pos_from[g];
-  } else {
-    src = gather ? (long long)gather[row] : row;
-    delta = (long long)pos_to[row] - (pos_from ? (long long)pos_from[from_by_src ? src : row] : 0LL);
-  }
-  const double th = fr.rev[l % (D / 2)];
   const int hc = h < heads ? h : heads - 1;   // lanes past the last head load a real row, store nothing
-  const long long off_in = (src * heads + hc) * D, off_out = (row * heads + h) * D;
   const bool second = LAYOUT == AKV_ROPE_HALF && j >= CPR;
   const int c = LAYOUT == AKV_ROPE_HALF ? (second ? j - CPR : j) : j;
-  float a[8], b[8];
-  if (LAYOUT == AKV_ROPE_HALF) {
-    Vec8<T>::load(in + off_in + 8 * c, a);
-    Vec8<T>::load(in + off_in + D / 2 + 8 * c, b);
-  } else {
-    Vec8<T>::load(in + off_in + 8 * j, a);
+  const double th = fr.rev[l % (D / 2)];
+  long long row[RPW], src[RPW], delta[RPW];
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    row[r] = rb * RPW + r < n_rows ? rb * RPW + r : n_rows - 1;
+    if constexpr (IX == IX_APPLY) {
+      src[r] = row[r];
+      delta[r] = pos_to[row[r]];
+    } else if constexpr (IX == IX_GATHER_ROW) {
+      const int g = gather[row[r]], pt = pos_to[row[r]], pf = pos_from[row[r]];
+      src[r] = g;
+      delta[r] = (long long)pt - pf;
+    } else if constexpr (IX == IX_GATHER_SRC) {
+      const int g = gather[row[r]], pt = pos_to[row[r]];
+      src[r] = g;
+      delta[r] = (long long)pt - pos_from[g];
+    } else {
+      src[r] = gather ? (long long)gather[row[r]] : row[r];
+      delta[r] = (long long)pos_to[row[r]] - (pos_from ? (long long)pos_from[from_by_src ? src[r] : row[r]] : 0LL);
+    }
   }
-  Raw8<T> vv;
-  if (vout) vv.load(vin + off_in + 8 * j);
-  float mc, ms;
-  angle_cs(delta, th, mc, ms);
+  Raw8<T> ra[RPW], rb2[RPW], vv[RPW];   // raw rows: fewer registers than converted ones
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    const long long off_in = (src[r] * heads + hc) * D;
+    if (LAYOUT == AKV_ROPE_HALF) {
+      ra[r].load(in + off_in + 8 * c);
+      rb2[r].load(in + off_in + D / 2 + 8 * c);
+    } else {
+      ra[r].load(in + off_in + 8 * j);
+    }
+    if (vout) vv[r].load(vin + off_in + 8 * j);
+  }
   const int base = (int)(threadIdx.x & 63) - l;
-  float y[8];
-  if (LAYOUT == AKV_ROPE_HALF) {
-    float cs[8], sn[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      cs[i] = __shfl(mc, base + 8 * c + i, 64);
-      sn[i] = __shfl(ms, base + 8 * c + i, 64);
+  for (int r = 0; r < RPW; ++r) {
+    float mc, ms;
+    angle_cs(delta[r], th, mc, ms);
+    float a[8], b[8], y[8];
+    ra[r].get(a);
+    if (LAYOUT == AKV_ROPE_HALF) rb2[r].get(b);
+    if (LAYOUT == AKV_ROPE_HALF) {
+      float cs[8], sn[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        cs[i] = __shfl(mc, base + 8 * c + i, 64);
+        sn[i] = __shfl(ms, base + 8 * c + i, 64);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        y[i] = second ? a[i] * sn[i] + b[i] * cs[i] : a[i] * cs[i] - b[i] * sn[i];
+    } else {
+      float cs[4], sn[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        cs[i] = __shfl(mc, base + 4 * j + i, 64);
+        sn[i] = __shfl(ms, base + 4 * j + i, 64);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        y[2 * i] = a[2 * i] * cs[i] - a[2 * i + 1] * sn[i];
+        y[2 * i + 1] = a[2 * i] * sn[i] + a[2 * i + 1] * cs[i];
+      }
     }
-    if (h >= heads) return;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) y[i] = second ? a[i] * sn[i] + b[i] * cs[i] : a[i] * cs[i] - b[i] * sn[i];
-  } else {
-    float cs[4], sn[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      cs[i] = __shfl(mc, base + 4 * j + i, 64);
-      sn[i] = __shfl(ms, base + 4 * j + i, 64);
+    if (h >= heads || rb * RPW + r >= n_rows) continue;
+    const long long off_out = (row[r] * heads + h) * D;
+    // Gathered forms write new copies once: streaming stores, so the next kernel
+    // finds no dirty lines to write back.  RoPE-apply output is read right away by
+    // the attention and stays cached.
+    if constexpr (IX == IX_APPLY) {
+      Vec8<T>::store(out + off_out + 8 * j, y);
+      if (vout) vv[r].store(vout + off_out + 8 * j);
+    } else {
+      store8_nt(out + off_out + 8 * j, y);
+      if (vout) vv[r].store_nt(vout + off_out + 8 * j);
     }
-    if (h >= heads) return;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      y[2 * i] = a[2 * i] * cs[i] - a[2 * i + 1] * sn[i];
-      y[2 * i + 1] = a[2 * i] * sn[i] + a[2 * i + 1] * cs[i];
-    }
-  }
-  // Gathered forms write new copies once: streaming stores, so the next kernel finds
-  // no dirty lines to write back.  RoPE-apply output is read right away by the
-  // attention and stays cached.
-  if constexpr (IX == IX_APPLY) {
-    Vec8<T>::store(out + off_out + 8 * j, y);
-    if (vout) vv.store(vout + off_out + 8 * j);
-  } else {
-    store8_nt(out + off_out + 8 * j, y);
-    if (vout) vv.store_nt(vout + off_out + 8 * j);
   }
 }
+
+// Rows per group of the row kernel.
+constexpr int kRowsPerGroup = 2;
 
 template <typename T, int LAYOUT, int CPR, int IX>
 void launch_row_ix(const RopeArgs& a, const Freqs& fr, hipStream_t s) {
   constexpr int HG = 32 / CPR < 8 ? 32 / CPR : 8;
+  constexpr int RPW = kRowsPerGroup;
   const int n_hg = (a.heads + HG - 1) / HG;
-  const long long threads = a.n_rows * n_hg * (long long)(HG * 2 * CPR);
+  const long long threads = (a.n_rows + RPW - 1) / RPW * n_hg * (long long)(HG * 2 * CPR);
   const unsigned blocks = (unsigned)((threads + 255) / 256);
-  hipLaunchKernelGGL((rope_row_kernel<T, LAYOUT, CPR, IX>), dim3(blocks), dim3(256), 0, s, (T*)a.out,
+  hipLaunchKernelGGL((rope_row_kernel<T, LAYOUT, CPR, IX, RPW>), dim3(blocks), dim3(256), 0, s, (T*)a.out,
                      (const T*)a.in, (T*)a.v_out, (const T*)a.v_in, (long long)a.n_rows, a.heads, n_hg,
                      a.gather, a.pos_from, a.pos_from_by_src ? 1 : 0, a.pos_to, fr);
 }
