@@ -156,10 +156,30 @@ __device__ __forceinline__ void tile_qk(WaveState& w, const uint16_t* lkb, const
   }
 }
 
+// V^T fragments of one tile from the row-major V tile through the transposing LDS
+// read (lane i of a 16-lane group gets element i%4 of the 8-byte chunk that lane
+// 4k + i/4 addresses, for k = 0..3).  Fragment g = 4kb + 2hf + db, two reads each.
+__device__ __forceinline__ void read_vt_part(VFrag& f, const uint16_t* lvb, int lane, int g) {
+  const int G = lane >> 4, i16 = lane & 15;
+  const int kb = g >> 2, hf = (g >> 1) & 1, db = g & 1;
+  const int key = kb * 32 + 16 * hf + 4 * (G >> 1) + (i16 >> 2);
+  const int dc = db * 32 + 16 * (G & 1) + 4 * (i16 & 3);
+  const s16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lvb + key * VP + dc));
+  const s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lvb + (key + 8) * VP + dc));
+  f.a[kb][hf][db] = cat4(r0, r1);
+}
+
+__device__ __forceinline__ void read_vt(VFrag& f, const uint16_t* lvb, int lane) {
+#pragma unroll
+  for (int g = 0; g < 8; ++g) read_vt_part(f, lvb, lane, g);
+}
+
 // tile_qk with the K fragments and the first Q' slice (b0) already in registers;
-// the remaining Q' slices are read from LDS one d slice ahead of their MFMAs.
+// the remaining Q' slices are read from LDS one d slice ahead of their MFMAs, and
+// after each d slice's MFMAs two of the next tile's V^T fragments (vf, from lvb)
+// are read, so those LDS reads issue between MFMAs instead of in one block.
 __device__ __forceinline__ void mfma_qk_lq(WaveState& w, const KFrag& f, const bf16x8 (&b0)[2], const uint16_t* lqw,
-                                           int lq, int lg) {
+                                           int lq, int lg, VFrag& vf, const uint16_t* lvb, int lane) {
   const f32x16 zero = {};
   bf16x8 b[2][2];
   b[0][0] = b0[0];
@@ -176,6 +196,8 @@ __device__ __forceinline__ void mfma_qk_lq(WaveState& w, const KFrag& f, const b
       for (int qb = 0; qb < 2; ++qb)
         w.s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[ds][kb], b[ds & 1][qb], ds ? w.s[kb][qb] : zero,
                                                               0, 0, 0);
+    read_vt_part(vf, lvb, lane, 2 * ds);
+    read_vt_part(vf, lvb, lane, 2 * ds + 1);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -332,24 +354,6 @@ __device__ __forceinline__ bf16x8 colsum_selector(int lane) {
   return a;
 }
 
-// V^T fragments of one tile from the row-major V tile through the transposing LDS
-// read (lane i of a 16-lane group gets element i%4 of the 8-byte chunk that lane
-// 4k + i/4 addresses, for k = 0..3).
-__device__ __forceinline__ void read_vt(VFrag& f, const uint16_t* lvb, int lane) {
-  const int G = lane >> 4, i16 = lane & 15;
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-      for (int db = 0; db < 2; ++db) {
-        const int key = kb * 32 + 16 * hf + 4 * (G >> 1) + (i16 >> 2);
-        const int dc = db * 32 + 16 * (G & 1) + 4 * (i16 & 3);
-        const s16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lvb + key * VP + dc));
-        const s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lvb + (key + 8) * VP + dc));
-        f.a[kb][hf][db] = cat4(r0, r1);
-      }
-}
 
 // O^T += V^T P^T for one tile (16 MFMAs).
 __device__ __forceinline__ void mfma_pv(WaveState& w, const VFrag& f) {
@@ -696,9 +700,10 @@ __device__ __forceinline__ void pp_pipeline(WaveState& w, f32x4 (&ls)[2], bf16x8
       tile_softmax_fast(w, (ent & 3) == AKV_TILE_PARTIAL, mtok[slot], mdrop[slot], q0, lq, lg);
     lds_barrier();
     // phase 2 (MFMA): PV of tile i, QK of tile i+1 (its K fragments are read between
-    // the PV MFMAs, which hide their latency), the V^T fragments of tile i+1 (both
-    // halves of it were stashed before the barrier above); then tile i+2 goes to the
-    // slot freed by tile i-1 (its last reader finished before the barrier above)
+    // the PV MFMAs, which hide their latency) with the V^T fragments of tile i+1 read
+    // between its MFMAs (both halves of that tile were stashed before the barrier
+    // above); then tile i+2 goes to the slot freed by tile i-1 (its last reader
+    // finished before the barrier above)
     __builtin_amdgcn_s_setprio(1);
     // (after the last tile, slot1 holds an older tile: its K reads are harmless and unused)
     KFrag kf;
@@ -706,8 +711,7 @@ __device__ __forceinline__ void pp_pipeline(WaveState& w, f32x4 (&ls)[2], bf16x8
     mfma_pv_read_k<!SAFE>(w, vf, kf, q0f, ls, sel, lk[slot1], lqw, lq, lg);
     // P of tile i is dead here, before the scores of tile i+1 are born: they share registers
     if (i + 1 < n) {
-      mfma_qk_lq(w, kf, q0f, lqw, lq, lg);
-      read_vt(vf, lv[slot1], lane);
+      mfma_qk_lq(w, kf, q0f, lqw, lq, lg, vf, lv[slot1], lane);
     }
     __builtin_amdgcn_s_setprio(0);
     if (fetch2) st.stash(lk[slot2], lv[slot2], mtok[slot2], mdrop[slot2], p2);
