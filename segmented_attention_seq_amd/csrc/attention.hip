@@ -699,22 +699,23 @@ __device__ __forceinline__ void pp_pipeline(WaveState& w, f32x4 (&ls)[2], bf16x8
     else
       tile_softmax_fast(w, (ent & 3) == AKV_TILE_PARTIAL, mtok[slot], mdrop[slot], q0, lq, lg);
     lds_barrier();
-    // phase 2 (MFMA): PV of tile i, QK of tile i+1 (its K fragments are read between
-    // the PV MFMAs, which hide their latency) with the V^T fragments of tile i+1 read
-    // between its MFMAs (both halves of that tile were stashed before the barrier
-    // above); then tile i+2 goes to the slot freed by tile i-1 (its last reader
-    // finished before the barrier above)
+    // phase 2 (MFMA): PV of tile i (the K fragments of tile i+1 are read between its
+    // MFMAs, which hide their latency); tile i+2 goes to the slot freed by tile i-1
+    // (its last reader finished before the barrier above); QK of tile i+1 with the
+    // V^T fragments of tile i+1 read between its MFMAs (both halves of that tile
+    // were stashed before the barrier above)
     __builtin_amdgcn_s_setprio(1);
     // (after the last tile, slot1 holds an older tile: its K reads are harmless and unused)
     KFrag kf;
     bf16x8 q0f[2];
     mfma_pv_read_k<!SAFE>(w, vf, kf, q0f, ls, sel, lk[slot1], lqw, lq, lg);
-    // P of tile i is dead here, before the scores of tile i+1 are born: they share registers
-    if (i + 1 < n) {
-      mfma_qk_lq(w, kf, q0f, lqw, lq, lg, vf, lv[slot1], lane);
-    }
-    __builtin_amdgcn_s_setprio(0);
+    // The stash goes ahead of QK: issued after QK's V^T reads, its LDS writes would
+    // wait behind them, and the barrier below waits for the writes.
     if (fetch2) st.stash(lk[slot2], lv[slot2], mtok[slot2], mdrop[slot2], p2);
+    __builtin_amdgcn_sched_barrier(0);
+    // P of tile i is dead here, before the scores of tile i+1 are born: they share registers
+    if (i + 1 < n) mfma_qk_lq(w, kf, q0f, lqw, lq, lg, vf, lv[slot1], lane);
+    __builtin_amdgcn_s_setprio(0);
     lds_barrier();
     slot = slot1;
     ent = e1;
