@@ -690,9 +690,9 @@ __device__ __forceinline__ void pp_pipeline(WaveState& w, f32x4 (&ls)[2], bf16x8
     const int slot1 = slot == NSLOT - 1 ? 0 : slot + 1;
     const int slot2 = slot1 == NSLOT - 1 ? 0 : slot1 + 1;
     if (fetch2) st.fetch(tile_src(e2, nvt, voff, r, tb, te, k, v, kver, vver), p2, hkv, hk, tok_drop, ver_src);
-    // phase 1 (VALU): softmax of tile i.  Its V^T fragments were read at the end of
-    // the previous MFMA phase: LDS reads issued here would hold up the exp stream
-    // while the partner wave's K and Q' reads occupy the LDS.
+    // phase 1 (VALU): softmax of tile i.  Its V^T fragments were read between the QK
+    // MFMAs of the previous MFMA phase: LDS reads issued here would hold up the exp
+    // stream while the partner wave's K and Q' reads occupy the LDS.
     __builtin_amdgcn_sched_barrier(0);
     if (SAFE)
       tile_softmax<true>(w, (ent & 3) == AKV_TILE_PARTIAL, mtok[slot], mdrop[slot], lk[slot], lqw, q0, lq, lg);
