@@ -93,6 +93,24 @@ def test_repos_fp32_head_dims_and_counts(d, H, layout):
     assert err <= 1e-5
 
 
+@pytest.mark.parametrize("n", [1, 2, 3, 257])
+def test_repos_writes_exactly_its_rows(n):
+    """Rows are handled in groups of two; a group past the last row must store
+    nothing: the output is a view into a larger buffer whose tail stays untouched."""
+    rng = np.random.default_rng(40 + n)
+    H, d = 8, 64
+    k = rng.standard_normal((300, H, d)).astype(np.float32)
+    g = rng.integers(0, 300, n).astype(np.int32)
+    pf = rng.integers(0, 5000, n).astype(np.int32)
+    pt = rng.integers(0, 5000, n).astype(np.int32)
+    full = nan_like((n + 4, H, d), torch.float32)
+    akv.rope_repos(full[:n], dev_tensor(k, False), dev_int(pt), dev_int(pf), dev_int(g), BASE)
+    ref = oracle.repos(k[g], pf, pt, BASE)
+    got = host_f64(full)
+    assert np.abs(got[:n] - ref).max() <= 1e-5
+    assert np.isnan(got[n:]).all()
+
+
 def test_repos_bf16_one_ulp_and_rne():
     rng = np.random.default_rng(12)
     n, H, d = 4000, 8, 64
