@@ -98,3 +98,12 @@ def test_traffic_key_ignores_comments_only(tmp_path, monkeypatch):
     assert bench.attn_src_hash() == h0
     (tmp_path / "f1.h").write_text("#define X 3 // two\n")
     assert bench.attn_src_hash() != h0
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """The bench measures one GPU; asking for more exits with a message before any
+    GPU or library work."""
+    r = subprocess.run([sys.executable, str(ROOT / "bench.py"), "--gpus", "2"], cwd=ROOT, capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
