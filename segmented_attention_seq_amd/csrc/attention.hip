@@ -29,7 +29,8 @@
 //     work item and a redo through the rescaling softmax when it fails;
 //   * 1, 2 or 4 query heads per kv head (seg_attn_bf16<GROUP>): one wave per query
 //     head, double-buffered tiles, the rescaling softmax (lazily moved exponent
-//     offset, bf16 dot2 row sums, per-tile range check);
+//     offset, bf16 dot2 row sums, per-tile range check); with 2 or 4 heads two
+//     workgroups share a CU, so MFMA and softmax work of the two overlap;
 //   * queries arrive either rotated or raw; raw ones are rotated to their append
 //     positions (tok_pos) in fp32 as they are loaded, before the scale and the one
 //     bf16 rounding (review §3.3: a vector at position p is the raw vector rotated
@@ -594,9 +595,13 @@ struct TileStage {
       int hq, int hkv, float scale, const int *__restrict__ tok_pos, RopeQ rq
 
 // Double-buffered pipeline: tile t+1 is loaded while tile t computes.  Used when
-// the query-head group is smaller than 8 (fewer than two waves per SIMD).
+// the query-head group is smaller than 8, so one workgroup has fewer than two waves
+// per SIMD.  With 2 or 4 waves the register budget is held to two waves per SIMD,
+// so two workgroups share each CU and one's MFMAs overlap the other's softmax
+// (39 KB of LDS each); a one-wave workgroup keeps the full register file, since
+// its 64-lane tile staging would spill at half of it.
 template <int GROUP>
-__global__ __launch_bounds__(64 * GROUP) void seg_attn_bf16(AKV_ATTN_PARAMS) {
+__global__ __launch_bounds__(64 * GROUP, GROUP >= 2 ? 2 : 1) void seg_attn_bf16(AKV_ATTN_PARAMS) {
   constexpr int NT = 64 * GROUP;
   __shared__ __attribute__((aligned(16))) uint16_t lk[2][BK * KP];
   __shared__ __attribute__((aligned(16))) uint16_t lv[2][BK * VP];
