@@ -28,9 +28,9 @@
 //     0 and takes the column sums from the matrix cores, with one range check per
 //     work item and a redo through the rescaling softmax when it fails;
 //   * 1, 2 or 4 query heads per kv head (seg_attn_bf16<GROUP>): one wave per query
-//     head, double-buffered tiles, the rescaling softmax (lazily moved exponent
-//     offset, bf16 dot2 row sums, per-tile range check); with 2 or 4 heads two
-//     workgroups share a CU, so MFMA and softmax work of the two overlap;
+//     head, one synchronously staged tile buffer, the rescaling softmax (lazily
+//     moved exponent offset, bf16 dot2 row sums, per-tile range check); several
+//     workgroups share a CU, so one's MFMA work overlaps another's softmax and loads;
 //   * queries arrive either rotated or raw; raw ones are rotated to their append
 //     positions (tok_pos) in fp32 as they are loaded, before the scale and the one
 //     bf16 rounding (review §3.3: a vector at position p is the raw vector rotated
@@ -594,18 +594,18 @@ struct TileStage {
       const int *__restrict__ ver_src, uint16_t *__restrict__ out, float *__restrict__ lse,       \
       int hq, int hkv, float scale, const int *__restrict__ tok_pos, RopeQ rq
 
-// Double-buffered pipeline: tile t+1 is loaded while tile t computes.  Used when
-// the query-head group is smaller than 8, so one workgroup has fewer than two waves
-// per SIMD.  With 2 or 4 waves the register budget is held to two waves per SIMD,
-// so two workgroups share each CU and one's MFMAs overlap the other's softmax
-// (39 KB of LDS each); a one-wave workgroup keeps the full register file, since
-// its 64-lane tile staging would spill at half of it.
+// One wave per query head for groups of 1, 2 or 4 query heads per kv head.  Each
+// K/V tile is staged synchronously into a single LDS buffer (20 KB per workgroup),
+// and the registers are held to two waves per SIMD, so several workgroups share a
+// CU: while one waits for its tile or runs its softmax, another's MFMAs run.  (A
+// double-buffered version that prefetched the next tile into registers spilled at
+// this register budget and ran slower.)
 template <int GROUP>
-__global__ __launch_bounds__(64 * GROUP, GROUP >= 2 ? 2 : 1) void seg_attn_bf16(AKV_ATTN_PARAMS) {
+__global__ __launch_bounds__(64 * GROUP, 2) void seg_attn_bf16(AKV_ATTN_PARAMS) {
   constexpr int NT = 64 * GROUP;
-  __shared__ __attribute__((aligned(16))) uint16_t lk[2][BK * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t lv[2][BK * VP];
-  __shared__ int mtok[2][BK], mdrop[2][BK];
+  __shared__ __attribute__((aligned(16))) uint16_t lk[BK * KP];
+  __shared__ __attribute__((aligned(16))) uint16_t lv[BK * VP];
+  __shared__ int mtok[BK], mdrop[BK];
 
   const int hk = blockIdx.x % hkv;
   const int item = order[blockIdx.x / hkv];
@@ -622,26 +622,16 @@ __global__ __launch_bounds__(64 * GROUP, GROUP >= 2 ? 2 : 1) void seg_attn_bf16(
   load_q<false>(w, nullptr, q, q0, q1, hq, h, lq, lg, sl2, tok_pos, rq);
   TileStage<NT> st;
   st.wave_s = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (t0 < t1) {
-    const int e = tiles[t0];
-    st.fetch(tile_src(e, nvt, voff, r, tb, te, k, v, kver, vver), (e & 3) == AKV_TILE_PARTIAL, hkv, hk,
-             tok_drop, ver_src);
-    st.stash(lk[0], lv[0], mtok[0], mdrop[0], (e & 3) == AKV_TILE_PARTIAL);
-  }
-  __syncthreads();
   for (int t = t0; t < t1; ++t) {
-    const int buf = (t - t0) & 1;
     const int ent = tiles[t];
-    const bool has_next = t + 1 < t1;
-    const int en = has_next ? tiles[t + 1] : 0;
-    if (has_next)
-      st.fetch(tile_src(en, nvt, voff, r, tb, te, k, v, kver, vver), (en & 3) == AKV_TILE_PARTIAL, hkv, hk,
-               tok_drop, ver_src);
-    tile_qk<false>(w, lk[buf], nullptr, lq, lg);
-    tile_softmax<false>(w, (ent & 3) == AKV_TILE_PARTIAL, mtok[buf], mdrop[buf], lk[buf], nullptr, q0, lq, lg);
-    tile_pv(w, lv[buf], lane);
-    if (has_next) st.stash(lk[buf ^ 1], lv[buf ^ 1], mtok[buf ^ 1], mdrop[buf ^ 1], (en & 3) == AKV_TILE_PARTIAL);
+    const bool partial = (ent & 3) == AKV_TILE_PARTIAL;
+    st.fetch(tile_src(ent, nvt, voff, r, tb, te, k, v, kver, vver), partial, hkv, hk, tok_drop, ver_src);
+    st.stash(lk, lv, mtok, mdrop, partial);
     lds_barrier();
+    tile_qk<false>(w, lk, nullptr, lq, lg);
+    tile_softmax<false>(w, partial, mtok, mdrop, lk, nullptr, q0, lq, lg);
+    tile_pv(w, lv, lane);
+    lds_barrier();  // every wave is done with this tile before the next one is staged
   }
   store_out<false>(w, out, lse, q0, q1, hq, h, lq, lg, nullptr, lane);
 }
