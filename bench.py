@@ -324,7 +324,7 @@ def main():
                                f"{n_keys} gathered keys", "restore_tokens": T, "visible_pairs": pairs,
                    "attn_flop_per_step": attn_flop, "version_rows": nv,
                    "stages": sorted(only)},
-        "roofline": {"bound": "mfma", "kernel": "segment attention (seg_attn_bf16)",
+        "roofline": {"bound": "mfma", "kernel": "segment attention (seg_attn_bf16_pp, 8 query heads per kv head)",
                      "achieved": attn_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": (attn_tflops / PEAK_BF16_TFLOPS) if attn_tflops else None,
                      "traffic": traffic},
