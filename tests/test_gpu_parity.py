@@ -389,6 +389,24 @@ def test_workloads_full_size_sampled(cfg, n_random):
     _check_rows(tr, (q, k, v), out, lse, bf16=True, rows=rows)
 
 
+
+@pytest.mark.parametrize("hq", [32, 16, 8])
+def test_48k_workload_smaller_head_groups_sampled(hq):
+    """The 48k restore with 4, 2 and 1 query heads per kv head (the one-wave-per-head
+    kernel, several workgroups per CU) at full size, checked on boundary and seeded
+    rows."""
+    tr = workload.config_trajectory(2)
+    q, k, v = workload.prefill_tensors(tr.n_tokens, hq, 8, 64, seed=300 + hq)
+    plan = akv.build_visibility(akv.ops_from_messages(tr.msg_len, tr.drop, tr.reposition))
+    T = tr.n_tokens
+    bufs = {"out": nan_like((T, hq, 64), torch.bfloat16), "lse": nan_like((T, hq), torch.float32)}
+    out, lse = akv.restore(plan, dev_tensor(q, True), dev_tensor(k, True), dev_tensor(v, True), BASE,
+                           with_lse=True, bufs=bufs)
+    torch.cuda.synchronize()
+    assert not torch.isnan(out).any().item()
+    rows = boundary_rows(plan.tables(), T, np.random.default_rng(hq), 48, edge=1)
+    _check_rows(tr, (q, k, v), out, lse, bf16=True, rows=rows)
+
 # ---------------------------------------------------------------- decode
 
 def _decode_case(batch, lo, hi, seed, hq=64, hkv=8, shuffle=False):
