@@ -870,12 +870,14 @@ int launch_segment_attention(const AttnArgs& a, void* stream) {
       case 1: AKV_LAUNCH_BF16(1); break;
       case 2: AKV_LAUNCH_BF16(2); break;
       case 4: AKV_LAUNCH_BF16(4); break;
-      default:
+      case 8:
         hipLaunchKernelGGL(seg_attn_bf16_pp, dim3((unsigned)blocks), dim3(512), 0, s, (const uint16_t*)a.q,
                            (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.k_ver,
                            (const uint16_t*)a.v_ver, a.item_desc, a.tiles, a.order, a.tok_drop, a.ver_src,
                            (uint16_t*)a.out, a.lse, a.hq, a.hkv, a.scale, a.tok_pos, a.rq);
         break;
+      default:
+        return fail(AKV_EUNSUPPORTED, "bf16 segment attention needs hq/hkv in {1, 2, 4, 8}");
     }
 #undef AKV_LAUNCH_BF16
   } else {
