@@ -29,4 +29,4 @@ from .replay import replay_tokens, replay_events  # noqa: F401
 from .attention import (attention_replay, segment_attention, visibility_mask,  # noqa: F401
                         decode, decode_after_ops, repos)
 from .tables import plan_tables, tile_classes, tile_class_of  # noqa: F401
-from .bf16 import f64_to_bf16_bits, bf16_bits_to_f64  # noqa: F401
+from .bf16 import f64_to_bf16_bits  # noqa: F401

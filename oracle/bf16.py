@@ -30,8 +30,3 @@ def f64_to_bf16_bits(x) -> np.ndarray:
         raise ValueError("value outside bf16 normal range")
     bits = (sign.astype(np.int64) << 15) | (np.where(zero, 0, e8) << 7) | np.where(zero, 0, keep)
     return bits.astype(np.uint16)
-
-
-def bf16_bits_to_f64(b) -> np.ndarray:
-    b = np.asarray(b, np.uint16).astype(np.uint32) << np.uint32(16)
-    return b.view(np.float32).astype(np.float64)

@@ -405,3 +405,156 @@ def test_replay_events_on_workloads():
         # tokens of a stretch sit at consecutive positions starting at r
         for tb, te, src in ev.epochs:
             assert np.array_equal(ev.tok_pos[tb:te], src.size + np.arange(te - tb))
+
+
+# ---------------------------------------------------------------- tables: two repos, a drop across stretches
+
+CLS = {"EMPTY": 0, "PARTIAL": 1, "FULL": 2}
+
+
+def test_two_repos_cross_stretch_drop_golden():
+    """Every table of a hand-worked request with two repos and a drop whose target
+    was appended one stretch before the boundary that drops it ([P1] §3.3, §4,
+    §4.2 / App. A.1.1)."""
+    g = _golden("two_repos_cross_stretch_drop.json")
+    e = g["expected"]
+    ops = _ops_from(g)
+    assert ops == [tuple([KIND[o[0]]] + o[1:]) for o in e["ops"]]
+    t = oracle.plan_tables(ops, bq=g["bq"], bk=g["bk"])
+    assert t["tok_pos"].tolist() == e["tok_pos"]
+    assert t["tok_drop"].tolist() == [NEVER if x == "never" else x for x in e["tok_drop"]]
+    assert t["segments"].tolist() == e["segments"]
+    assert t["epochs"].tolist() == e["epochs"]
+    assert t["versions"].tolist() == e["versions"]
+    assert t["visible_pairs"] == e["visible_pairs"]
+    assert t["items"].tolist() == e["items"]
+    assert t["tile_ptr"].tolist() == e["tile_ptr"]
+    assert list(zip(t["tile_k"].tolist(), t["tile_cls"].tolist())) == [(k, CLS[c]) for k, c in e["tiles"]]
+    assert t["final_tok"].tolist() == e["final_tok"]
+    assert t["final_pos"].tolist() == e["final_pos"]
+    assert t["p_next"] == e["p_next"]
+    # the one-spot form agrees on every tile of every item, EMPTY ones included
+    ev = oracle.replay_events(ops)
+    listed = {}
+    for n, (s, qt) in enumerate(e["items"]):
+        for k, c in e["tiles"][e["tile_ptr"][n]:e["tile_ptr"][n + 1]]:
+            listed[(s, qt, k)] = CLS[c]
+    for n, (s, qt) in enumerate(e["items"]):
+        tb, te, r, _ = e["epochs"][s]
+        for k in range(-(-r // g["bk"]) + -(-(te - tb) // g["bk"])):
+            assert oracle.tile_class_of(ev, s, qt, k, g["bq"], g["bk"]) == listed.get((s, qt, k), 0), (s, qt, k)
+
+
+def _stretches_from_ops(ops):
+    """(tok_begin, tok_end) of every run of tokens between REPOS ops that appends
+    at least one token, read straight off the op list."""
+    out, t, start = [], 0, 0
+    for op in ops:
+        if op[0] == APPEND:
+            t += op[1]
+        elif op[0] == REPOS:
+            if t > start:
+                out.append((start, t))
+            start = t
+    if t > start:
+        out.append((start, t))
+    return out
+
+
+def _brute_tile_classes(ops, bq, bk):
+    """Tile classes of every (stretch, q-tile, k-tile), EMPTY ones included, from
+    the token-by-token replay alone: inside a stretch no repos happens, so a key a
+    query sees sits at its current position, which is its index on the stretch's
+    axis (version rows 0..r-1, then own tokens from r); r is the position the
+    stretch's first token is appended at (the next append after a repos uses r).
+    Key slots past the end of a part hold no key and count as hidden, so a tile
+    with such a slot is never FULL (a FULL tile is one that may run unmasked)."""
+    recs, _ = oracle.replay_tokens(ops)
+    res = {}
+    for s, (tb, te) in enumerate(_stretches_from_ops(ops)):
+        r = recs[tb][0]
+        nvt, nown = -(-r // bk), te - tb
+        nkt = nvt + -(-nown // bk)
+        exists = np.zeros(nkt * bk, bool)          # key slots that hold a key
+        exists[:r] = True
+        exists[nvt * bk:nvt * bk + nown] = True
+        for qt in range(-(-nown // bq)):
+            rows = range(tb + qt * bq, min(te, tb + (qt + 1) * bq))
+            m = np.zeros((len(rows), nkt * bk), bool)
+            for a, i in enumerate(rows):
+                for j, pj in recs[i][1]:
+                    slot = pj if pj < r else nvt * bk + (pj - r)
+                    assert exists[slot]
+                    m[a, slot] = True
+            for kt in range(nkt):
+                blk, inr = m[:, kt * bk:(kt + 1) * bk], exists[kt * bk:(kt + 1) * bk]
+                res[(s, qt, kt)] = 0 if not blk.any() else 2 if (inr.all() and blk.all()) else 1
+    return res
+
+
+@st.composite
+def longer_op_sequences(draw):
+    M = draw(st.integers(1, 9))
+    lens = draw(st.lists(st.integers(0, 13), min_size=M, max_size=M))
+    drop = {}
+    for k in range(M):
+        tg = draw(st.lists(st.integers(0, k), max_size=3))
+        if tg:
+            drop[k] = tg
+    repos = draw(st.lists(st.integers(0, M - 1), max_size=4))
+    return lens, drop, repos
+
+
+@settings(max_examples=250, deadline=None)
+@given(st.one_of(op_sequences(), longer_op_sequences()),
+       st.sampled_from([(1, 1), (2, 2), (3, 2), (2, 3), (4, 4), (5, 3)]))
+def test_tile_classes_match_brute_force_from_replay(seq, tiles):
+    """tile_classes (the listed non-EMPTY tiles) and tile_class_of (any one tile)
+    against classes read off the token-by-token replay."""
+    lens, drop, repos = seq
+    ops = oracle.canonical_ops(lens, drop, repos)
+    bq, bk = tiles
+    brute = _brute_tile_classes(ops, bq, bk)
+    ev = oracle.replay_events(ops)
+    items, ptr, kts, cls = oracle.tile_classes(ev, bq, bk)
+    listed = {}
+    for n, (s, qt) in enumerate(items.tolist()):
+        for kt, c in zip(kts[ptr[n]:ptr[n + 1]].tolist(), cls[ptr[n]:ptr[n + 1]].tolist()):
+            listed[(s, qt, kt)] = c
+    assert listed == {key: c for key, c in brute.items() if c}
+    assert [tuple(x) for x in items.tolist()] == sorted({(s, qt) for s, qt, _ in brute})
+    for (s, qt, kt), c in brute.items():
+        assert oracle.tile_class_of(ev, s, qt, kt, bq, bk) == c, (s, qt, kt)
+
+
+@settings(max_examples=250, deadline=None)
+@given(st.one_of(op_sequences(), longer_op_sequences()))
+def test_segment_stretches_and_versions_against_replay(seq):
+    """T3's stretch column and T4/T5 against the op list and the token replay: a
+    segment lies inside the stretch it names; stretch rows are (begin, end, r,
+    running row offset); version row v of a stretch is the key its queries see at
+    position v, listed in ascending token order with its append position."""
+    lens, drop, repos = seq
+    ops = oracle.canonical_ops(lens, drop, repos)
+    t = oracle.plan_tables(ops, with_tiles=False)
+    recs, _ = oracle.replay_tokens(ops)
+    stretches = _stretches_from_ops(ops)
+    for b, e, s in t["segments"].tolist():
+        assert stretches[s][0] <= b < e <= stretches[s][1]
+    assert sorted({s for _, _, s in t["segments"].tolist()}) == list(range(len(stretches)))
+    off = 0
+    vers = t["versions"].tolist()
+    for s, (tb, te) in enumerate(stretches):
+        r = recs[tb][0]
+        assert t["epochs"][s].tolist() == [tb, te, r, off]
+        rows = vers[off:off + r]
+        assert [v for _, _, v in rows] == list(range(r))
+        assert [j for j, _, _ in rows] == sorted(j for j, _, _ in rows)
+        for j, pf, _ in rows:
+            assert j < tb and pf == recs[j][0]
+        for i in range(tb, te):
+            for j, pj in recs[i][1]:
+                if pj < r:
+                    assert rows[pj][0] == j
+        off += r
+    assert off == len(vers)
