@@ -80,9 +80,14 @@ __device__ __forceinline__ float xhalf_sum(float x) {
 // __syncthreads release fence would drain them).  The memory clobber keeps the
 // compiler from moving LDS accesses across the barrier, the scheduling fences
 // keep it from moving register-only work (exp, MFMA) from one phase to the other.
+// The wait is issued through the builtin so the compiler's wait-count tracking
+// knows the LDS and scalar-memory counters are drained here (a wait hidden in
+// inline asm made it re-wait for reads issued after the barrier).
+constexpr int kWaitLgkm0 = 0xC07F;  // s_waitcnt lgkmcnt(0), vmcnt and expcnt unconstrained
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  asm volatile("s_barrier" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -175,27 +180,30 @@ __device__ __forceinline__ void read_vt(VFrag& f, const uint16_t* lvb, int lane)
   for (int g = 0; g < 8; ++g) read_vt_part(f, lvb, lane, g);
 }
 
-// tile_qk with the K fragments and the first Q' slice (b0) already in registers;
-// the remaining Q' slices are read from LDS one d slice ahead of their MFMAs, and
-// after each d slice's MFMAs two of the next tile's V^T fragments (vf, from lvb)
-// are read, so those LDS reads issue between MFMAs instead of in one block.
-__device__ __forceinline__ void mfma_qk_lq(WaveState& w, const KFrag& f, const bf16x8 (&b0)[2], const uint16_t* lqw,
+// tile_qk with the K fragments and the first two Q' slices (qf[0], qf[1]) already
+// in registers; the remaining Q' slices are read from LDS two d slices ahead of
+// their MFMAs, and after each d slice's MFMAs two of the next tile's V^T fragments
+// (vf, from lvb) are read, so those LDS reads issue between MFMAs instead of in
+// one block.
+__device__ __forceinline__ void mfma_qk_lq(WaveState& w, const KFrag& f, const bf16x8 (&qf)[2][2], const uint16_t* lqw,
                                            int lq, int lg, VFrag& vf, const uint16_t* lvb, int lane) {
   const f32x16 zero = {};
-  bf16x8 b[2][2];
-  b[0][0] = b0[0];
-  b[0][1] = b0[1];
+  bf16x8 b[3][2];
+  b[0][0] = qf[0][0];
+  b[0][1] = qf[0][1];
+  b[1][0] = qf[1][0];
+  b[1][1] = qf[1][1];
 #pragma unroll
   for (int ds = 0; ds < 4; ++ds) {
-    if (ds < 3) {
-      b[(ds + 1) & 1][0] = row_frag(lqw, lq, ds + 1, lg);
-      b[(ds + 1) & 1][1] = row_frag(lqw, 32 + lq, ds + 1, lg);
+    if (ds + 2 < 4) {
+      b[(ds + 2) % 3][0] = row_frag(lqw, lq, ds + 2, lg);
+      b[(ds + 2) % 3][1] = row_frag(lqw, 32 + lq, ds + 2, lg);
     }
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb)
-        w.s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[ds][kb], b[ds & 1][qb], ds ? w.s[kb][qb] : zero,
+        w.s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[ds][kb], b[ds % 3][qb], ds ? w.s[kb][qb] : zero,
                                                               0, 0, 0);
     read_vt_part(vf, lvb, lane, 2 * ds);
     read_vt_part(vf, lvb, lane, 2 * ds + 1);
@@ -371,11 +379,12 @@ __device__ __forceinline__ void mfma_pv(WaveState& w, const VFrag& f) {
 
 // mfma_pv with the next tile's K fragments read in between: after the 4 MFMAs of
 // each (kb, hf) quarter, whose V^T and P registers then die, the two K fragments
-// of one 16-wide d slice are read (and, after the last quarter, the first Q'
-// slice).  The reads' latency hides behind the MFMAs.  With SUMS, each quarter
-// also adds its P slice into the column sums ls (colsum_selector).
+// of one 16-wide d slice are read (and, after the second and the last quarter,
+// the first and the second Q' slice).  The reads' latency hides behind the MFMAs.
+// With SUMS, each quarter also adds its P slice into the column sums ls
+// (colsum_selector).
 template <bool SUMS>
-__device__ __forceinline__ void mfma_pv_read_k(WaveState& w, const VFrag& f, KFrag& kf, bf16x8 (&q0f)[2],
+__device__ __forceinline__ void mfma_pv_read_k(WaveState& w, const VFrag& f, KFrag& kf, bf16x8 (&qf)[2][2],
                                                f32x4 (&ls)[2], bf16x8 sel, const uint16_t* lkb,
                                                const uint16_t* lqw, int lq, int lg) {
 #pragma unroll
@@ -395,9 +404,9 @@ __device__ __forceinline__ void mfma_pv_read_k(WaveState& w, const VFrag& f, KFr
       const int ds = kb * 2 + hf;
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) kf.a[ds][kk] = row_frag(lkb, kk * 32 + lq, ds, lg);
-      if (ds == 3) {
-        q0f[0] = row_frag(lqw, lq, 0, lg);
-        q0f[1] = row_frag(lqw, 32 + lq, 0, lg);
+      if (ds == 1 || ds == 3) {
+        qf[ds >> 1][0] = row_frag(lqw, lq, ds >> 1, lg);
+        qf[ds >> 1][1] = row_frag(lqw, 32 + lq, ds >> 1, lg);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -537,28 +546,51 @@ __device__ __forceinline__ int local_tid(int wave_s) {
 }
 
 // Cooperative global -> register -> LDS staging of one K/V tile and its mask metadata.
+// The tile's PARTIAL flag travels with the fetched registers to the stash.
 template <int NT>
 struct TileStage {
   static constexpr int CPT = (BK * 8 + NT - 1) / NT;  // 16-byte chunks of K (and V) per thread
+  static constexpr bool EXACT = CPT * NT == BK * 8;   // every thread owns exactly CPT chunks
   uint4 kx[CPT], vx[CPT];
   int mt, md;
+  bool partial;
   int wave_s;  // this wave's index (uniform)
-  __device__ __forceinline__ void fetch(const TileSrc& ts, bool partial, int hkv, int hk, const int* tok_drop,
+  // Chunk c of a tile is 16-byte piece c % 8 of key row c / 8 (the masks tell the
+  // compiler that the key index is below 64, so its products are 24-bit).
+  __device__ __forceinline__ void fetch(const TileSrc& ts, bool part, int hkv, int hk, const int* tok_drop,
                                         const int* ver_src) {
+    partial = part;
     const int tid = local_tid(wave_s);
+    // row0's head-hk row as a uniform base; the per-thread byte offset is 32-bit
+    const long long base = ((long long)ts.row0 * hkv + hk) * D;
+    const char* kb = (const char*)(ts.k + base);
+    const char* vb = (const char*)(ts.v + base);
+    const uint32_t row_bytes = (uint32_t)hkv * (D * 2);
+    if (ts.nrows == BK) {  // uniform: a whole tile of keys
 #pragma unroll
-    for (int j = 0; j < CPT; ++j) {
-      const int c = tid + j * NT;
-      const int key = c >> 3, ch = c & 7;
-      kx[j] = make_uint4(0, 0, 0, 0);
-      vx[j] = make_uint4(0, 0, 0, 0);
-      if (c < BK * 8 && key < ts.nrows) {
-        const long long off = ((long long)(ts.row0 + key) * hkv + hk) * D + ch * 8;
-        kx[j] = *(const uint4*)(ts.k + off);
-        vx[j] = *(const uint4*)(ts.v + off);
+      for (int j = 0; j < CPT; ++j) {
+        const int c = tid + j * NT;
+        if (EXACT || c < BK * 8) {
+          const uint32_t off = __umul24((uint32_t)(c >> 3) & (BK - 1), row_bytes) + (uint32_t)(c & 7) * 16u;
+          kx[j] = *(const uint4*)(kb + off);
+          vx[j] = *(const uint4*)(vb + off);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < CPT; ++j) {
+        const int c = tid + j * NT;
+        const int key = (c >> 3) & (BK - 1);
+        kx[j] = make_uint4(0, 0, 0, 0);
+        vx[j] = make_uint4(0, 0, 0, 0);
+        if ((EXACT || c < BK * 8) && key < ts.nrows) {
+          const uint32_t off = __umul24((uint32_t)key, row_bytes) + (uint32_t)(c & 7) * 16u;
+          kx[j] = *(const uint4*)(kb + off);
+          vx[j] = *(const uint4*)(vb + off);
+        }
       }
     }
-    if (partial && tid < BK) {
+    if (part && tid < BK) {
       const int key = tid;
       mt = INT_MAX;
       md = INT_MIN;
@@ -568,13 +600,13 @@ struct TileStage {
       }
     }
   }
-  __device__ __forceinline__ void stash(uint16_t* lkb, uint16_t* lvb, int* mtok, int* mdrop, bool partial) {
+  __device__ __forceinline__ void stash(uint16_t* lkb, uint16_t* lvb, int* mtok, int* mdrop) {
     const int tid = local_tid(wave_s);
 #pragma unroll
     for (int j = 0; j < CPT; ++j) {
       const int c = tid + j * NT;
-      if (c < BK * 8) {
-        const int key = c >> 3, ch = c & 7;
+      if (EXACT || c < BK * 8) {
+        const int key = (c >> 3) & (BK - 1), ch = c & 7;
         *(uint4*)(lkb + key * KP + ch * 8) = kx[j];
         *(uint4*)(lvb + key * VP + ch * 8) = vx[j];
       }
@@ -626,7 +658,7 @@ __global__ __launch_bounds__(64 * GROUP, 2) void seg_attn_bf16(AKV_ATTN_PARAMS) 
     const int ent = tiles[t];
     const bool partial = (ent & 3) == AKV_TILE_PARTIAL;
     st.fetch(tile_src(ent, nvt, voff, r, tb, te, k, v, kver, vver), partial, hkv, hk, tok_drop, ver_src);
-    st.stash(lk, lv, mtok, mdrop, partial);
+    st.stash(lk, lv, mtok, mdrop);
     lds_barrier();
     tile_qk<false>(w, lk, nullptr, lq, lg);
     tile_softmax<false>(w, partial, mtok, mdrop, lk, nullptr, q0, lq, lg);
@@ -640,82 +672,102 @@ __global__ __launch_bounds__(64 * GROUP, 2) void seg_attn_bf16(AKV_ATTN_PARAMS) 
 // Waves 0-3 (group A) and 4-7 (group B) run the same tile loop one phase apart,
 // separated by workgroup barriers, so while one wave of a SIMD issues MFMAs
 // (PV of tile t and QK of tile t+1) its partner runs the softmax of its tile on
-// the VALU.  Each K/V tile stays in LDS for four phases, so tiles rotate through
-// three LDS slots; tile t+2 is fetched to registers at the start of iteration t
-// and written to its slot one phase later, after its previous occupant's last
-// reader has passed a barrier.
+// the VALU.  A K/V tile is read from LDS for three phases (its K and V^T in the
+// MFMA phase before its softmax, its mask in the softmax), so tiles rotate
+// through three LDS slots.  Tile t+3 is fetched to registers at the start of
+// iteration t's softmax phase and written to its slot at the start of the next
+// iteration's softmax phase: the slot then belongs to tile t, whose last reader
+// passed the barrier that closed the previous MFMA phase.  So the MFMA phase
+// issues only MFMAs and LDS reads; the staging's address arithmetic and waits
+// would otherwise stall it behind the partner wave's exp stream.  The loop is
+// unrolled over the three slots so every LDS slot address is a constant.
 //
 // SAFE = false is the fast pass (offset 0, column sums on the matrix cores);
 // SAFE = true is the lazily-rescaled softmax with per-tile range checks.
 constexpr int kPPThreads = 512;
 constexpr int kPPSlots = 3;
 
+struct PPCtx {
+  uint16_t (*lk)[BK * KP];
+  uint16_t (*lv)[BK * VP];
+  int (*mtok)[BK];
+  int (*mdrop)[BK];
+  const uint16_t* lqw;
+  const int* tiles;  // this work item's tile entries
+  const uint16_t *k, *v, *kver, *vver;
+  const int *tok_drop, *ver_src;
+  int n, nvt, voff, r, tb, te, hkv, hk, q0, lq, lg, lane;
+  __device__ __forceinline__ TileSrc src(int ent) const { return tile_src(ent, nvt, voff, r, tb, te, k, v, kver, vver); }
+  // entry of tile t, or of the last tile past the end (n >= 1; the caller ignores it)
+  __device__ __forceinline__ int entry(int t) const { return tiles[min(t, n - 1)]; }
+};
+
+// One iteration of the ping-pong loop for tile i held in LDS slot S; ent holds
+// the entries of tiles i .. i+3 and is advanced by one.
+template <bool SAFE, int S>
+__device__ __forceinline__ void pp_step(WaveState& w, f32x4 (&ls)[2], bf16x8 sel, TileStage<kPPThreads>& st,
+                                        VFrag& vf, const PPCtx& c, int i, int (&ent)[4]) {
+  constexpr int S1 = (S + 1) % kPPSlots, S2 = (S + 2) % kPPSlots;
+  // phase 1 (VALU): tile i+2 (fetched one iteration ago) goes to the slot of tile
+  // i-1, tile i+3 is fetched, then the softmax of tile i.  Its V^T fragments were
+  // read between the QK MFMAs of the previous MFMA phase.
+  if (i + 2 < c.n) st.stash(c.lk[S2], c.lv[S2], c.mtok[S2], c.mdrop[S2]);
+  if (i + 3 < c.n)
+    st.fetch(c.src(ent[3]), (ent[3] & 3) == AKV_TILE_PARTIAL, c.hkv, c.hk, c.tok_drop, c.ver_src);
+  __builtin_amdgcn_sched_barrier(0);
+  // the entry the next iteration fetches by, requested here: its scalar load is
+  // waited for only at the barrier that ends this phase
+  const int ent_next = c.entry(i + 4);
+  const bool part = (ent[0] & 3) == AKV_TILE_PARTIAL;
+  if (SAFE)
+    tile_softmax<true>(w, part, c.mtok[S], c.mdrop[S], c.lk[S], c.lqw, c.q0, c.lq, c.lg);
+  else
+    tile_softmax_fast(w, part, c.mtok[S], c.mdrop[S], c.q0, c.lq, c.lg);
+  lds_barrier();
+  // phase 2 (MFMA): PV of tile i with the K fragments of tile i+1 read between its
+  // MFMAs; QK of tile i+1 with its V^T fragments read between those MFMAs (after
+  // the last tile, slot S1 holds an older tile: its K reads are harmless and unused)
+  __builtin_amdgcn_s_setprio(1);
+  KFrag kf;
+  bf16x8 qf[2][2];
+  mfma_pv_read_k<!SAFE>(w, vf, kf, qf, ls, sel, c.lk[S1], c.lqw, c.lq, c.lg);
+  __builtin_amdgcn_sched_barrier(0);
+  // P of tile i is dead here, before the scores of tile i+1 are born: they share registers
+  if (i + 1 < c.n) mfma_qk_lq(w, kf, qf, c.lqw, c.lq, c.lg, vf, c.lv[S1], c.lane);
+  __builtin_amdgcn_s_setprio(0);
+  lds_barrier();
+  ent[0] = ent[1];
+  ent[1] = ent[2];
+  ent[2] = ent[3];
+  ent[3] = ent_next;
+}
+
 template <bool SAFE>
 __device__ __forceinline__ void pp_pipeline(WaveState& w, f32x4 (&ls)[2], bf16x8 sel, TileStage<kPPThreads>& st,
-                                            uint16_t (*lk)[BK * KP], uint16_t (*lv)[BK * VP], int (*mtok)[BK],
-                                            int (*mdrop)[BK], const uint16_t* lqw, const int* tiles, int t0, int n,
-                                            int nvt, int voff, int r, int tb, int te, const uint16_t* k,
-                                            const uint16_t* v, const uint16_t* kver, const uint16_t* vver, int hkv,
-                                            int hk, const int* tok_drop, const int* ver_src, int q0, int lq, int lg,
-                                            int lane, bool lag) {
-  constexpr int NSLOT = kPPSlots;
+                                            const PPCtx& c, bool lag) {
+  // tiles 0 and 1 staged, tile 2 fetched
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    if (j < n) {
-      const int e = tiles[t0 + j];
-      const bool pt = (e & 3) == AKV_TILE_PARTIAL;
-      st.fetch(tile_src(e, nvt, voff, r, tb, te, k, v, kver, vver), pt, hkv, hk, tok_drop, ver_src);
-      st.stash(lk[j], lv[j], mtok[j], mdrop[j], pt);
+    if (j < c.n) {
+      const int e = c.tiles[j];
+      st.fetch(c.src(e), (e & 3) == AKV_TILE_PARTIAL, c.hkv, c.hk, c.tok_drop, c.ver_src);
+      st.stash(c.lk[j], c.lv[j], c.mtok[j], c.mdrop[j]);
     }
   }
-  __syncthreads();
-  if (lag) lds_barrier();
-  tile_qk<true>(w, lk[0], lqw, lq, lg);
-  VFrag vf;
-  read_vt(vf, lv[0], lane);
+  int ent[4] = {c.entry(0), c.entry(1), c.entry(2), c.entry(3)};
+  if (c.n > 2) st.fetch(c.src(ent[2]), (ent[2] & 3) == AKV_TILE_PARTIAL, c.hkv, c.hk, c.tok_drop, c.ver_src);
   lds_barrier();
-  int slot = 0;  // slot of tile i
-  // tile entries i, i+1, i+2 in hand; entry i+3 is requested one iteration ahead
-  int ent = tiles[t0], e1 = n > 1 ? tiles[t0 + 1] : 0, e2n = n > 2 ? tiles[t0 + 2] : 0;
-  for (int i = 0; i < n; ++i) {
-    const int e3n = i + 3 < n ? tiles[t0 + i + 3] : 0;
-    const bool fetch2 = i + 2 < n;
-    const int e2 = e2n;
-    const bool p2 = (e2 & 3) == AKV_TILE_PARTIAL;
-    const int slot1 = slot == NSLOT - 1 ? 0 : slot + 1;
-    const int slot2 = slot1 == NSLOT - 1 ? 0 : slot1 + 1;
-    if (fetch2) st.fetch(tile_src(e2, nvt, voff, r, tb, te, k, v, kver, vver), p2, hkv, hk, tok_drop, ver_src);
-    // phase 1 (VALU): softmax of tile i.  Its V^T fragments were read between the QK
-    // MFMAs of the previous MFMA phase: LDS reads issued here would hold up the exp
-    // stream while the partner wave's K and Q' reads occupy the LDS.
-    __builtin_amdgcn_sched_barrier(0);
-    if (SAFE)
-      tile_softmax<true>(w, (ent & 3) == AKV_TILE_PARTIAL, mtok[slot], mdrop[slot], lk[slot], lqw, q0, lq, lg);
-    else
-      tile_softmax_fast(w, (ent & 3) == AKV_TILE_PARTIAL, mtok[slot], mdrop[slot], q0, lq, lg);
-    lds_barrier();
-    // phase 2 (MFMA): PV of tile i (the K fragments of tile i+1 are read between its
-    // MFMAs, which hide their latency); tile i+2 goes to the slot freed by tile i-1
-    // (its last reader finished before the barrier above); QK of tile i+1 with the
-    // V^T fragments of tile i+1 read between its MFMAs (both halves of that tile
-    // were stashed before the barrier above)
-    __builtin_amdgcn_s_setprio(1);
-    // (after the last tile, slot1 holds an older tile: its K reads are harmless and unused)
-    KFrag kf;
-    bf16x8 q0f[2];
-    mfma_pv_read_k<!SAFE>(w, vf, kf, q0f, ls, sel, lk[slot1], lqw, lq, lg);
-    // The stash goes ahead of QK: issued after QK's V^T reads, its LDS writes would
-    // wait behind them, and the barrier below waits for the writes.
-    if (fetch2) st.stash(lk[slot2], lv[slot2], mtok[slot2], mdrop[slot2], p2);
-    __builtin_amdgcn_sched_barrier(0);
-    // P of tile i is dead here, before the scores of tile i+1 are born: they share registers
-    if (i + 1 < n) mfma_qk_lq(w, kf, q0f, lqw, lq, lg, vf, lv[slot1], lane);
-    __builtin_amdgcn_s_setprio(0);
-    lds_barrier();
-    slot = slot1;
-    ent = e1;
-    e1 = e2n;
-    e2n = e3n;
+  if (lag) lds_barrier();
+  tile_qk<true>(w, c.lk[0], c.lqw, c.lq, c.lg);
+  VFrag vf;
+  read_vt(vf, c.lv[0], c.lane);
+  lds_barrier();
+  for (int i = 0; i < c.n; i += 3) {
+    pp_step<SAFE, 0>(w, ls, sel, st, vf, c, i, ent);
+    if (i + 1 >= c.n) break;
+    pp_step<SAFE, 1>(w, ls, sel, st, vf, c, i + 1, ent);
+    if (i + 2 >= c.n) break;
+    pp_step<SAFE, 2>(w, ls, sel, st, vf, c, i + 2, ent);
   }
   if (!lag) lds_barrier();
 }
@@ -754,8 +806,32 @@ __global__ __launch_bounds__(kPPThreads) void seg_attn_bf16_pp(AKV_ATTN_PARAMS) 
   st.wave_s = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const bf16x8 sel = colsum_selector(lane);
   f32x4 ls[2] = {};
-  pp_pipeline<false>(w, ls, sel, st, lk, lv, mtok, mdrop, lqw, tiles, t0, n, nvt, voff, r, tb, te, k, v, kver, vver,
-                     hkv, hk, tok_drop, ver_src, q0, lq, lg, lane, lag);
+  PPCtx c;
+  c.lk = lk;
+  c.lv = lv;
+  c.mtok = mtok;
+  c.mdrop = mdrop;
+  c.lqw = lqw;
+  c.tiles = tiles + t0;
+  c.k = k;
+  c.v = v;
+  c.kver = kver;
+  c.vver = vver;
+  c.tok_drop = tok_drop;
+  c.ver_src = ver_src;
+  c.n = n;
+  c.nvt = nvt;
+  c.voff = voff;
+  c.r = r;
+  c.tb = tb;
+  c.te = te;
+  c.hkv = hkv;
+  c.hk = hk;
+  c.q0 = q0;
+  c.lq = lq;
+  c.lg = lg;
+  c.lane = lane;
+  pp_pipeline<false>(w, ls, sel, st, c, lag);
   // Accept the fast pass when every real query column's sum lies in [2^-40, 2^100]
   // (also false for inf/NaN); otherwise the workgroup redoes the item with the
   // rescaling softmax.
@@ -770,8 +846,7 @@ __global__ __launch_bounds__(kPPThreads) void seg_attn_bf16_pp(AKV_ATTN_PARAMS) 
   if (__builtin_amdgcn_readfirstlane(redo)) {
     asm volatile("");  // rare: keep the second pipeline out of the common path
     load_q<false>(w, nullptr, q, q0, q0, hq, h, lq, lg, 0.f, tok_pos, rq);  // resets O, offsets and sums (Q' stays in LDS)
-    pp_pipeline<true>(w, ls, sel, st, lk, lv, mtok, mdrop, lqw, tiles, t0, n, nvt, voff, r, tb, te, k, v, kver,
-                      vver, hkv, hk, tok_drop, ver_src, q0, lq, lg, lane, lag);
+    pp_pipeline<true>(w, ls, sel, st, c, lag);
   } else {
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) w.lrun[qb] = ls[qb][0];
