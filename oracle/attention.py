@@ -28,6 +28,8 @@ values untouched) and `decode_after_ops` (decode continuing a replayed state).
 """
 from __future__ import annotations
 
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 
 from .replay import replay_tokens, replay_events
@@ -86,21 +88,43 @@ def visibility_mask(ev, e):
     return mask, key_tok, key_pos
 
 
+def _pool_map(fn, items, threads):
+    """fn over items, on a thread pool when threads > 1 (numpy releases the GIL in
+    its array kernels); results in item order."""
+    items = list(items)
+    if threads <= 1 or len(items) <= 1:
+        return [fn(x) for x in items]
+    with ThreadPoolExecutor(max_workers=min(threads, len(items))) as ex:
+        return list(ex.map(fn, items))
+
+
 def segment_attention(q_raw, k_raw, v, ops=None, ev=None, base=150000.0, layout=HALF,
-                      scale=None, rows=None, chunk=64):
+                      scale=None, rows=None, chunk=64, compact=False, threads=1):
     """Batched (restore-prefill) definition with an explicit mask per stretch.
 
     rows: optional sorted array of query token indices to compute (others are
-    left NaN).  Returns (o [T, Hq, d], lse [T, Hq]) float64."""
+    left NaN).  Returns (o [T, Hq, d], lse [T, Hq]) float64, or with compact=True
+    only the requested rows, (o [len(rows), Hq, d], lse [len(rows), Hq]).
+    threads > 1 spreads the independent (query chunk, head) products and the key
+    rotation of each stretch (in blocks of rows) over a thread pool; every element
+    is computed exactly as in the single-threaded walk."""
     if ev is None:
         ev = replay_events(ops)
     T, hq, d = q_raw.shape
     hkv = k_raw.shape[1]
     grp = hq // hkv
     scale = 1.0 / np.sqrt(d) if scale is None else scale
-    o = np.full((T, hq, d), np.nan)
-    lse = np.full((T, hq), np.nan)
-    want = np.ones(T, bool) if rows is None else np.isin(np.arange(T), rows)
+    if rows is None:
+        rows = np.arange(T)
+        compact = False
+    rows = np.asarray(rows, np.int64)
+    slot = np.full(T, -1, np.int64)           # output row of each requested token
+    slot[rows] = np.arange(rows.size) if compact else rows
+    n_out = rows.size if compact else T
+    o = np.full((n_out, hq, d), np.nan)
+    lse = np.full((n_out, hq), np.nan)
+    want = slot >= 0
+    kblk = 8192
     for e, (tb, te, src) in enumerate(ev.epochs):
         qrows = np.nonzero(want[tb:te])[0] + tb
         if qrows.size == 0:
@@ -109,17 +133,23 @@ def segment_attention(q_raw, k_raw, v, ops=None, ev=None, base=150000.0, layout=
         key_tok = np.concatenate([src, own])
         key_pos = np.concatenate([np.arange(src.size), ev.tok_pos[own]])
         key_drop = ev.tok_drop[key_tok]
-        kr = rope(np.asarray(k_raw[key_tok], np.float64), key_pos, base, layout)  # [m, hkv, d]
+        parts = _pool_map(lambda a: rope(np.asarray(k_raw[key_tok[a:a + kblk]], np.float64),
+                                         key_pos[a:a + kblk], base, layout),
+                          range(0, key_tok.size, kblk), threads)
+        kr = np.concatenate(parts)                                     # [m, hkv, d]
         vv = np.asarray(v[key_tok], np.float64)
         for c0 in range(0, qrows.size, chunk):
             qi = qrows[c0:c0 + chunk]
             qr = rope(np.asarray(q_raw[qi], np.float64), ev.tok_pos[qi], base, layout)  # [n, hq, d]
             mask = (key_tok[None, :] <= qi[:, None]) & (qi[:, None] < key_drop[None, :])
-            for h in range(hq):
+
+            def one_head(h):
                 g = h // grp
-                oo, ll = _softmax_attend(qr[:, h], kr[:, g], vv[:, g], scale, mask)
-                o[qi, h] = oo
-                lse[qi, h] = ll
+                return _softmax_attend(qr[:, h], kr[:, g], vv[:, g], scale, mask)
+
+            for h, (oo, ll) in enumerate(_pool_map(one_head, range(hq), threads)):
+                o[slot[qi], h] = oo
+                lse[slot[qi], h] = ll
     return o, lse
 
 
