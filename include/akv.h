@@ -239,11 +239,14 @@ int akv_segment_attention_rope(const akv_plan* plan, const void* dev_plan,
  * int32 (indptr[batch] = total gathered keys).  max_n: host-side bound on every
  * request's key count, in [1, 2^31); it is checked but does not shape the launch,
  * which cuts all the batch's gathered keys into equal ranges, one per CU, and merges
- * each request's partials.  A request with zero keys is an error the kernel cannot
- * report (its output is left unwritten); callers must include the new token's own
- * slot.  ws: device workspace of at least akv_decode_workspace_bytes(...) bytes
- * (about (256 + batch) * hq * 264 bytes), owned by the caller; its contents are
- * scratch.  scale <= 0 means 1/sqrt(d).  d == 64.
+ * each request's partials.  A request with zero keys (indptr[b+1] <= indptr[b])
+ * has nothing to attend to: its output rows are written as bf16 NaN and its lse
+ * entries as -inf, so the caller can detect it after the fact (the indices live on
+ * the device and are not read by the host; callers that include the new token's
+ * own slot never meet this).  ws: device workspace of at least
+ * akv_decode_workspace_bytes(...) bytes (about (256 + batch) * hq * 264 bytes),
+ * owned by the caller; its contents are scratch.  scale <= 0 means 1/sqrt(d).
+ * d == 64.
  */
 uint64_t akv_decode_workspace_bytes(int32_t batch, int32_t hq, int32_t hkv, int32_t d, int64_t max_n);
 int akv_decode_attention(const void* q, const void* k_pool, const void* v_pool,

@@ -248,7 +248,11 @@ __global__ __launch_bounds__(64) void decode_merge(const float* __restrict__ ws,
   const int lane = threadIdx.x;
   const long long P = wgs, N = indptr[batch];
   const long long rb = indptr[b], re = indptr[b + 1];
-  if (N <= 0 || re <= rb) return;  // invalid input: a request with no keys
+  if (N <= 0 || re <= rb) {  // a request with no keys: attention over nothing is undefined
+    out[((long long)b * hq + h) * D + lane] = 0x7FC0;  // bf16 quiet NaN
+    if (lse && lane == 0) lse[(long long)b * hq + h] = -INFINITY;  // log of an empty sum
+    return;
+  }
   const long long w0 = rb * P / N, w1 = (re - 1) * P / N;  // workgroups holding the first and last key
   const int cnt = (int)(w1 - w0 + 1);
   const long long stride = (long long)hkv * grp * (D + 2);

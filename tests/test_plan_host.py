@@ -161,3 +161,20 @@ def test_empty_and_degenerate():
     # drop everything then append: the new token sees only itself
     lens, drop = [5, 3], {0: [0]}
     _compare(lens, drop, [0], 4, 4)
+
+
+@pytest.mark.parametrize("cfg,parts,n_edge", [(2, 1, 32), (3, 3, 352), (4, 4, 800)])
+def test_full_size_parity_parts_cover_every_boundary_row(cfg, parts, n_edge):
+    """The parts of the full-size GPU parity check (tests/test_gpu_parity.py) cover
+    every boundary-adjacent row and every seeded row of the workload exactly once."""
+    from tests.gpu_helpers import SEEDED_ROWS, edge_rows, full_size_rows
+    tr = workload.config_trajectory(cfg)
+    plan = akv.build_visibility(akv.ops_from_messages(tr.msg_len, tr.drop, tr.reposition))
+    t, T = plan.tables(), tr.n_tokens
+    got = [full_size_rows(t, T, cfg, p, parts) for p in range(parts)]
+    edges = edge_rows(t, T)
+    seeded = np.unique(np.random.default_rng(cfg).integers(0, T, SEEDED_ROWS[cfg]))
+    assert edges.size == n_edge
+    assert np.array_equal(np.concatenate([g[1] for g in got]), edges)
+    assert np.array_equal(np.concatenate([g[2] for g in got]), seeded)
+    assert np.array_equal(np.concatenate([g[0] for g in got]), np.union1d(edges, seeded))
