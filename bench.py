@@ -7,8 +7,12 @@ One step = one pass over every stage of the path on synthetic agent inputs:
   A4  segment-batch attention (bf16 MFMA)
   A5  batched repos of 96,000 surviving keys (gathered, p -> q)
   A6  decode: 14 requests x 1 query over 32k-96k gathered active keys each
-The restore stages run on the 48k-token, 20-round trajectory with tool-response
-rolling drop (64/8 GQA heads, d = 64, bf16) unless --config picks another.
+The restore stages run on the ~300k-token, 100-round trajectory with tool-response
+rolling drop (keep 12) and a repos whenever the next position reaches the 96k
+window (7 repos stretches, 384,931 version rows; 64/8 GQA heads, d = 64, bf16,
+RoPE base 150000), the largest restore workload that fits one GPU, unless
+--config picks another.  The host builds each step's plan while the GPU runs the
+previous step, and uploads it on a copy stream into one of two device buffers.
 
 Prints one JSON line.  `value` = algorithmic attention FLOP of the restore
 (4 * d * Hq * visible pairs) per step / wall time per step (all stages included).
@@ -33,7 +37,9 @@ PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
 ATTN_SRCS = [os.path.join(ROOT, "segmented_attention_seq_amd", "csrc", f)
              for f in ("attention.hip", "internal.h", "rope_angle.h")]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "segment_attention_48k_traffic.md")
+TRAFFIC_FILES = {2: os.path.join(ROOT, "profiles", "segment_attention_48k_traffic.md"),
+                 3: os.path.join(ROOT, "profiles", "segment_attention_300k_traffic.md"),
+                 4: os.path.join(ROOT, "profiles", "segment_attention_192k_traffic.md")}
 
 
 def parse_args():
@@ -41,7 +47,7 @@ def parse_args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4],
+    ap.add_argument("--config", type=int, default=3, choices=[2, 3, 4],
                     help="restore workload: 2 = 48k/20 rounds, 3 = ~300k/100 rounds with 96k repos "
                          "window, 4 = 192k/200 rounds with repos every round")
     ap.add_argument("--hq", type=int, default=64, choices=[8, 16, 32, 64],
@@ -74,9 +80,10 @@ def attn_src_hash():
 def read_traffic(cfg):
     """HBM bytes per segment-attention launch measured with rocprofv3 counters, if
     the file was taken on this exact kernel source and workload; else None."""
-    if cfg != 2 or not os.path.exists(TRAFFIC_FILE):
+    path = TRAFFIC_FILES.get(cfg)
+    if not path or not os.path.exists(path):
         return None
-    txt = open(TRAFFIC_FILE).read()
+    txt = open(path).read()
     h = re.search(r"kernel code sha256\[:16\]:\s*([0-9a-f]{16})", txt)
     b = re.search(r"HBM bytes per launch \(scaled\):\s*([0-9.e+]+)", txt)
     if not h or not b or h.group(1) != attn_src_hash():
@@ -98,34 +105,38 @@ class _Bf16Rows:
 
 def cpu_baseline(tr, q, k, v, target_s):
     """Time the CPU oracle (as it stands) on a seeded sample of query rows of the
-    same restore workload; report its rate in the metric's unit."""
+    same restore workload; report its rate in the metric's unit.  The oracle spreads
+    its (query chunk, head) products and key rotations over a thread pool of the
+    host's cores (at most 16, the box's share); `cores` is that pool, and the
+    parallelism it reached (process CPU time over wall time) is reported with it."""
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
-        cores = os.cpu_count()
+    from threadpoolctl import threadpool_limits
+    threads = max(1, min(16, os.cpu_count() or 1))
     ops = oracle.canonical_ops(tr.msg_len, tr.drop, tr.reposition)
     ev = oracle.replay_events(ops)
     ep = ev.epoch_of_token()
     T, hq, d = q.shape
     order = np.random.default_rng(12345).permutation(T)
-    n, done, secs, flop = 64, 0, 0.0, 0.0
+    n, done, secs, cpu, flop = 64, 0, 0.0, 0.0, 0.0
     while secs < target_s and done < T:
         rows = np.sort(order[done:done + n])
-        t0 = time.perf_counter()
-        oracle.segment_attention(_Bf16Rows(q), _Bf16Rows(k), _Bf16Rows(v), ev=ev, rows=rows,
-                                 base=150000.0)
+        t0, c0 = time.perf_counter(), time.process_time()
+        with threadpool_limits(1):
+            oracle.segment_attention(_Bf16Rows(q), _Bf16Rows(k), _Bf16Rows(v), ev=ev, rows=rows,
+                                     base=150000.0, compact=True, threads=threads)
         secs += time.perf_counter() - t0
+        cpu += time.process_time() - c0
         for i in rows:   # keys row i attends to: version rows and own tokens j <= i not yet dropped
             tb, te, src = ev.epochs[ep[i]]
             nvis = int((ev.tok_drop[src] > i).sum() + (ev.tok_drop[tb:i + 1] > i).sum())
             flop += 4.0 * d * hq * nvis
         done += rows.size
         n = int(min(4 * n, max(64, n * (target_s - secs) / max(secs, 1e-3))))
-    return {"value": flop / secs / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+    return {"value": flop / secs / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "parallelism": round(cpu / secs, 2),
             "sample": f"{done} random query rows (all {hq} heads) of the restore workload, float64 "
-                      f"NumPy oracle, {secs:.1f} s"}
+                      f"NumPy oracle on a pool of {threads} threads (BLAS single-threaded inside it), "
+                      f"{secs:.1f} s wall, {cpu:.1f} s CPU"}
 
 
 def _back_to_back(ms, nbytes):
@@ -164,7 +175,6 @@ def main():
             "k_ver": torch.empty((nv, hkv, d), dtype=torch.bfloat16, device=dev),
             "v_ver": torch.empty((nv, hkv, d), dtype=torch.bfloat16, device=dev),
             "out": torch.empty_like(qd)}
-    dev_plans = [torch.empty(1 << 20, dtype=torch.uint8, device=dev) for _ in range(2)]
 
     rb = workload.repos_batch() if "repos" in only else workload.repos_batch(n_keys=64)
     nrep = rb.slots.size
@@ -205,8 +215,11 @@ def main():
 
     ev_names = ["rope", "versions", "attn", "repos", "decode"]
     stage_ms = {n: [] for n in ev_names}
-    host_ms = []
+    build_ms, upload_ms = [], []
     keep_plans = []
+    dev_plans = [torch.empty(int(plan0.info["device_bytes"]), dtype=torch.uint8, device=dev) for _ in range(2)]
+    copy_stream = torch.cuda.Stream(device=dev)     # default priority
+    plan_free = [None, None]    # per device buffer: the attention that last read it has finished
 
     def mark():
         e = torch.cuda.Event(enable_timing=True)
@@ -214,21 +227,27 @@ def main():
         return e
 
     def step(i, timed):
-        t0 = time.perf_counter()
         ev = {}
         last = None
         if "restore" in only:
+            # A1 on the host while the GPU still runs the previous step; the image goes up
+            # on the copy stream into the buffer the step before the previous one used
+            t0 = time.perf_counter()
             plan = akv.build_visibility(akv.ops_from_messages(*req_ops))
+            t1 = time.perf_counter()
             buf = dev_plans[i % 2]
-            if buf.numel() < plan.info["device_bytes"]:
-                buf = dev_plans[i % 2] = torch.empty(int(plan.info["device_bytes"]), dtype=torch.uint8,
-                                                     device=dev)
-            akv._check(akv._lib.akv_plan_upload(plan.handle, buf.data_ptr(), buf.numel(), akv._stream(dev)),
+            if plan_free[i % 2] is not None:
+                copy_stream.wait_event(plan_free[i % 2])
+            akv._check(akv._lib.akv_plan_upload(plan.handle, buf.data_ptr(), buf.numel(), copy_stream.cuda_stream),
                        "akv_plan_upload")
+            uploaded = torch.cuda.Event()
+            uploaded.record(copy_stream)
+            torch.cuda.current_stream().wait_event(uploaded)
             plan._dev[str(dev)] = buf
             keep_plans.append(plan)
             del keep_plans[:-3]      # host images stay alive until their copies ran
-            host_ms.append((time.perf_counter() - t0) * 1e3)
+            build_ms.append((t1 - t0) * 1e3)
+            upload_ms.append((time.perf_counter() - t1) * 1e3)
             # One event between consecutive stages (each record is a marker packet
             # of a few microseconds on the GPU timeline): stage k runs from mark k to
             # mark k+1.
@@ -242,6 +261,7 @@ def main():
             akv.segment_attention(plan, qd, bufs["k_rot"], vd, bufs["k_ver"], bufs["v_ver"], bufs["out"],
                                   rope_base=workload.ROPE_BASE)
             last = mark()
+            plan_free[i % 2] = last
             ev.update(rope=(m0, m1), versions=(m1, m2), attn=(m2, last))
         if "repos" in only:
             pool, out = repos_sets[i % len(repos_sets)]
@@ -297,7 +317,9 @@ def main():
     value = attn_flop / (ms_per_step * 1e-3) / 1e12 if "restore" in only else 0.0
     attn_tflops = attn_flop / (avg["attn"] * 1e-3) / 1e12 if avg["attn"] else None
     traffic = read_traffic(args.config) if hq // hkv == 8 else None   # counters were taken on 64/8
-    comps = {"host_plan_ms": float(np.mean(host_ms)) if host_ms else None}
+    comps = {"host_plan_build_ms": float(np.mean(build_ms)) if build_ms else None,
+             "host_plan_upload_ms": float(np.mean(upload_ms)) if upload_ms else None,
+             "plan_device_bytes": int(plan0.info["device_bytes"])}
     for n in ev_names:
         comps[f"{n}_ms"] = avg[n]
     if avg["repos"]:
