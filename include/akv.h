@@ -255,6 +255,24 @@ int akv_decode_attention(const void* q, const void* k_pool, const void* v_pool,
                          int dtype, void* out, float* lse, void* ws, uint64_t ws_bytes,
                          akv_stream_t stream);
 
+/* akv_decode_attention for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same kernels and results, with the workspace taken from a fixed 16 MiB scratch
+ * array the library holds on each device it runs on (found once per device on the
+ * first call there, held until the process ends).  The call allocates nothing.
+ * Every call on a device shares that device's scratch, which keeps the last
+ * call's contents (the kernels need no cleared state): calls that overlap on one
+ * device, on different streams or from different threads, race and must be
+ * serialised by the caller.  Arguments and errors as akv_decode_attention without
+ * ws / ws_bytes; AKV_EINVAL when the batch needs more than 16 MiB of scratch
+ * (akv_decode_workspace_bytes(...) > 16 MiB, i.e. (256 + batch) * hq > 63,550 for
+ * d == 64), AKV_EHIP when the scratch address cannot be found.
+ */
+int akv_decode_attention_noalloc(const void* q, const void* k_pool, const void* v_pool,
+                                 const int32_t* indptr, const int32_t* indices, int32_t batch,
+                                 int32_t hq, int32_t hkv, int32_t d, int64_t max_n, float scale,
+                                 int dtype, void* out, float* lse, akv_stream_t stream);
+
 /* ---------------------------------------------------------------------------
  * KV cache index: which rows of a request are already held, where, and at which
  * position; what has to be recomputed; which rows to give up under pressure.

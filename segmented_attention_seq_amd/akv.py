@@ -99,6 +99,8 @@ _sig("akv_segment_attention_rope", C.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _
 _sig("akv_decode_workspace_bytes", _u64, _i32, _i32, _i32, _i32, _i64)
 _sig("akv_decode_attention", C.c_int, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i64, _f32, C.c_int,
      _vp, _vp, _vp, _u64, _vp)
+_sig("akv_decode_attention_noalloc", C.c_int, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i64, _f32, C.c_int,
+     _vp, _vp, _vp)
 _sig("akv_cache_create", C.c_int, _i32, C.POINTER(_vp))
 _sig("akv_cache_destroy", None, _vp)
 _sig("akv_cache_match", C.c_int, _vp, _vp, _i64, _vp, _i64, _i32, _vp, _vp, C.POINTER(akv_cache_match_info))
@@ -111,6 +113,7 @@ EXPORTED = ["akv_status_string", "akv_last_error", "akv_version", "akv_ops_from_
             "akv_build_visibility", "akv_plan_info_get", "akv_plan_tables_get", "akv_plan_upload",
             "akv_plan_destroy", "akv_rope_repos", "akv_kv_reuse", "akv_rope_apply", "akv_build_kv_versions",
             "akv_segment_attention", "akv_segment_attention_rope", "akv_decode_workspace_bytes", "akv_decode_attention",
+            "akv_decode_attention_noalloc",
             "akv_cache_create", "akv_cache_destroy", "akv_cache_match", "akv_cache_alloc",
             "akv_cache_insert", "akv_cache_unlock", "akv_cache_stats_get"]
 
@@ -451,6 +454,27 @@ def decode_attention(q, k_pool, v_pool, indptr, indices, max_n: int, out, lse=No
     _check(_lib.akv_decode_attention(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), indptr.data_ptr(),
                                      indices.data_ptr(), B, hq, hkv, d, max_n, scale, BF16, out.data_ptr(),
                                      lp, ws.data_ptr(), nbytes, _stream(dev)), "akv_decode_attention")
+    return out
+
+
+def decode_attention_noalloc(q, k_pool, v_pool, indptr, indices, max_n: int, out, lse=None,
+                             scale: float = 0.0):
+    """decode_attention on the library's fixed per-device scratch (no workspace is
+    allocated or passed); calls on one device must not overlap."""
+    import torch
+    B, hq, d = q.shape
+    hkv = k_pool.shape[1]
+    dev = q.device
+    _req(q, "q", torch.bfloat16, device=dev)
+    _req(k_pool, "k_pool", torch.bfloat16, device=dev)
+    _req(v_pool, "v_pool", torch.bfloat16, tuple(k_pool.shape), dev)
+    _req(indptr, "indptr", torch.int32, (B + 1,), dev)
+    _req(indices, "indices", torch.int32, device=dev)
+    _req(out, "out", torch.bfloat16, (B, hq, d), dev)
+    lp = _req(lse, "lse", torch.float32, (B, hq), dev) if lse is not None else None
+    _check(_lib.akv_decode_attention_noalloc(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), indptr.data_ptr(),
+                                             indices.data_ptr(), B, hq, hkv, d, max_n, scale, BF16,
+                                             out.data_ptr(), lp, _stream(dev)), "akv_decode_attention_noalloc")
     return out
 
 

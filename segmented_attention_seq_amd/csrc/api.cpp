@@ -276,22 +276,50 @@ uint64_t akv_decode_workspace_bytes(int32_t batch, int32_t hq, int32_t hkv, int3
   return 4 * akv::decode_ws_floats(batch, hq, d);
 }
 
-int akv_decode_attention(const void* q, const void* k_pool, const void* v_pool, const int32_t* indptr,
-                         const int32_t* indices, int32_t batch, int32_t hq, int32_t hkv, int32_t d,
-                         int64_t max_n, float scale, int dtype, void* out, float* lse, void* ws,
-                         uint64_t ws_bytes, akv_stream_t stream) {
+// Argument checks shared by the two decode entry points (the workspace aside).
+static int decode_check(const void* q, const void* k_pool, const void* v_pool, const int32_t* indptr,
+                        const int32_t* indices, int32_t batch, int32_t hq, int32_t hkv, int32_t d, int64_t max_n,
+                        int dtype, const void* out) {
   if (dtype != AKV_BF16) return fail(AKV_EUNSUPPORTED, "decode attention is bf16 only");
   if (d != 64) return fail(AKV_EUNSUPPORTED, "decode attention needs d == 64");
   if (hq < 1 || hkv < 1 || hq % hkv || hq / hkv > 16)
     return fail(AKV_EUNSUPPORTED, "decode needs hq a multiple of hkv with hq/hkv <= 16");
   if (batch < 0) return fail(AKV_EINVAL, "batch < 0");
   if (batch == 0) return AKV_OK;
-  if (!q || !k_pool || !v_pool || !indptr || !indices || !out || !ws)
-    return fail(AKV_EINVAL, "NULL pointer argument");
+  if (!q || !k_pool || !v_pool || !indptr || !indices || !out) return fail(AKV_EINVAL, "NULL pointer argument");
   if (max_n < 1 || max_n > INT32_MAX) return fail(AKV_EINVAL, "max_n must be in [1, 2^31)");
+  return AKV_OK;
+}
+
+int akv_decode_attention(const void* q, const void* k_pool, const void* v_pool, const int32_t* indptr,
+                         const int32_t* indices, int32_t batch, int32_t hq, int32_t hkv, int32_t d,
+                         int64_t max_n, float scale, int dtype, void* out, float* lse, void* ws,
+                         uint64_t ws_bytes, akv_stream_t stream) {
+  int st = decode_check(q, k_pool, v_pool, indptr, indices, batch, hq, hkv, d, max_n, dtype, out);
+  if (st != AKV_OK || batch == 0) return st;
+  if (!ws) return fail(AKV_EINVAL, "NULL pointer argument");
   if (ws_bytes < 4 * akv::decode_ws_floats(batch, hq, d)) return fail(AKV_EINVAL, "decode workspace too small");
   if (!(scale > 0.0f)) scale = 1.0f / std::sqrt((float)d);
   akv::DecodeArgs a{q, k_pool, v_pool, indptr, indices, batch, hq, hkv, d, scale, out, lse, (float*)ws};
+  return akv::launch_decode(a, stream);
+}
+
+int akv_decode_attention_noalloc(const void* q, const void* k_pool, const void* v_pool, const int32_t* indptr,
+                                 const int32_t* indices, int32_t batch, int32_t hq, int32_t hkv, int32_t d,
+                                 int64_t max_n, float scale, int dtype, void* out, float* lse,
+                                 akv_stream_t stream) {
+  int st = decode_check(q, k_pool, v_pool, indptr, indices, batch, hq, hkv, d, max_n, dtype, out);
+  if (st != AKV_OK || batch == 0) return st;
+  float* ws = nullptr;
+  uint64_t cap = 0;
+  st = akv::decode_static_scratch(&ws, &cap);
+  if (st != AKV_OK) return st;
+  const uint64_t need = akv::decode_ws_floats(batch, hq, d);
+  if (need > cap)
+    return fail(AKV_EINVAL, "decode needs " + std::to_string(4 * need) + " bytes of scratch; the fixed scratch holds " +
+                                std::to_string(4 * cap));
+  if (!(scale > 0.0f)) scale = 1.0f / std::sqrt((float)d);
+  akv::DecodeArgs a{q, k_pool, v_pool, indptr, indices, batch, hq, hkv, d, scale, out, lse, ws};
   return akv::launch_decode(a, stream);
 }
 

@@ -25,6 +25,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <mutex>
 
 #include "internal.h"
 
@@ -307,7 +308,34 @@ __global__ __launch_bounds__(64) void decode_merge(const float* __restrict__ ws,
   if (lse && lane == 0) lse[(long long)b * hq + h] = M * scale + logf(L);
 }
 
+// Scratch for callers that cannot allocate (akv_decode_attention_noalloc): one
+// fixed array per device, found through hipGetSymbolAddress (in host code the
+// array's name is only a stand-in for the symbol, never a device address).
+constexpr uint64_t kStaticScratchFloats = 4ull << 20;  // 16 MiB
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) float scratch[kStaticScratchFloats];
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[kMaxDevices] = {};
+
 }  // namespace
+
+int decode_static_scratch(float** ptr, uint64_t* floats) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(AKV_EHIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(AKV_EUNSUPPORTED, "device index beyond the scratch table");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(AKV_EHIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+    g_scratch_ptr[dev] = (float*)p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  *floats = kStaticScratchFloats;
+  return AKV_OK;
+}
 
 uint64_t decode_ws_floats(int32_t batch, int32_t hq, int32_t d) {
   return ((uint64_t)kDecodeWGs + (uint64_t)batch) * hq * (uint64_t)(d + 2);

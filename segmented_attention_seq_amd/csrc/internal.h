@@ -108,5 +108,8 @@ struct DecodeArgs {
 // the at most kDecodeWGs + batch - 1 (workgroup, request) overlaps.
 uint64_t decode_ws_floats(int32_t batch, int32_t hq, int32_t d);
 int launch_decode(const DecodeArgs& a, void* stream);
+// The current device's fixed decode scratch (device address and size in floats),
+// looked up once per device; for the entry point that allocates nothing.
+int decode_static_scratch(float** ptr, uint64_t* floats);
 
 }  // namespace akv
