@@ -53,6 +53,8 @@ def parse_args():
     ap.add_argument("--hq", type=int, default=64, choices=[8, 16, 32, 64],
                     help="query heads of the restore (8 kv heads): 64 is the workloads' 64/8 GQA; "
                          "32, 16 and 8 run the 4-, 2- and 1-head-group kernel on seeded synthetic queries")
+    ap.add_argument("--fused-versions", action="store_true",
+                    help="build no version buffers: the attention rotates version rows as it stages key tiles")
     ap.add_argument("--repos-sets", type=int, default=4, help="repos buffer sets rotated per step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
@@ -171,9 +173,12 @@ def main():
     nv = int(plan0.info["n_versions"])
     pairs = int(plan0.info["visible_pairs"])
     attn_flop = 4.0 * d * hq * pairs
+    fused = args.fused_versions
+    nvb = 0 if fused else nv    # version buffers are not built with fused versions
     bufs = {"k_rot": torch.empty_like(kd),
-            "k_ver": torch.empty((nv, hkv, d), dtype=torch.bfloat16, device=dev),
-            "v_ver": torch.empty((nv, hkv, d), dtype=torch.bfloat16, device=dev),
+            "k_ver": torch.empty((nvb, hkv, d), dtype=torch.bfloat16, device=dev),
+            "v_ver": torch.empty((nvb, hkv, d), dtype=torch.bfloat16, device=dev),
+            "rot_ws": torch.empty(max(akv.rot_table_bytes(plan0, d), 4), dtype=torch.uint8, device=dev),
             "out": torch.empty_like(qd)}
 
     rb = workload.repos_batch() if "repos" in only else workload.repos_batch(n_keys=64)
@@ -255,11 +260,15 @@ def main():
             akv.rope_apply(plan, bufs["k_rot"], kd)   # queries are rotated inside the attention
             m1 = mark()
             m2 = m1
-            if nv:
+            if nv and not fused:
                 akv.build_kv_versions(plan, bufs["k_rot"], vd, bufs["k_ver"], bufs["v_ver"])
                 m2 = mark()
-            akv.segment_attention(plan, qd, bufs["k_rot"], vd, bufs["k_ver"], bufs["v_ver"], bufs["out"],
-                                  rope_base=workload.ROPE_BASE)
+            if fused:   # the run table fill and the attention
+                akv.segment_attention_fused(plan, qd, bufs["k_rot"], vd, bufs["out"], rope_base=workload.ROPE_BASE,
+                                            ws=bufs["rot_ws"])
+            else:
+                akv.segment_attention(plan, qd, bufs["k_rot"], vd, bufs["k_ver"], bufs["v_ver"], bufs["out"],
+                                      rope_base=workload.ROPE_BASE)
             last = mark()
             plan_free[i % 2] = last
             ev.update(rope=(m0, m1), versions=(m1, m2), attn=(m2, last))
@@ -316,7 +325,8 @@ def main():
 
     value = attn_flop / (ms_per_step * 1e-3) / 1e12 if "restore" in only else 0.0
     attn_tflops = attn_flop / (avg["attn"] * 1e-3) / 1e12 if avg["attn"] else None
-    traffic = read_traffic(args.config) if hq // hkv == 8 else None   # counters were taken on 64/8
+    # counters were taken on 64/8 with version buffers
+    traffic = read_traffic(args.config) if hq // hkv == 8 and not fused else None
     comps = {"host_plan_build_ms": float(np.mean(build_ms)) if build_ms else None,
              "host_plan_upload_ms": float(np.mean(upload_ms)) if upload_ms else None,
              "plan_device_bytes": int(plan0.info["device_bytes"])}
@@ -336,7 +346,7 @@ def main():
     if avg["rope"]:
         rope_bytes = 2 * kd.numel() * 2 + 4 * T
         comps["rope_apply_gbs"] = rope_bytes / (avg["rope"] * 1e-3) / 1e9
-    if avg["versions"] and nv:
+    if avg["versions"] and nv and not fused:
         comps["versions_gbs"] = (nv * hkv * d * 2 * 4 + 12 * nv) / (avg["versions"] * 1e-3) / 1e9
 
     workload_name = {2: "48k-token 20-round agent trajectory, rolling drop keep 12 (8 drops)",
@@ -350,8 +360,10 @@ def main():
                                f"+ batched repos of {nrep} keys + decode of {db.q.shape[0]} requests over "
                                f"{n_keys} gathered keys", "restore_tokens": T, "visible_pairs": pairs,
                    "attn_flop_per_step": attn_flop, "version_rows": nv,
+                   "versions": "rotated while key tiles are staged" if fused else "built into buffers",
                    "stages": sorted(only)},
-        "roofline": {"bound": "mfma", "kernel": ("segment attention (seg_attn_bf16_pp, 8 query heads per kv head)"
+        "roofline": {"bound": "mfma", "kernel": ("segment attention (seg_attn_bf16_pp, 8 query heads per kv head"
+                                                   + (", version rows rotated at staging)" if fused else ")")
                                                    if hq // hkv == 8 else
                                                    f"segment attention (seg_attn_bf16<{hq // hkv}>)"),
                      "achieved": attn_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",

@@ -128,6 +128,7 @@ typedef struct {
   int64_t n_final, p_next;
   int32_t bq, bk;
   uint64_t device_bytes;       /* size of the device image for akv_plan_upload */
+  int64_t n_runs;              /* runs of version rows that move by one shift (ver_run) */
 } akv_plan_info;
 
 typedef struct {
@@ -142,6 +143,10 @@ typedef struct {
   const int32_t* item_order;   /* [n_items] launch order: descending tile count */
   const int32_t* final_tok;    /* [n_final] */
   const int32_t* final_pos;    /* [n_final] */
+  const int32_t* ver_run;      /* [n_versions] run of each version row: a run is a maximal
+                                  stretch of consecutive version rows of one repos stretch
+                                  whose shift to_pos - from_pos is the same */
+  const int32_t* run_delta;    /* [n_runs] that shift */
 } akv_plan_tables;
 
 int  akv_plan_info_get(const akv_plan* plan, akv_plan_info* info);
@@ -230,6 +235,31 @@ int akv_segment_attention_rope(const akv_plan* plan, const void* dev_plan,
                                const void* k_ver, const void* v_ver, void* out, float* lse,
                                int dtype, int32_t hq, int32_t hkv, int32_t d, float scale,
                                double rope_base, int rope_layout, akv_stream_t stream);
+
+/* ---------------------------------------------------------------- A3 + A4 fused
+ *
+ * Segment attention that builds no version buffers: each version row's key is
+ * rotated from its source key as the attention stages its key tile, and its value
+ * row is read from the source.  Review "single-prefill restore with segment-batch
+ * attention" (§4.2, App. A.1.1): the per-segment KV versions are temporary; key
+ * rotation and value copy make them.  Version row v of a stretch is the key of
+ * source token j = ver_src[v] moved from its append position tok_pos[j] to v, i.e.
+ * rotated by the shift of its run (akv_plan_tables.ver_run / run_delta); every run's
+ * (cos, sin) per frequency is evaluated once into the workspace, with the same
+ * arithmetic as akv_build_kv_versions, so the output equals that of
+ * akv_segment_attention_rope over akv_build_kv_versions buffers bit for bit.
+ * q_raw: raw queries [T][hq][d] (rotated on load as in akv_segment_attention_rope);
+ * k: keys rotated to their append positions (akv_rope_apply); v: values.
+ * ws: caller device memory of at least akv_rot_table_bytes(plan, d) bytes (may be
+ * NULL when that is 0), overwritten.  bf16 only, d == 64, hq == 8 * hkv (other
+ * shapes: AKV_EUNSUPPORTED; use the version-buffer path).  Other errors as
+ * akv_segment_attention_rope, plus AKV_EINVAL for a short workspace.
+ */
+uint64_t akv_rot_table_bytes(const akv_plan* plan, int32_t d);
+int akv_segment_attention_fused(const akv_plan* plan, const void* dev_plan, const void* q_raw,
+                                const void* k, const void* v, void* out, float* lse, int dtype,
+                                int32_t hq, int32_t hkv, int32_t d, float scale, double rope_base,
+                                int rope_layout, void* ws, uint64_t ws_bytes, akv_stream_t stream);
 
 /* ---------------------------------------------------------------- A6: decode
  *

@@ -48,7 +48,7 @@ class akv_plan_info(C.Structure):
     _fields_ = [(n, C.c_int64) for n in ("n_tokens", "n_segments", "n_epochs", "n_versions",
                                           "n_items", "n_tiles", "n_full", "n_partial",
                                           "visible_pairs", "n_final", "p_next")] + \
-               [("bq", C.c_int32), ("bk", C.c_int32), ("device_bytes", C.c_uint64)]
+               [("bq", C.c_int32), ("bk", C.c_int32), ("device_bytes", C.c_uint64), ("n_runs", C.c_int64)]
 
 
 _P32 = C.POINTER(C.c_int32)
@@ -67,7 +67,7 @@ class akv_cache_stats(C.Structure):
 class akv_plan_tables(C.Structure):
     _fields_ = [(n, _P32) for n in ("tok_pos", "tok_drop", "segments", "epochs", "versions",
                                      "items", "tile_ptr", "tiles", "item_order", "final_tok",
-                                     "final_pos")]
+                                     "final_pos", "ver_run", "run_delta")]
 
 
 def _sig(name, res, *args):
@@ -99,6 +99,9 @@ _sig("akv_segment_attention_rope", C.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _
 _sig("akv_decode_workspace_bytes", _u64, _i32, _i32, _i32, _i32, _i64)
 _sig("akv_decode_attention", C.c_int, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i64, _f32, C.c_int,
      _vp, _vp, _vp, _u64, _vp)
+_sig("akv_rot_table_bytes", C.c_uint64, _vp, _i32)
+_sig("akv_segment_attention_fused", C.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, C.c_int, _i32, _i32, _i32, _f32,
+     C.c_double, C.c_int, _vp, _u64, _vp)
 _sig("akv_decode_attention_noalloc", C.c_int, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i64, _f32, C.c_int,
      _vp, _vp, _vp)
 _sig("akv_cache_create", C.c_int, _i32, C.POINTER(_vp))
@@ -113,7 +116,7 @@ EXPORTED = ["akv_status_string", "akv_last_error", "akv_version", "akv_ops_from_
             "akv_build_visibility", "akv_plan_info_get", "akv_plan_tables_get", "akv_plan_upload",
             "akv_plan_destroy", "akv_rope_repos", "akv_kv_reuse", "akv_rope_apply", "akv_build_kv_versions",
             "akv_segment_attention", "akv_segment_attention_rope", "akv_decode_workspace_bytes", "akv_decode_attention",
-            "akv_decode_attention_noalloc",
+            "akv_decode_attention_noalloc", "akv_rot_table_bytes", "akv_segment_attention_fused",
             "akv_cache_create", "akv_cache_destroy", "akv_cache_match", "akv_cache_alloc",
             "akv_cache_insert", "akv_cache_unlock", "akv_cache_stats_get"]
 
@@ -271,6 +274,8 @@ class Plan:
             "item_order": arr(v.item_order, i["n_items"]),
             "final_tok": arr(v.final_tok, i["n_final"]),
             "final_pos": arr(v.final_pos, i["n_final"]),
+            "ver_run": arr(v.ver_run, i["n_versions"]),
+            "run_delta": arr(v.run_delta, i["n_runs"]),
         }
         return t
 
@@ -429,6 +434,37 @@ def segment_attention(plan: Plan, q, k, v, k_ver, v_ver, out, lse=None, scale: f
     return out
 
 
+def rot_table_bytes(plan: Plan, d: int) -> int:
+    return int(_lib.akv_rot_table_bytes(plan.handle, d))
+
+
+def segment_attention_fused(plan: Plan, q_raw, k, v, out, lse=None, scale: float = 0.0,
+                            rope_base: float = 150000.0, layout: int = ROPE_HALF, ws=None):
+    """Segment attention with version rows rotated while key tiles are staged
+    (akv_segment_attention_fused): raw queries, keys rotated to their append
+    positions, values; no version buffers."""
+    import torch
+    T, hq, d = q_raw.shape
+    hkv = k.shape[1]
+    dev = q_raw.device
+    if T != plan.info["n_tokens"]:
+        raise ValueError("token count differs from the plan")
+    _req(q_raw, "q_raw", device=dev)
+    _req(k, "k", q_raw.dtype, (T, hkv, d), dev)
+    _req(v, "v", q_raw.dtype, (T, hkv, d), dev)
+    _req(out, "out", q_raw.dtype, (T, hq, d), dev)
+    lp = _req(lse, "lse", torch.float32, (T, hq), dev) if lse is not None else None
+    need = rot_table_bytes(plan, d)
+    if ws is None and need:
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    wp, wn = (None, 0) if ws is None else (_req(ws, "ws", device=dev), ws.numel() * ws.element_size())
+    _check(_lib.akv_segment_attention_fused(plan.handle, plan.upload(dev).data_ptr(), q_raw.data_ptr(), k.data_ptr(),
+                                            v.data_ptr(), out.data_ptr(), lp, _dtype_code(q_raw), hq, hkv, d,
+                                            scale, float(rope_base), layout, wp, wn, _stream(dev)),
+           "akv_segment_attention_fused")
+    return out
+
+
 def decode_workspace_bytes(batch: int, hq: int, hkv: int, d: int, max_n: int) -> int:
     return int(_lib.akv_decode_workspace_bytes(batch, hq, hkv, d, max_n))
 
@@ -479,17 +515,32 @@ def decode_attention_noalloc(q, k_pool, v_pool, indptr, indices, max_n: int, out
 
 
 def restore(plan: Plan, q_raw, k_raw, v, base: float = 150000.0, layout: int = ROPE_HALF,
-            with_lse: bool = False, scale: float = 0.0, bufs: Optional[dict] = None, fuse_q: bool = True):
+            with_lse: bool = False, scale: float = 0.0, bufs: Optional[dict] = None, fuse_q: bool = True,
+            fused_versions: bool = False):
     """Restore prefill: RoPE-apply K to its append positions, build the per-stretch
     KV versions, run segment attention, which rotates the raw queries as it loads
-    them (fuse_q=False: RoPE-apply Q into a rotated copy first).  Returns (out, lse
-    or None).  `bufs` may hold preallocated q_rot/k_rot/k_ver/v_ver/out/lse tensors."""
+    them (fuse_q=False: RoPE-apply Q into a rotated copy first).  With
+    fused_versions, no version buffers are built: the attention rotates version
+    rows as it stages key tiles.  Returns (out, lse or None).  `bufs` may hold
+    preallocated q_rot/k_rot/k_ver/v_ver/out/lse/rot_ws tensors."""
     import torch
     T, hq, d = q_raw.shape
     hkv = k_raw.shape[1]
     dev, dt = q_raw.device, q_raw.dtype
     nv = int(plan.info["n_versions"])
     b = {} if bufs is None else bufs
+    if fused_versions:
+        kr = b.get("k_rot")
+        kr = torch.empty_like(k_raw) if kr is None else kr
+        out = b.get("out")
+        out = torch.empty_like(q_raw) if out is None else out
+        lse = b.get("lse")
+        if with_lse and lse is None:
+            lse = torch.empty((T, hq), dtype=torch.float32, device=dev)
+        rope_apply(plan, kr, k_raw, base, layout)
+        segment_attention_fused(plan, q_raw, kr, v, out, lse if with_lse else None, scale, base, layout,
+                                b.get("rot_ws"))
+        return out, (lse if with_lse else None)
     qr = None
     if not fuse_q:
         qr = b.get("q_rot")

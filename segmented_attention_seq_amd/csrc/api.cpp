@@ -115,6 +115,7 @@ int akv_plan_info_get(const akv_plan* p, akv_plan_info* info) {
   info->bq = p->bq;
   info->bk = p->bk;
   info->device_bytes = p->image_bytes;
+  info->n_runs = p->n_runs;
   return AKV_OK;
 }
 
@@ -131,6 +132,8 @@ int akv_plan_tables_get(const akv_plan* p, akv_plan_tables* v) {
   v->item_order = p->item_order.data();
   v->final_tok = p->final_tok.data();
   v->final_pos = p->final_pos.data();
+  v->ver_run = p->ver_run.data();
+  v->run_delta = p->run_delta.data();
   return AKV_OK;
 }
 
@@ -216,7 +219,8 @@ namespace {
 
 int segment_attention(const akv_plan* p, const void* dev_plan, const void* q, const void* k, const void* v,
                       const void* k_ver, const void* v_ver, void* out, float* lse, int dtype, int32_t hq,
-                      int32_t hkv, int32_t d, float scale, const akv::RopeQ& rq, akv_stream_t stream) {
+                      int32_t hkv, int32_t d, float scale, const akv::RopeQ& rq, akv_stream_t stream,
+                      bool fused = false, float* rot_tab = nullptr) {
   if (!p || !dev_plan) return fail(AKV_EINVAL, "NULL plan or device plan");
   if (dtype != AKV_F32 && dtype != AKV_BF16) return fail(AKV_EINVAL, "dtype must be AKV_F32 or AKV_BF16");
   if (hq < 1 || hkv < 1 || hq % hkv) return fail(AKV_EINVAL, "hq must be a positive multiple of hkv");
@@ -232,7 +236,8 @@ int segment_attention(const akv_plan* p, const void* dev_plan, const void* q, co
   }
   if (p->T == 0) return AKV_OK;
   if (!q || !k || !v || !out) return fail(AKV_EINVAL, "NULL q, k, v or out");
-  if (!p->versions.empty() && (!k_ver || !v_ver)) return fail(AKV_EINVAL, "plan has version rows: k_ver/v_ver required");
+  if (!fused && !p->versions.empty() && (!k_ver || !v_ver))
+    return fail(AKV_EINVAL, "plan has version rows: k_ver/v_ver required");
   if (!(scale > 0.0f)) scale = 1.0f / std::sqrt((float)d);
   const auto* base = (const uint8_t*)dev_plan;
   akv::AttnArgs a{q, k, v, k_ver, v_ver, out, lse,
@@ -240,6 +245,13 @@ int segment_attention(const akv_plan* p, const void* dev_plan, const void* q, co
                   (const int32_t*)(base + p->off_order), (const int32_t*)(base + p->off_tok_drop),
                   (const int32_t*)(base + p->off_ver_src), (const int32_t*)(base + p->off_tok_pos),
                   (int64_t)p->items.size() / 2, hq, hkv, d, p->bq, p->bk, scale, dtype, rq};
+  if (fused) {
+    a.fused = true;
+    a.ver_run = (const int32_t*)(base + p->off_ver_run);
+    a.run_delta = (const int32_t*)(base + p->off_run_delta);
+    a.n_runs = p->n_runs;
+    a.rot_tab = rot_tab;
+  }
   return akv::launch_segment_attention(a, stream);
 }
 
@@ -268,6 +280,32 @@ int akv_segment_attention_rope(const akv_plan* p, const void* dev_plan, const vo
   rq.on = 1;
   rq.layout = rope_layout;
   return segment_attention(p, dev_plan, q_raw, k, v, k_ver, v_ver, out, lse, dtype, hq, hkv, d, scale, rq, stream);
+}
+
+uint64_t akv_rot_table_bytes(const akv_plan* p, int32_t d) {
+  if (!p || d < 2 || d > 128 || d % 2) return 0;
+  return (uint64_t)p->n_runs * (uint64_t)(d / 2) * 8;
+}
+
+int akv_segment_attention_fused(const akv_plan* p, const void* dev_plan, const void* q_raw, const void* k,
+                                const void* v, void* out, float* lse, int dtype, int32_t hq, int32_t hkv,
+                                int32_t d, float scale, double rope_base, int rope_layout, void* ws,
+                                uint64_t ws_bytes, akv_stream_t stream) {
+  if (!p || !dev_plan) return fail(AKV_EINVAL, "NULL plan or device plan");
+  if (!(rope_base > 1.0) || !std::isfinite(rope_base)) return fail(AKV_EINVAL, "RoPE base must be finite and > 1");
+  if (rope_layout != AKV_ROPE_HALF && rope_layout != AKV_ROPE_INTERLEAVED)
+    return fail(AKV_EINVAL, "rope_layout must be AKV_ROPE_HALF or AKV_ROPE_INTERLEAVED");
+  if (dtype != AKV_BF16 || d != 64 || hkv < 1 || hq != 8 * hkv)
+    return fail(AKV_EUNSUPPORTED, "fused version rotation needs bf16, d == 64 and hq == 8 * hkv");
+  const uint64_t need = akv_rot_table_bytes(p, d);
+  if (ws_bytes < need || (need && !ws)) return fail(AKV_EINVAL, "rotation table workspace too small");
+  akv::RopeQ rq{};
+  const double two_pi = 6.283185307179586476925286766559;
+  for (int i = 0; i < d / 2; ++i) rq.rev[i] = std::pow(rope_base, -2.0 * i / d) / two_pi;
+  rq.on = 1;
+  rq.layout = rope_layout;
+  return segment_attention(p, dev_plan, q_raw, k, v, nullptr, nullptr, out, lse, dtype, hq, hkv, d, scale, rq,
+                           stream, true, (float*)ws);
 }
 
 uint64_t akv_decode_workspace_bytes(int32_t batch, int32_t hq, int32_t hkv, int32_t d, int64_t max_n) {

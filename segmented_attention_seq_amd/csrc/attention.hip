@@ -84,6 +84,7 @@ __device__ __forceinline__ float xhalf_sum(float x) {
 // knows the LDS and scalar-memory counters are drained here (a wait hidden in
 // inline asm made it re-wait for reads issued after the barrier).
 constexpr int kWaitLgkm0 = 0xC07F;  // s_waitcnt lgkmcnt(0), vmcnt and expcnt unconstrained
+constexpr int kWaitVm0 = 0x0F70;    // s_waitcnt vmcnt(0), expcnt and lgkmcnt unconstrained
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_sched_barrier(0);
   __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
@@ -451,8 +452,8 @@ __device__ __forceinline__ void load_q(WaveState& w, uint16_t* lqw, const uint16
             float c, s;
             rope_angle_cs(pos, rq.rev[ds * 16 + lg * 8 + j], c, s);
             const float a = f[ds][j], bb = f[ds + 2][j];
-            f[ds][j] = a * c - bb * s;
-            f[ds + 2][j] = a * s + bb * c;
+            f[ds][j] = rot_first(a, bb, c, s);
+            f[ds + 2][j] = rot_second(a, bb, c, s);
           }
       } else {
 #pragma unroll
@@ -462,8 +463,8 @@ __device__ __forceinline__ void load_q(WaveState& w, uint16_t* lqw, const uint16
             float c, s;
             rope_angle_cs(pos, rq.rev[ds * 8 + lg * 4 + m], c, s);
             const float a = f[ds][2 * m], bb = f[ds][2 * m + 1];
-            f[ds][2 * m] = a * c - bb * s;
-            f[ds][2 * m + 1] = a * s + bb * c;
+            f[ds][2 * m] = rot_first(a, bb, c, s);
+            f[ds][2 * m + 1] = rot_second(a, bb, c, s);
           }
       }
     }
@@ -547,20 +548,116 @@ __device__ __forceinline__ int local_tid(int wave_s) {
 
 // Cooperative global -> register -> LDS staging of one K/V tile and its mask metadata.
 // The tile's PARTIAL flag travels with the fetched registers to the stash.
-template <int NT>
+//
+// With ROT, version rows are not read from version buffers: row v of a stretch is
+// the key of its source token ver_src[v] (rotated to its append position) turned
+// by the shift of its run, v - tok_pos[src], whose (cos, sin) per frequency come
+// from the run table rot; the value row is the source's, unchanged.  Thread tid
+// owns key tid / 8 and its four pairs 4p .. 4p+3 (p = tid % 8): in the half layout
+// the 8-byte pieces at elements 4p and 32 + 4p, in the interleaved one the 16 bytes
+// at element 8p.  The key's (source, run) are loaded ahead of the tile (load_idx),
+// the rows with the tile (fetch), the four (cos, sin) pairs of its run ahead of the
+// stash (load_rot), and the key is rotated as it is written to LDS (stash), with the
+// same arithmetic as the version builder.
+template <int NT, bool ROT = false>
 struct TileStage {
   static constexpr int CPT = (BK * 8 + NT - 1) / NT;  // 16-byte chunks of K (and V) per thread
   static constexpr bool EXACT = CPT * NT == BK * 8;   // every thread owns exactly CPT chunks
+  static_assert(!ROT || CPT == 1, "rotated staging needs one chunk per thread");
   uint4 kx[CPT], vx[CPT];
   int mt, md;
   bool partial;
   int wave_s;  // this wave's index (uniform)
+  // ROT only
+  bool rot;        // the fetched tile holds version rows
+  int isrc, irun;  // source row and run of the thread's key in the next version tile
+  int srun;        // run of the thread's key in the fetched tile (-1: past the tile's rows)
+  int mrow0, mnrows;  // the fetched tile's first row and row count (uniform), for its mask
+  int layout;      // AKV_ROPE_HALF or AKV_ROPE_INTERLEAVED
+  float* rl;       // this wave's 2.5 KB of LDS: (cos, sin) of its lanes' pairs, then their (source, run)
+
+  // With ROT the mask metadata of a PARTIAL tile is loaded just before the tile's
+  // stash rather than with its rows, so it holds no registers across the MFMA
+  // phase and the softmax in between (PARTIAL tiles are rare; their loads wait).
+  __device__ __forceinline__ void load_mask(const int* tok_drop, const int* ver_src) {
+    if (!ROT || !partial) return;
+    const int tid = local_tid(wave_s);
+    if (tid < BK) {
+      mt = INT_MAX;
+      md = INT_MIN;
+      if (tid < mnrows) {
+        mt = rot ? -1 : mrow0 + tid;
+        md = tok_drop[rot ? ver_src[mrow0 + tid] : mrow0 + tid];
+      }
+    }
+  }
+
+  // The (cos, sin) of the four pairs of the thread's key in the fetched version
+  // tile, requested ahead of its stash and copied by the memory pipe straight into
+  // the wave's LDS region (lane l's 32 bytes at l * 16 and 1024 + l * 16), so they
+  // hold no registers in between.  A key past the tile's rows reads run 0: its
+  // staged row is zero and stays zero.
+  __device__ __forceinline__ void load_rot(const float* rot_tab) {
+    if (!ROT || !rot) return;
+    const int pp = local_tid(wave_s) & 7;
+    const float* t = rot_tab + ((long long)(srun > 0 ? srun : 0) * (D / 2) + 4 * pp) * 2;
+    typedef __attribute__((address_space(3))) void lds_void;
+    __builtin_amdgcn_global_load_lds((const void*)t, (lds_void*)rl, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void*)(t + 4), (lds_void*)(rl + 256), 16, 0, 0);
+  }
+
+  // (source, run) of this thread's key in a version tile, requested ahead of the
+  // tile's fetch and copied by the memory pipe into the wave's LDS (lane l's at
+  // 2048 + 4 l and 2304 + 4 l bytes), so they hold no registers across the softmax.
+  __device__ __forceinline__ void load_idx(const TileSrc& ts, const int* ver_src, const int* ver_run) {
+    if (!ROT || !ts.ver) return;
+    const int key = (local_tid(wave_s) >> 3) & (BK - 1);
+    const int row = ts.row0 + (key < ts.nrows ? key : ts.nrows - 1);
+    typedef __attribute__((address_space(3))) void lds_void;
+    __builtin_amdgcn_global_load_lds((const void*)(ver_src + row), (lds_void*)(rl + 512), 4, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void*)(ver_run + row), (lds_void*)(rl + 576), 4, 0, 0);
+  }
+  // The (source, run) copied by load_idx, into registers for the fetch.
+  __device__ __forceinline__ void read_idx() {
+    const int lane = local_tid(wave_s) & 63;
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    isrc = ((const int*)rl)[512 + lane];
+    irun = ((const int*)rl)[576 + lane];
+  }
+
   // Chunk c of a tile is 16-byte piece c % 8 of key row c / 8 (the masks tell the
   // compiler that the key index is below 64, so its products are 24-bit).
   __device__ __forceinline__ void fetch(const TileSrc& ts, bool part, int hkv, int hk, const int* tok_drop,
                                         const int* ver_src) {
     partial = part;
     const int tid = local_tid(wave_s);
+    if (ROT && ts.ver) {
+      rot = true;
+      read_idx();
+      const int key = (tid >> 3) & (BK - 1), pp = tid & 7;
+      kx[0] = make_uint4(0, 0, 0, 0);
+      vx[0] = make_uint4(0, 0, 0, 0);
+      srun = key < ts.nrows ? irun : -1;
+      if (key < ts.nrows) {
+        const uint16_t* kr = ts.k + ((long long)isrc * hkv + hk) * D;
+        const uint16_t* vr = ts.v + ((long long)isrc * hkv + hk) * D;
+        if (layout == AKV_ROPE_HALF) {
+          const uint2 lo = *(const uint2*)(kr + 4 * pp), hi = *(const uint2*)(kr + D / 2 + 4 * pp);
+          kx[0] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        } else {
+          kx[0] = *(const uint4*)(kr + 8 * pp);
+        }
+        vx[0] = *(const uint4*)(vr + 8 * pp);
+      }
+      mrow0 = ts.row0;
+      mnrows = ts.nrows;
+      return;
+    }
+    if (ROT) {
+      rot = false;
+      mrow0 = ts.row0;
+      mnrows = ts.nrows;
+    }
     // row0's head-hk row as a uniform base; the per-thread byte offset is 32-bit
     const long long base = ((long long)ts.row0 * hkv + hk) * D;
     const char* kb = (const char*)(ts.k + base);
@@ -590,7 +687,7 @@ struct TileStage {
         }
       }
     }
-    if (part && tid < BK) {
+    if (!ROT && part && tid < BK) {
       const int key = tid;
       mt = INT_MAX;
       md = INT_MIN;
@@ -602,13 +699,43 @@ struct TileStage {
   }
   __device__ __forceinline__ void stash(uint16_t* lkb, uint16_t* lvb, int* mtok, int* mdrop) {
     const int tid = local_tid(wave_s);
+    if (ROT && rot) {
+      const int key = (tid >> 3) & (BK - 1), pp = tid & 7, lane = tid & 63;
+      // the copies into LDS (load_rot) count as vector-memory loads of this wave
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      const float4 r0 = *(const float4*)(rl + 4 * lane), r1 = *(const float4*)(rl + 256 + 4 * lane);
+      const float cs[4] = {r0.x, r0.z, r1.x, r1.z}, sn[4] = {r0.y, r0.w, r1.y, r1.w};
+      const bf16x8 x = __builtin_bit_cast(bf16x8, kx[0]);
+      bf16x8 y;
+      if (layout == AKV_ROPE_HALF) {  // x[i] and x[4 + i] are the two members of pair 4p + i
 #pragma unroll
-    for (int j = 0; j < CPT; ++j) {
-      const int c = tid + j * NT;
-      if (EXACT || c < BK * 8) {
-        const int key = (c >> 3) & (BK - 1), ch = c & 7;
-        *(uint4*)(lkb + key * KP + ch * 8) = kx[j];
-        *(uint4*)(lvb + key * VP + ch * 8) = vx[j];
+        for (int i = 0; i < 4; ++i) {
+          const float a = (float)x[i], b = (float)x[4 + i];
+          y[i] = (__bf16)rot_first(a, b, cs[i], sn[i]);
+          y[4 + i] = (__bf16)rot_second(a, b, cs[i], sn[i]);
+        }
+        const uint4 u = __builtin_bit_cast(uint4, y);
+        *(uint2*)(lkb + key * KP + 4 * pp) = make_uint2(u.x, u.y);
+        *(uint2*)(lkb + key * KP + D / 2 + 4 * pp) = make_uint2(u.z, u.w);
+      } else {  // x[2i], x[2i+1] are pair 4p + i
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float a = (float)x[2 * i], b = (float)x[2 * i + 1];
+          y[2 * i] = (__bf16)rot_first(a, b, cs[i], sn[i]);
+          y[2 * i + 1] = (__bf16)rot_second(a, b, cs[i], sn[i]);
+        }
+        *(bf16x8*)(lkb + key * KP + 8 * pp) = y;
+      }
+      *(uint4*)(lvb + key * VP + 8 * pp) = vx[0];
+    } else {
+#pragma unroll
+      for (int j = 0; j < CPT; ++j) {
+        const int c = tid + j * NT;
+        if (EXACT || c < BK * 8) {
+          const int key = (c >> 3) & (BK - 1), ch = c & 7;
+          *(uint4*)(lkb + key * KP + ch * 8) = kx[j];
+          *(uint4*)(lvb + key * VP + ch * 8) = vx[j];
+        }
       }
     }
     if (partial && tid < BK) {
@@ -696,6 +823,8 @@ struct PPCtx {
   const int* tiles;  // this work item's tile entries
   const uint16_t *k, *v, *kver, *vver;
   const int *tok_drop, *ver_src;
+  const int* ver_run;   // rotated staging: run of each version row
+  const float* rot_tab; // rotated staging: (cos, sin) per run and frequency
   int n, nvt, voff, r, tb, te, hkv, hk, q0, lq, lg, lane;
   __device__ __forceinline__ TileSrc src(int ent) const { return tile_src(ent, nvt, voff, r, tb, te, k, v, kver, vver); }
   // entry of tile t, or of the last tile past the end (n >= 1; the caller ignores it)
@@ -704,18 +833,26 @@ struct PPCtx {
 
 // One iteration of the ping-pong loop for tile i held in LDS slot S; ent holds
 // the entries of tiles i .. i+3 and is advanced by one.
-template <bool SAFE, int S>
-__device__ __forceinline__ void pp_step(WaveState& w, f32x4 (&ls)[2], bf16x8 sel, TileStage<kPPThreads>& st,
+template <bool SAFE, int S, bool ROT>
+__device__ __forceinline__ void pp_step(WaveState& w, f32x4 (&ls)[2], bf16x8 sel, TileStage<kPPThreads, ROT>& st,
                                         VFrag& vf, const PPCtx& c, int i, int (&ent)[4]) {
   constexpr int S1 = (S + 1) % kPPSlots, S2 = (S + 2) % kPPSlots;
   // phase 1 (VALU): tile i+2 (fetched one iteration ago) goes to the slot of tile
-  // i-1, tile i+3 is fetched, then the softmax of tile i.  Its V^T fragments were
-  // read between the QK MFMAs of the previous MFMA phase.
-  if (i + 2 < c.n) st.stash(c.lk[S2], c.lv[S2], c.mtok[S2], c.mdrop[S2]);
-  if (i + 3 < c.n)
-    st.fetch(c.src(ent[3]), (ent[3] & 3) == AKV_TILE_PARTIAL, c.hkv, c.hk, c.tok_drop, c.ver_src);
+  // i-1, tile i+3 is fetched, and the softmax of tile i runs.  Its V^T fragments
+  // were read between the QK MFMAs of the previous MFMA phase.  Without ROT the
+  // stash and fetch come first; with ROT the tile's (cos, sin) and the next tile's
+  // source rows are requested first, and the stash (which rotates) and the fetch
+  // (which gathers by those rows) come after the softmax, so that neither the
+  // rotation values nor the rows cross the MFMA phase in registers.
+  if (!ROT) {
+    if (i + 2 < c.n) st.stash(c.lk[S2], c.lv[S2], c.mtok[S2], c.mdrop[S2]);
+    if (i + 3 < c.n) st.fetch(c.src(ent[3]), (ent[3] & 3) == AKV_TILE_PARTIAL, c.hkv, c.hk, c.tok_drop, c.ver_src);
+  } else {
+    if (i + 2 < c.n) st.load_rot(c.rot_tab);
+    if (i + 3 < c.n) st.load_idx(c.src(ent[3]), c.ver_src, c.ver_run);
+  }
   __builtin_amdgcn_sched_barrier(0);
-  // the entry the next iteration fetches by, requested here: its scalar load is
+  // the entry the next iteration loads by, requested here: its scalar load is
   // waited for only at the barrier that ends this phase
   const int ent_next = c.entry(i + 4);
   const bool part = (ent[0] & 3) == AKV_TILE_PARTIAL;
@@ -723,6 +860,14 @@ __device__ __forceinline__ void pp_step(WaveState& w, f32x4 (&ls)[2], bf16x8 sel
     tile_softmax<true>(w, part, c.mtok[S], c.mdrop[S], c.lk[S], c.lqw, c.q0, c.lq, c.lg);
   else
     tile_softmax_fast(w, part, c.mtok[S], c.mdrop[S], c.q0, c.lq, c.lg);
+  if (ROT) {
+    __builtin_amdgcn_sched_barrier(0);
+    if (i + 2 < c.n) {
+      st.load_mask(c.tok_drop, c.ver_src);   // PARTIAL tiles only (rare): its wait is short-lived
+      st.stash(c.lk[S2], c.lv[S2], c.mtok[S2], c.mdrop[S2]);
+    }
+    if (i + 3 < c.n) st.fetch(c.src(ent[3]), (ent[3] & 3) == AKV_TILE_PARTIAL, c.hkv, c.hk, c.tok_drop, c.ver_src);
+  }
   lds_barrier();
   // phase 2 (MFMA): PV of tile i with the K fragments of tile i+1 read between its
   // MFMAs; QK of tile i+1 with its V^T fragments read between those MFMAs (after
@@ -742,20 +887,26 @@ __device__ __forceinline__ void pp_step(WaveState& w, f32x4 (&ls)[2], bf16x8 sel
   ent[3] = ent_next;
 }
 
-template <bool SAFE>
-__device__ __forceinline__ void pp_pipeline(WaveState& w, f32x4 (&ls)[2], bf16x8 sel, TileStage<kPPThreads>& st,
-                                            const PPCtx& c, bool lag) {
+template <bool SAFE, bool ROT>
+__device__ __forceinline__ void pp_pipeline(WaveState& w, f32x4 (&ls)[2], bf16x8 sel,
+                                            TileStage<kPPThreads, ROT>& st, const PPCtx& c, bool lag) {
   // tiles 0 and 1 staged, tile 2 fetched
+  int ent[4] = {c.entry(0), c.entry(1), c.entry(2), c.entry(3)};
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     if (j < c.n) {
-      const int e = c.tiles[j];
-      st.fetch(c.src(e), (e & 3) == AKV_TILE_PARTIAL, c.hkv, c.hk, c.tok_drop, c.ver_src);
+      const TileSrc ts = c.src(ent[j]);
+      st.load_idx(ts, c.ver_src, c.ver_run);
+      st.fetch(ts, (ent[j] & 3) == AKV_TILE_PARTIAL, c.hkv, c.hk, c.tok_drop, c.ver_src);
+      st.load_rot(c.rot_tab);
+      st.load_mask(c.tok_drop, c.ver_src);
       st.stash(c.lk[j], c.lv[j], c.mtok[j], c.mdrop[j]);
     }
   }
-  int ent[4] = {c.entry(0), c.entry(1), c.entry(2), c.entry(3)};
-  if (c.n > 2) st.fetch(c.src(ent[2]), (ent[2] & 3) == AKV_TILE_PARTIAL, c.hkv, c.hk, c.tok_drop, c.ver_src);
+  if (c.n > 2) {
+    st.load_idx(c.src(ent[2]), c.ver_src, c.ver_run);
+    st.fetch(c.src(ent[2]), (ent[2] & 3) == AKV_TILE_PARTIAL, c.hkv, c.hk, c.tok_drop, c.ver_src);
+  }
   lds_barrier();
   if (lag) lds_barrier();
   tile_qk<true>(w, c.lk[0], c.lqw, c.lq, c.lg);
@@ -763,11 +914,11 @@ __device__ __forceinline__ void pp_pipeline(WaveState& w, f32x4 (&ls)[2], bf16x8
   read_vt(vf, c.lv[0], c.lane);
   lds_barrier();
   for (int i = 0; i < c.n; i += 3) {
-    pp_step<SAFE, 0>(w, ls, sel, st, vf, c, i, ent);
+    pp_step<SAFE, 0, ROT>(w, ls, sel, st, vf, c, i, ent);
     if (i + 1 >= c.n) break;
-    pp_step<SAFE, 1>(w, ls, sel, st, vf, c, i + 1, ent);
+    pp_step<SAFE, 1, ROT>(w, ls, sel, st, vf, c, i + 1, ent);
     if (i + 2 >= c.n) break;
-    pp_step<SAFE, 2>(w, ls, sel, st, vf, c, i + 2, ent);
+    pp_step<SAFE, 2, ROT>(w, ls, sel, st, vf, c, i + 2, ent);
   }
   if (!lag) lds_barrier();
 }
@@ -776,12 +927,17 @@ __device__ __forceinline__ void pp_pipeline(WaveState& w, f32x4 (&ls)[2], bf16x8
 // product and accumulation of the PV step far from overflow.
 constexpr float kFastHi = 1.2676506002282294e30f;  // 2^100
 
-__global__ __launch_bounds__(kPPThreads) void seg_attn_bf16_pp(AKV_ATTN_PARAMS) {
+// ROT: version rows are rotated from the source keys while tiles are staged
+// (TileStage), with ver_run / rot_tab, instead of read from version buffers.
+template <bool ROT>
+__global__ __launch_bounds__(kPPThreads) void seg_attn_bf16_pp(AKV_ATTN_PARAMS, const int* __restrict__ ver_run,
+                                                               const float* __restrict__ rot_tab) {
   constexpr int GROUP = 8;
   __shared__ __attribute__((aligned(16))) uint16_t lk[kPPSlots][BK * KP];
   __shared__ __attribute__((aligned(16))) uint16_t lv[kPPSlots][BK * VP];
   __shared__ int mtok[kPPSlots][BK], mdrop[kPPSlots][BK];
   __shared__ __attribute__((aligned(16))) uint16_t lqs[GROUP][64 * KP];
+  __shared__ __attribute__((aligned(16))) float rtab[ROT ? GROUP * 640 : 4];  // ROT: 2.5 KB per wave
   __shared__ int redo;
 
   const int hk = blockIdx.x % hkv;
@@ -802,8 +958,10 @@ __global__ __launch_bounds__(kPPThreads) void seg_attn_bf16_pp(AKV_ATTN_PARAMS) 
 
   WaveState w;
   load_q<true>(w, lqw, q, q0, q1, hq, h, lq, lg, sl2, tok_pos, rq);
-  TileStage<kPPThreads> st;
+  TileStage<kPPThreads, ROT> st;
   st.wave_s = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  st.layout = rq.layout;
+  st.rl = rtab + (ROT ? st.wave_s * 640 : 0);
   const bf16x8 sel = colsum_selector(lane);
   f32x4 ls[2] = {};
   PPCtx c;
@@ -815,10 +973,12 @@ __global__ __launch_bounds__(kPPThreads) void seg_attn_bf16_pp(AKV_ATTN_PARAMS) 
   c.tiles = tiles + t0;
   c.k = k;
   c.v = v;
-  c.kver = kver;
-  c.vver = vver;
+  c.kver = ROT ? k : kver;   // rotated staging gathers version rows from the source keys
+  c.vver = ROT ? v : vver;
   c.tok_drop = tok_drop;
   c.ver_src = ver_src;
+  c.ver_run = ver_run;
+  c.rot_tab = rot_tab;
   c.n = n;
   c.nvt = nvt;
   c.voff = voff;
@@ -831,7 +991,7 @@ __global__ __launch_bounds__(kPPThreads) void seg_attn_bf16_pp(AKV_ATTN_PARAMS) 
   c.lq = lq;
   c.lg = lg;
   c.lane = lane;
-  pp_pipeline<false>(w, ls, sel, st, c, lag);
+  pp_pipeline<false, ROT>(w, ls, sel, st, c, lag);
   // Accept the fast pass when every real query column's sum lies in [2^-40, 2^100]
   // (also false for inf/NaN); otherwise the workgroup redoes the item with the
   // rescaling softmax.
@@ -846,12 +1006,27 @@ __global__ __launch_bounds__(kPPThreads) void seg_attn_bf16_pp(AKV_ATTN_PARAMS) 
   if (__builtin_amdgcn_readfirstlane(redo)) {
     asm volatile("");  // rare: keep the second pipeline out of the common path
     load_q<false>(w, nullptr, q, q0, q0, hq, h, lq, lg, 0.f, tok_pos, rq);  // resets O, offsets and sums (Q' stays in LDS)
-    pp_pipeline<true>(w, ls, sel, st, c, lag);
+    pp_pipeline<true, ROT>(w, ls, sel, st, c, lag);
   } else {
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) w.lrun[qb] = ls[qb][0];
   }
   store_out<true>(w, out, lse, q0, q1, hq, h, lq, lg, lqw, lane);
+}
+
+// (cos, sin) of every version run's shift for every frequency: table[run][i] =
+// (cos, sin)(delta_run * theta_i), evaluated as in the RoPE kernels (rope_angle.h),
+// so a key rotated at staging time equals its version-buffer copy bit for bit.
+__global__ __launch_bounds__(256) void rot_table_kernel(const int* __restrict__ run_delta, long long n_runs,
+                                                        int half, RopeQ rq, float* __restrict__ table) {
+  const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (t >= n_runs * half) return;
+  const long long run = t / half;
+  const int i = (int)(t - run * half);
+  float c, s;
+  rope_angle_cs((double)run_delta[run], rq.rev[i], c, s);
+  table[2 * t] = c;
+  table[2 * t + 1] = s;
 }
 
 // float32 path: one thread per (query token, head), keys walked one at a time
@@ -884,8 +1059,8 @@ __global__ __launch_bounds__(256) void seg_attn_f32(
       rope_angle_cs(pos, rq.rev[i], c, s);
       const int ia = rq.layout == AKV_ROPE_HALF ? i : 2 * i, ib = rq.layout == AKV_ROPE_HALF ? i + DD / 2 : 2 * i + 1;
       const float a = qv[ia], b = qv[ib];
-      qv[ia] = a * c - b * s;
-      qv[ib] = a * s + b * c;
+      qv[ia] = rot_first(a, b, c, s);
+      qv[ib] = rot_second(a, b, c, s);
     }
   }
   float m = -INFINITY, l = 0.f;
@@ -946,10 +1121,23 @@ int launch_segment_attention(const AttnArgs& a, void* stream) {
       case 2: AKV_LAUNCH_BF16(2); break;
       case 4: AKV_LAUNCH_BF16(4); break;
       case 8:
-        hipLaunchKernelGGL(seg_attn_bf16_pp, dim3((unsigned)blocks), dim3(512), 0, s, (const uint16_t*)a.q,
-                           (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.k_ver,
-                           (const uint16_t*)a.v_ver, a.item_desc, a.tiles, a.order, a.tok_drop, a.ver_src,
-                           (uint16_t*)a.out, a.lse, a.hq, a.hkv, a.scale, a.tok_pos, a.rq);
+        if (a.fused) {
+          if (a.n_runs > 0) {
+            const long long n = a.n_runs * (a.d / 2);
+            hipLaunchKernelGGL(rot_table_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a.run_delta,
+                               a.n_runs, a.d / 2, a.rq, a.rot_tab);
+          }
+          hipLaunchKernelGGL(seg_attn_bf16_pp<true>, dim3((unsigned)blocks), dim3(512), 0, s, (const uint16_t*)a.q,
+                             (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.k_ver,
+                             (const uint16_t*)a.v_ver, a.item_desc, a.tiles, a.order, a.tok_drop, a.ver_src,
+                             (uint16_t*)a.out, a.lse, a.hq, a.hkv, a.scale, a.tok_pos, a.rq, a.ver_run,
+                             (const float*)a.rot_tab);
+        } else {
+          hipLaunchKernelGGL(seg_attn_bf16_pp<false>, dim3((unsigned)blocks), dim3(512), 0, s, (const uint16_t*)a.q,
+                             (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.k_ver,
+                             (const uint16_t*)a.v_ver, a.item_desc, a.tiles, a.order, a.tok_drop, a.ver_src,
+                             (uint16_t*)a.out, a.lse, a.hq, a.hkv, a.scale, a.tok_pos, a.rq, nullptr, nullptr);
+        }
         break;
       default:
         return fail(AKV_EUNSUPPORTED, "bf16 segment attention needs hq/hkv in {1, 2, 4, 8}");

@@ -29,17 +29,19 @@ struct akv_plan {
   I32Vec segments;    // 3 per segment
   I32Vec epochs;      // 4 per stretch
   I32Vec versions;    // 3 per version row
+  I32Vec ver_run;     // run of each version row (rows of a run move by one shift)
+  I32Vec run_delta;   // the shift (row index - append position) of each run
   I32Vec items;       // 2 per item
   I32Vec tile_ptr;    // n_items + 1
   I32Vec tiles;       // k_tile * 4 + class
   I32Vec item_order;
   I32Vec final_tok, final_pos;
-  int64_t visible_pairs = 0, p_next = 0, n_full = 0, n_partial = 0;
+  int64_t visible_pairs = 0, p_next = 0, n_full = 0, n_partial = 0, n_runs = 0;
   // device image: contiguous int32 arrays at 256-byte aligned offsets
   std::unique_ptr<uint8_t[]> image;
   uint64_t image_bytes = 0;
-  uint64_t off_tok_pos = 0, off_tok_drop = 0, off_ver_src = 0, off_ver_to = 0, off_item_desc = 0,
-           off_tiles = 0, off_order = 0;
+  uint64_t off_tok_pos = 0, off_tok_drop = 0, off_ver_src = 0, off_ver_to = 0, off_ver_run = 0,
+           off_run_delta = 0, off_item_desc = 0, off_tiles = 0, off_order = 0;
 };
 
 namespace akv {
@@ -88,6 +90,15 @@ struct AttnArgs {
   float scale;
   int dtype;
   RopeQ rq;
+  // Version rows rotated at staging time (no version buffers): the plan's run of
+  // each version row and shift of each run, and a table of n_runs * d/2 (cos, sin)
+  // pairs that the launch fills first (nullptr when the plan has no runs); without
+  // `fused` the attention reads k_ver / v_ver.
+  bool fused = false;
+  const int32_t* ver_run = nullptr;
+  const int32_t* run_delta = nullptr;
+  int64_t n_runs = 0;
+  float* rot_tab = nullptr;
 };
 int launch_segment_attention(const AttnArgs& a, void* stream);
 

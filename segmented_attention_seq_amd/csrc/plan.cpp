@@ -296,25 +296,7 @@ int build_plan(const akv_op* ops, int64_t n_ops, int32_t bq, int32_t bk, akv_pla
     if (n_tiles > INT32_MAX) throw std::length_error("too many tiles");
     p->n_partial = n_tiles - p->n_full;
 
-    // Device image layout.  Version rows carry only (src, to); kernels read the
-    // source's append position and drop boundary through tok_pos / tok_drop.
-    uint64_t off = 0;
-    auto place = [&](uint64_t bytes) { uint64_t o = off; off += (bytes + 255) & ~uint64_t(255); return o; };
-    p->off_tok_pos = place(4 * T);
-    p->off_tok_drop = place(4 * T);
-    p->off_ver_src = place(4 * ver_total);
-    p->off_ver_to = place(4 * ver_total);
-    p->off_item_desc = place(4 * (uint64_t)n_items * ID_WORDS);
-    p->off_tiles = place(4 * (uint64_t)n_tiles);
-    p->off_order = place(4 * (uint64_t)n_items);
-    p->image_bytes = std::max<uint64_t>(off, 256);
-    p->image.reset(new uint8_t[p->image_bytes]);   // padding between arrays is never read
-    int32_t* img_src = (int32_t*)(p->image.get() + p->off_ver_src);
-    int32_t* img_to = (int32_t*)(p->image.get() + p->off_ver_to);
-    int32_t* img_desc = (int32_t*)(p->image.get() + p->off_item_desc);
-    int32_t* img_tiles = (int32_t*)(p->image.get() + p->off_tiles);
-
-    // T5 version rows (src, its append position, row index) and their image columns.
+    // T5 version rows (src, its append position, row index).
     p->versions.resize(3 * ver_total);
     par_for(ver_total, 4096, [&](int64_t lo, int64_t hi) {
       int64_t e = stretch_of(vrow, lo);
@@ -327,12 +309,70 @@ int build_plan(const akv_op* ops, int64_t n_ops, int32_t bq, int32_t bk, akv_pla
           w[0] = (int32_t)j;
           w[1] = p->tok_pos[j];
           w[2] = (int32_t)vv;
-          img_src[b + vv] = (int32_t)j;
-          img_to[b + vv] = (int32_t)vv;
         });
         v = end;
       }
     });
+
+    // Runs of version rows that move by one shift (row index - append position):
+    // a run starts at a stretch's first version row and wherever the shift changes.
+    // Consecutive surviving tokens of one append keep consecutive positions, so a
+    // stretch has few runs (a table of per-run rotations serves all its rows).
+    {
+      auto shift = [&](int64_t v) { return p->versions[3 * v + 2] - p->versions[3 * v + 1]; };
+      auto starts = [&](int64_t v) { return p->versions[3 * v + 2] == 0 || shift(v) != shift(v - 1); };
+      const int64_t nch = std::max<int64_t>(1, std::min<int64_t>(256, (ver_total + 16383) / 16384));
+      std::vector<int64_t> cbase(nch + 1, 0);
+      par_for(nch, 1, [&](int64_t lo, int64_t hi) {
+        for (int64_t c = lo; c < hi; ++c) {
+          int64_t k = 0;
+          for (int64_t v = ver_total * c / nch; v < ver_total * (c + 1) / nch; ++v) k += starts(v);
+          cbase[c + 1] = k;
+        }
+      });
+      for (int64_t c = 0; c < nch; ++c) cbase[c + 1] += cbase[c];
+      p->n_runs = cbase[nch];
+      if (p->n_runs > INT32_MAX) throw std::length_error("too many version runs");
+      p->ver_run.resize(ver_total);
+      p->run_delta.resize(p->n_runs);
+      par_for(nch, 1, [&](int64_t lo, int64_t hi) {
+        for (int64_t c = lo; c < hi; ++c) {
+          int64_t id = cbase[c] - 1;
+          for (int64_t v = ver_total * c / nch; v < ver_total * (c + 1) / nch; ++v) {
+            if (starts(v)) p->run_delta[++id] = shift(v);
+            p->ver_run[v] = (int32_t)id;
+          }
+        }
+      });
+    }
+
+    // Device image layout.  Version rows carry only (src, to, run); kernels read the
+    // source's append position and drop boundary through tok_pos / tok_drop.
+    uint64_t off = 0;
+    auto place = [&](uint64_t bytes) { uint64_t o = off; off += (bytes + 255) & ~uint64_t(255); return o; };
+    p->off_tok_pos = place(4 * T);
+    p->off_tok_drop = place(4 * T);
+    p->off_ver_src = place(4 * ver_total);
+    p->off_ver_to = place(4 * ver_total);
+    p->off_ver_run = place(4 * ver_total);
+    p->off_run_delta = place(4 * (uint64_t)p->n_runs);
+    p->off_item_desc = place(4 * (uint64_t)n_items * ID_WORDS);
+    p->off_tiles = place(4 * (uint64_t)n_tiles);
+    p->off_order = place(4 * (uint64_t)n_items);
+    p->image_bytes = std::max<uint64_t>(off, 256);
+    p->image.reset(new uint8_t[p->image_bytes]);   // padding between arrays is never read
+    int32_t* img_src = (int32_t*)(p->image.get() + p->off_ver_src);
+    int32_t* img_to = (int32_t*)(p->image.get() + p->off_ver_to);
+    int32_t* img_desc = (int32_t*)(p->image.get() + p->off_item_desc);
+    int32_t* img_tiles = (int32_t*)(p->image.get() + p->off_tiles);
+    par_for(ver_total, 1 << 15, [&](int64_t lo, int64_t hi) {
+      for (int64_t v = lo; v < hi; ++v) {
+        img_src[v] = p->versions[3 * v];
+        img_to[v] = p->versions[3 * v + 2];
+      }
+      std::memcpy(p->image.get() + p->off_ver_run + 4 * lo, p->ver_run.data() + lo, 4 * (hi - lo));
+    });
+    if (p->n_runs) std::memcpy(p->image.get() + p->off_run_delta, p->run_delta.data(), 4 * p->n_runs);
 
     // T6 tile lists, items and item descriptors.
     p->tiles.resize(n_tiles);

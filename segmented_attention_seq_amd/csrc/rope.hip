@@ -139,17 +139,17 @@ __global__ __launch_bounds__(256) void rope_kernel(T* __restrict__ out, const T*
       // pair i = (a[i], b[i])
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        ya[i] = a[i] * cs[i] - b[i] * sn[i];
-        yb[i] = a[i] * sn[i] + b[i] * cs[i];
+        ya[i] = rot_first(a[i], b[i], cs[i], sn[i]);
+        yb[i] = rot_second(a[i], b[i], cs[i], sn[i]);
       }
     } else {
       // pairs are adjacent: (a[0],a[1]) .. (a[6],a[7]), (b[0],b[1]) .. (b[6],b[7])
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        ya[2 * i] = a[2 * i] * cs[i] - a[2 * i + 1] * sn[i];
-        ya[2 * i + 1] = a[2 * i] * sn[i] + a[2 * i + 1] * cs[i];
-        yb[2 * i] = b[2 * i] * cs[i + 4] - b[2 * i + 1] * sn[i + 4];
-        yb[2 * i + 1] = b[2 * i] * sn[i + 4] + b[2 * i + 1] * cs[i + 4];
+        ya[2 * i] = rot_first(a[2 * i], a[2 * i + 1], cs[i], sn[i]);
+        ya[2 * i + 1] = rot_second(a[2 * i], a[2 * i + 1], cs[i], sn[i]);
+        yb[2 * i] = rot_first(b[2 * i], b[2 * i + 1], cs[i + 4], sn[i + 4]);
+        yb[2 * i + 1] = rot_second(b[2 * i], b[2 * i + 1], cs[i + 4], sn[i + 4]);
       }
     }
     Vec8<T>::store(y + h * d + oa, ya);
@@ -253,7 +253,7 @@ __global__ __launch_bounds__(256) void rope_row_kernel(T* __restrict__ out, cons
       }
 #pragma unroll
       for (int i = 0; i < 8; ++i)
-        y[i] = second ? a[i] * sn[i] + b[i] * cs[i] : a[i] * cs[i] - b[i] * sn[i];
+        y[i] = second ? rot_second(a[i], b[i], cs[i], sn[i]) : rot_first(a[i], b[i], cs[i], sn[i]);
     } else {
       float cs[4], sn[4];
 #pragma unroll
@@ -263,8 +263,8 @@ __global__ __launch_bounds__(256) void rope_row_kernel(T* __restrict__ out, cons
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        y[2 * i] = a[2 * i] * cs[i] - a[2 * i + 1] * sn[i];
-        y[2 * i + 1] = a[2 * i] * sn[i] + a[2 * i + 1] * cs[i];
+        y[2 * i] = rot_first(a[2 * i], a[2 * i + 1], cs[i], sn[i]);
+        y[2 * i + 1] = rot_second(a[2 * i], a[2 * i + 1], cs[i], sn[i]);
       }
     }
     if (h >= heads || rb * RPW + r >= n_rows) continue;

@@ -22,4 +22,11 @@ __device__ __forceinline__ void rope_angle_cs(double delta, double rev, float& c
   c = __builtin_amdgcn_cosf(r);
 }
 
+// Pair (a, b) rotated by the angle with cosine c and sine s: first member
+// a c - b s, second member a s + b c.  Every kernel that rotates keys or queries
+// goes through these two, with their fused multiply-adds spelled out, so a key
+// rotated while a tile is staged and one rotated into a version buffer round alike.
+__device__ __forceinline__ float rot_first(float a, float b, float c, float s) { return __builtin_fmaf(a, c, -(b * s)); }
+__device__ __forceinline__ float rot_second(float a, float b, float c, float s) { return __builtin_fmaf(a, s, b * c); }
+
 }  // namespace akv

@@ -410,6 +410,82 @@ def test_workloads_full_size_boundary_and_seeded_rows(cfg, part, parts):
     _check_rows(tr, qkv, out, lse, bf16=True, rows=rows)
 
 
+# ---------------------------------------------------------------- fused version rows
+
+def _restore_both(tr, q, k, v, hq, hkv, layout=akv.ROPE_HALF):
+    """The same restore with version buffers and with version rows rotated while
+    key tiles are staged."""
+    plan = akv.build_visibility(akv.ops_from_messages(tr.msg_len, tr.drop, tr.reposition))
+    T = tr.n_tokens
+    res = []
+    for fused in (False, True):
+        bufs = {"out": nan_like((T, hq, 64), torch.bfloat16), "lse": nan_like((T, hq), torch.float32)}
+        out, lse = akv.restore(plan, dev_tensor(q, True), dev_tensor(k, True), dev_tensor(v, True), BASE, layout,
+                               with_lse=True, bufs=bufs, fused_versions=fused)
+        torch.cuda.synchronize()
+        res.append((out, lse))
+    return plan, res
+
+
+@pytest.mark.parametrize("seed,layout,keep", [(171, akv.ROPE_HALF, 1), (172, akv.ROPE_INTERLEAVED, 2),
+                                              (173, akv.ROPE_HALF, 3), (174, akv.ROPE_HALF, 0)])
+def test_fused_versions_equal_version_buffers(seed, layout, keep):
+    """Version rows rotated at staging time equal the version-buffer path bit for
+    bit (the same rotation arithmetic, the same attention), on trajectories with a
+    repos after every round, rolling drops (PARTIAL tiles) and ragged tails; and
+    both meet the oracle."""
+    tr = workload.agent_trajectory(5, seed=seed, total=2600, keep=keep, repos="every", user_len=50,
+                                   assist_range=(20, 200), tool_range=(60, 500), name=f"fused{seed}")
+    q, k, v = workload.prefill_tensors(tr.n_tokens, 16, 2, 64, seed=seed + 1)
+    plan, ((o0, l0), (o1, l1)) = _restore_both(tr, q, k, v, 16, 2, layout)
+    assert plan.info["n_versions"] > 0 and plan.info["n_runs"] > 1
+    assert torch.equal(o0.view(torch.int16), o1.view(torch.int16))
+    assert torch.equal(l0, l1)
+    _check_rows(tr, (q, k, v), o1, l1, bf16=True, layout=layout)
+
+
+@pytest.mark.parametrize("cfg", [3, 4])
+def test_fused_versions_workloads_full_size(cfg):
+    """The 300k (7 repos stretches) and 192k (200 stretches) restores with version
+    rows rotated at staging time: the whole output equals the version-buffer path's
+    bit for bit (that path is checked on every boundary row in
+    test_workloads_full_size_boundary_and_seeded_rows), and the first stretch range
+    with version rows is checked against the oracle directly."""
+    tr, qkv, tables, out_ref, lse_ref = _restored(cfg)
+    q, k, v = qkv
+    plan = akv.build_visibility(akv.ops_from_messages(tr.msg_len, tr.drop, tr.reposition))
+    T, hq, d = q.shape
+    bufs = {"out": nan_like((T, hq, d), torch.bfloat16), "lse": nan_like((T, hq), torch.float32)}
+    out, lse = akv.restore(plan, dev_tensor(q, True), dev_tensor(k, True), dev_tensor(v, True), BASE,
+                           with_lse=True, bufs=bufs, fused_versions=True)
+    torch.cuda.synchronize()
+    print(f"[cfg{cfg} fused] version rows {plan.info['n_versions']}, runs {plan.info['n_runs']}", flush=True)
+    assert torch.equal(out.view(torch.int16), out_ref.view(torch.int16))
+    assert torch.equal(lse, lse_ref)
+    parts = {3: 3, 4: 4}[cfg]
+    rows, e_part, s_part, _ = full_size_rows(tables, T, cfg, 1, parts)
+    _check_rows(tr, qkv, out, lse, bf16=True, rows=rows)
+
+
+def test_fused_versions_rejects_unsupported():
+    tr = workload.agent_trajectory(2, seed=181, total=400, keep=1, repos="every", user_len=20,
+                                   assist_range=(20, 60), tool_range=(40, 120))
+    plan = akv.build_visibility(akv.ops_from_messages(tr.msg_len, tr.drop, tr.reposition))
+    q, k, v = workload.prefill_tensors(tr.n_tokens, 8, 2, 64, seed=182)
+    out = nan_like((tr.n_tokens, 8, 64), torch.bfloat16)
+    with pytest.raises(akv.AkvError) as e:   # 4 query heads per kv head
+        akv.segment_attention_fused(plan, dev_tensor(q, True), dev_tensor(k, True), dev_tensor(v, True), out)
+    assert e.value.status == akv.EUNSUPPORTED
+    q8 = workload.prefill_tensors(tr.n_tokens, 16, 2, 64, seed=183)[0]
+    out8 = nan_like((tr.n_tokens, 16, 64), torch.bfloat16)
+    assert akv.rot_table_bytes(plan, 64) == plan.info["n_runs"] * 32 * 8 > 0
+    short = torch.empty(8, dtype=torch.uint8, device="cuda")
+    with pytest.raises(akv.AkvError) as e:
+        akv.segment_attention_fused(plan, dev_tensor(q8, True), dev_tensor(k, True), dev_tensor(v, True), out8,
+                                    ws=short)
+    assert e.value.status == akv.EINVAL
+
+
 @pytest.mark.parametrize("hq", [32, 16, 8])
 def test_48k_workload_smaller_head_groups_sampled(hq):
     """The 48k restore with 4, 2 and 1 query heads per kv head (the one-wave-per-head

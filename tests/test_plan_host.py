@@ -88,6 +88,13 @@ def _compare(lens, drop, repos, bq, bk, tiles="full", rng=None):
         assert np.array_equal(t[name], o[name].astype(np.int32).reshape(t[name].shape)), name
     assert info["p_next"] == o["p_next"]
     assert info["visible_pairs"] == o["visible_pairs"]
+    # runs of version rows with one shift (to - from), restarting at every stretch
+    ver = o["versions"].reshape(-1, 3)
+    shift = ver[:, 2] - ver[:, 1]
+    starts = (ver[:, 2] == 0) | np.r_[True, shift[1:] != shift[:-1]] if ver.size else np.zeros(0, bool)
+    assert np.array_equal(t["ver_run"], np.cumsum(starts) - 1)
+    assert np.array_equal(t["run_delta"], shift[starts])
+    assert info["n_runs"] == int(starts.sum())
     n_items = info["n_items"]
     order = t["item_order"]
     assert sorted(order.tolist()) == list(range(n_items))
