@@ -300,28 +300,33 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     avg = {n: (float(np.mean(v)) if v else None) for n, v in stage_ms.items()}
 
-    # The short kernels once more, back to back between one pair of events, so the
-    # marker packets of the per-stage events (a few microseconds each) do not count
-    # against them: repos over the rotating buffer sets (together larger than the
-    # last-level cache), decode over its 1.9 GB of gathered rows.
-    b2b = {}
+    # The short kernels once more, back to back between one pair of events per round,
+    # so the marker packets of the per-stage events (a few microseconds each) do not
+    # count against them: repos over the rotating buffer sets (together larger than
+    # the last-level cache), decode over its 1.9 GB of gathered rows.
+    # Each is the median over several rounds, since one round of a 35 us kernel moves
+    # by several percent from round to round.
+    b2b, b2b_rounds = {}, {}
+
+    def rounds(launch, n, k):
+        per = []
+        for _ in range(k):
+            e0 = mark()
+            for j in range(n):
+                launch(j)
+            e1 = mark()
+            torch.cuda.synchronize()
+            per.append(e0.elapsed_time(e1) / n)
+        return float(np.median(per)), per
+
     if "repos" in only:
-        n_b2b = 4 * len(repos_sets)
-        e0 = mark()
-        for j in range(n_b2b):
+        def repos_launch(j):
             pool, out = repos_sets[j % len(repos_sets)]
             akv.rope_repos(out, pool, r_to, r_from, r_idx)
-        e1 = mark()
-        torch.cuda.synchronize()
-        b2b["repos"] = e0.elapsed_time(e1) / n_b2b
+        b2b["repos"], b2b_rounds["repos"] = rounds(repos_launch, 4 * len(repos_sets), 5)
     if "decode" in only:
-        n_b2b = 8
-        e0 = mark()
-        for _ in range(n_b2b):
-            akv.decode_attention(dq, pool_k, pool_v, d_indptr, d_indices, max_n, dout, ws=dws)
-        e1 = mark()
-        torch.cuda.synchronize()
-        b2b["decode"] = e0.elapsed_time(e1) / n_b2b
+        b2b["decode"], b2b_rounds["decode"] = rounds(
+            lambda j: akv.decode_attention(dq, pool_k, pool_v, d_indptr, d_indices, max_n, dout, ws=dws), 8, 3)
 
     value = attn_flop / (ms_per_step * 1e-3) / 1e12 if "restore" in only else 0.0
     attn_tflops = attn_flop / (avg["attn"] * 1e-3) / 1e12 if avg["attn"] else None
@@ -337,12 +342,14 @@ def main():
         comps["repos"] = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                           "frac": gbs / PEAK_HBM_GBS, "bytes_per_launch": repos_bytes, "keys": nrep}
         comps["repos"].update(_back_to_back(b2b["repos"], repos_bytes))
+        comps["repos"]["b2b_rounds_us"] = [round(x * 1e3, 2) for x in b2b_rounds["repos"]]
     if avg["decode"]:
         gbs = decode_bytes / (avg["decode"] * 1e-3) / 1e9
         comps["decode"] = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                            "frac": gbs / PEAK_HBM_GBS, "bytes_per_launch": decode_bytes,
                            "gathered_keys": n_keys, "requests": int(db.q.shape[0])}
         comps["decode"].update(_back_to_back(b2b["decode"], decode_bytes))
+        comps["decode"]["b2b_rounds_us"] = [round(x * 1e3, 2) for x in b2b_rounds["decode"]]
     if avg["rope"]:
         rope_bytes = 2 * kd.numel() * 2 + 4 * T
         comps["rope_apply_gbs"] = rope_bytes / (avg["rope"] * 1e-3) / 1e9
