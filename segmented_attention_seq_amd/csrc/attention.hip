@@ -21,6 +21,11 @@
 //     element i of 4 consecutive rows);
 //   * the plan's tile list skips EMPTY tiles, FULL tiles run unmasked, PARTIAL
 //     tiles build the mask from per-key (token, drop) pairs staged in LDS;
+//   * K/V tiles reach LDS by direct global -> LDS copies (global_load_lds, 16
+//     bytes a lane) into unpadded rows whose 16-byte chunks are XOR-swizzled by
+//     row, so the K row reads and the transposing V reads stay free of bank
+//     conflicts; the rotated-staging variant goes through registers into rows
+//     padded to 144 and 160 bytes;
 //   * blockIdx -> (item, kv head) puts consecutive workgroups on different kv heads,
 //     so with 8 kv heads each XCD's L2 streams a single head's K/V;
 //   * 8 query heads per kv head (seg_attn_bf16_pp): two wave groups ping-pong
@@ -58,6 +63,7 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
 
 constexpr int D = 64;    // head dim
@@ -85,6 +91,7 @@ __device__ __forceinline__ float xhalf_sum(float x) {
 // inline asm made it re-wait for reads issued after the barrier).
 constexpr int kWaitLgkm0 = 0xC07F;  // s_waitcnt lgkmcnt(0), vmcnt and expcnt unconstrained
 constexpr int kWaitVm0 = 0x0F70;    // s_waitcnt vmcnt(0), expcnt and lgkmcnt unconstrained
+constexpr int kWaitVm2 = 0x0F72;    // s_waitcnt vmcnt(2), expcnt and lgkmcnt unconstrained
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_sched_barrier(0);
   __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
@@ -138,6 +145,22 @@ __device__ __forceinline__ bf16x8 row_frag(const uint16_t* base, int row, int ds
   return *(const bf16x8*)(base + row * KP + ds * 16 + lg * 8);
 }
 
+// Swizzled tile layout (SW): rows of 64 bf16 with no padding, as the direct
+// global -> LDS copies write them (64 lanes x 16 bytes, contiguous).  16-byte
+// chunk c of K row r sits at chunk c ^ swz_k(r), of V row r at c ^ swz_v(r).  A K
+// fragment read (lanes 0-31 read rows r0..r0+31 at one chunk) then spreads every 8
+// consecutive rows, and every 16 rows of equal parity, over all eight chunks; a
+// transposing V read (16 lanes: 4 consecutive rows x 32 bytes) puts its four rows
+// on four different chunk pairs, and 32 lanes put rows of equal parity on
+// different halves of the row.
+__device__ __forceinline__ int swz_k(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+__device__ __forceinline__ int swz_v(int r) { return (r & 3) << 1; }
+template <bool SW>
+__device__ __forceinline__ bf16x8 k_frag(const uint16_t* lkb, int row, int ds, int lg) {
+  if (SW) return *(const bf16x8*)(lkb + row * D + (((2 * ds + lg) ^ swz_k(row)) << 3));
+  return row_frag(lkb, row, ds, lg);
+}
+
 // Q' operand of query block qb, d slice ds: from registers, or (QL) from the
 // wave's Q' rows in LDS.
 template <bool QL>
@@ -148,7 +171,7 @@ __device__ __forceinline__ bf16x8 q_frag(const WaveState& w, const uint16_t* lqw
 
 // S^T = K Q'^T for one 64-key tile (16 MFMAs), operands read as they are used.
 // Q' is Q scaled by scale*log2(e), so the scores are already in log2 units.
-template <bool QL>
+template <bool QL, bool SW = false>
 __device__ __forceinline__ void tile_qk(WaveState& w, const uint16_t* lkb, const uint16_t* lqw, int lq, int lg) {
   const f32x16 zero = {};
 #pragma unroll
@@ -156,7 +179,7 @@ __device__ __forceinline__ void tile_qk(WaveState& w, const uint16_t* lkb, const
     const bf16x8 b0 = q_frag<QL>(w, lqw, 0, ds, lq, lg), b1 = q_frag<QL>(w, lqw, 1, ds, lq, lg);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const bf16x8 a = row_frag(lkb, kb * 32 + lq, ds, lg);
+      const bf16x8 a = k_frag<SW>(lkb, kb * 32 + lq, ds, lg);
       w.s[kb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b0, ds ? w.s[kb][0] : zero, 0, 0, 0);
       w.s[kb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b1, ds ? w.s[kb][1] : zero, 0, 0, 0);
     }
@@ -166,26 +189,38 @@ __device__ __forceinline__ void tile_qk(WaveState& w, const uint16_t* lkb, const
 // V^T fragments of one tile from the row-major V tile through the transposing LDS
 // read (lane i of a 16-lane group gets element i%4 of the 8-byte chunk that lane
 // 4k + i/4 addresses, for k = 0..3).  Fragment g = 4kb + 2hf + db, two reads each.
+template <bool SW = false>
 __device__ __forceinline__ void read_vt_part(VFrag& f, const uint16_t* lvb, int lane, int g) {
   const int G = lane >> 4, i16 = lane & 15;
   const int kb = g >> 2, hf = (g >> 1) & 1, db = g & 1;
   const int key = kb * 32 + 16 * hf + 4 * (G >> 1) + (i16 >> 2);
   const int dc = db * 32 + 16 * (G & 1) + 4 * (i16 & 3);
-  const s16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lvb + key * VP + dc));
-  const s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lvb + (key + 8) * VP + dc));
+  // swz_v(key + 8) == swz_v(key)
+  const int off = SW ? key * D + (((dc >> 3) ^ swz_v(key)) << 3) + (dc & 7) : key * VP + dc;
+  const int pitch = SW ? D : VP;
+  const s16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lvb + off));
+  const s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lvb + off + 8 * pitch));
   f.a[kb][hf][db] = cat4(r0, r1);
 }
 
+template <bool SW = false>
 __device__ __forceinline__ void read_vt(VFrag& f, const uint16_t* lvb, int lane) {
 #pragma unroll
-  for (int g = 0; g < 8; ++g) read_vt_part(f, lvb, lane, g);
+  for (int g = 0; g < 8; ++g) read_vt_part<SW>(f, lvb, lane, g);
 }
+
+// No work hooked into an MFMA sequence.
+struct NoCopy {
+  __device__ __forceinline__ void operator()() const {}
+  static constexpr bool kActive = false;
+};
 
 // tile_qk with the K fragments and the first two Q' slices (qf[0], qf[1]) already
 // in registers; the remaining Q' slices are read from LDS two d slices ahead of
 // their MFMAs, and after each d slice's MFMAs two of the next tile's V^T fragments
 // (vf, from lvb) are read, so those LDS reads issue between MFMAs instead of in
 // one block.
+template <bool SW>
 __device__ __forceinline__ void mfma_qk_lq(WaveState& w, const KFrag& f, const bf16x8 (&qf)[2][2], const uint16_t* lqw,
                                            int lq, int lg, VFrag& vf, const uint16_t* lvb, int lane) {
   const f32x16 zero = {};
@@ -206,8 +241,8 @@ __device__ __forceinline__ void mfma_qk_lq(WaveState& w, const KFrag& f, const b
       for (int qb = 0; qb < 2; ++qb)
         w.s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[ds][kb], b[ds % 3][qb], ds ? w.s[kb][qb] : zero,
                                                               0, 0, 0);
-    read_vt_part(vf, lvb, lane, 2 * ds);
-    read_vt_part(vf, lvb, lane, 2 * ds + 1);
+    read_vt_part<SW>(vf, lvb, lane, 2 * ds);
+    read_vt_part<SW>(vf, lvb, lane, 2 * ds + 1);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -292,7 +327,7 @@ __device__ __forceinline__ void prep_scores(WaveState& w, bool partial, const in
 // Mask (PARTIAL tiles), online softmax in log2 units, P -> bf16 B operand.  The
 // scores die as P is formed; the rare path that moves a column's offset
 // recomputes them from the tile's K rows (still in LDS at lkb).
-template <bool QL>
+template <bool QL, bool SW = false>
 __device__ __forceinline__ void tile_softmax(WaveState& w, bool partial, const int* mtok, const int* mdrop,
                                              const uint16_t* lkb, const uint16_t* lqw, int q0, int lq, int lg) {
   prep_scores(w, partial, mtok, mdrop, q0, lq, lg);
@@ -302,7 +337,7 @@ __device__ __forceinline__ void tile_softmax(WaveState& w, bool partial, const i
   const bool bad0 = out_of_range(tot[0], w.lrun[0]), bad1 = out_of_range(tot[1], w.lrun[1]);
   if (__any(bad0 || bad1)) {
     asm volatile("");  // rare: scores far above or below the offset
-    tile_qk<QL>(w, lkb, lqw, lq, lg);
+    tile_qk<QL, SW>(w, lkb, lqw, lq, lg);
     prep_scores(w, partial, mtok, mdrop, q0, lq, lg);
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
@@ -384,10 +419,10 @@ __device__ __forceinline__ void mfma_pv(WaveState& w, const VFrag& f) {
 // the first and the second Q' slice).  The reads' latency hides behind the MFMAs.
 // With SUMS, each quarter also adds its P slice into the column sums ls
 // (colsum_selector).
-template <bool SUMS>
+template <bool SUMS, bool SW, class Copy = NoCopy>
 __device__ __forceinline__ void mfma_pv_read_k(WaveState& w, const VFrag& f, KFrag& kf, bf16x8 (&qf)[2][2],
                                                f32x4 (&ls)[2], bf16x8 sel, const uint16_t* lkb,
-                                               const uint16_t* lqw, int lq, int lg) {
+                                               const uint16_t* lqw, int lq, int lg, const Copy& copy = Copy()) {
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -403,8 +438,16 @@ __device__ __forceinline__ void mfma_pv_read_k(WaveState& w, const VFrag& f, KFr
           ls[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel, w.pb[kb][qb][hf], ls[qb], 0, 0, 0);
       }
       const int ds = kb * 2 + hf;
+      if (Copy::kActive && ds == 0) {
+        copy();
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) kf.a[ds][kk] = row_frag(lkb, kk * 32 + lq, ds, lg);
+        for (int g = 0; g < 6; ++g) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002 | 0x004, 8, 0);
+        }
+      }
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) kf.a[ds][kk] = k_frag<SW>(lkb, kk * 32 + lq, ds, lg);
       if (ds == 1 || ds == 3) {
         qf[ds >> 1][0] = row_frag(lqw, lq, ds >> 1, lg);
         qf[ds >> 1][1] = row_frag(lqw, 32 + lq, ds >> 1, lg);
@@ -559,6 +602,17 @@ __device__ __forceinline__ int local_tid(int wave_s) {
 // the rows with the tile (fetch), the four (cos, sin) pairs of its run ahead of the
 // stash (load_rot), and the key is rotated as it is written to LDS (stash), with the
 // same arithmetic as the version builder.
+// 16 bytes per lane from gbase + voff (bytes) into LDS at lds + 16 * lane, by the
+// memory pipe (global_load_lds_dwordx4; lds must be uniform).  Issued as inline
+// assembly so that the compiler, which cannot tell one tile slot from another,
+// does not make every later LDS read wait for the copy; the pipeline orders the
+// copy against the slot's readers itself (vmcnt waits before barriers).
+__device__ __forceinline__ void lds_copy16(const void* gbase, uint32_t voff, const uint16_t* lds) {
+  const uint32_t la = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(gbase), "s"(la)
+               : "m0");
+}
+
 template <int NT, bool ROT = false>
 struct TileStage {
   static constexpr int CPT = (BK * 8 + NT - 1) / NT;  // 16-byte chunks of K (and V) per thread
@@ -601,7 +655,6 @@ struct TileStage {
     if (!ROT || !rot) return;
     const int pp = local_tid(wave_s) & 7;
     const float* t = rot_tab + ((long long)(srun > 0 ? srun : 0) * (D / 2) + 4 * pp) * 2;
-    typedef __attribute__((address_space(3))) void lds_void;
     __builtin_amdgcn_global_load_lds((const void*)t, (lds_void*)rl, 16, 0, 0);
     __builtin_amdgcn_global_load_lds((const void*)(t + 4), (lds_void*)(rl + 256), 16, 0, 0);
   }
@@ -613,7 +666,6 @@ struct TileStage {
     if (!ROT || !ts.ver) return;
     const int key = (local_tid(wave_s) >> 3) & (BK - 1);
     const int row = ts.row0 + (key < ts.nrows ? key : ts.nrows - 1);
-    typedef __attribute__((address_space(3))) void lds_void;
     __builtin_amdgcn_global_load_lds((const void*)(ver_src + row), (lds_void*)(rl + 512), 4, 0, 0);
     __builtin_amdgcn_global_load_lds((const void*)(ver_run + row), (lds_void*)(rl + 576), 4, 0, 0);
   }
@@ -695,6 +747,43 @@ struct TileStage {
         mt = ts.ver ? -1 : ts.row0 + key;
         md = tok_drop[ts.ver ? ver_src[ts.row0 + key] : ts.row0 + key];
       }
+    }
+  }
+  // SW layout: this wave's eight rows of the tile (rows 8 wave .. 8 wave + 7) copied
+  // by the memory pipe straight into LDS.  Lane l writes its 16 bytes at l * 16 of
+  // the wave's 1 KB, which is chunk l % 8 of row 8 wave + l / 8, so it reads the
+  // source chunk that the swizzle places there.  Rows past a ragged tile's end copy
+  // its last row (finite values; the tile is PARTIAL and its mask hides them).
+  __device__ __forceinline__ void dma(const TileSrc& ts, int hkv, int hk, uint16_t* lkb, uint16_t* lvb) {
+    const int lane = local_tid(wave_s) & 63;
+    const int row = 8 * wave_s + (lane >> 3), p = lane & 7;
+    const int srow = row < ts.nrows ? row : ts.nrows - 1;
+    // row0's head-hk row as a uniform base; the per-lane byte offset is 32-bit
+    const long long base = ((long long)ts.row0 * hkv + hk) * D;
+    const uint32_t rbytes = __umul24((uint32_t)srow & (BK - 1), (uint32_t)hkv * (D * 2));
+    const uint32_t ok = rbytes + ((uint32_t)(p ^ swz_k(row)) << 4);
+    const uint32_t ov = rbytes + ((uint32_t)(p ^ swz_v(row)) << 4);
+    lds_copy16(ts.k + base, ok, lkb + 8 * wave_s * D);
+    lds_copy16(ts.v + base, ov, lvb + 8 * wave_s * D);
+  }
+  // The mask metadata of a PARTIAL tile into registers (wave 0), for stash_mask.
+  __device__ __forceinline__ void fetch_mask(const TileSrc& ts, bool part, const int* tok_drop, const int* ver_src) {
+    partial = part;
+    const int tid = local_tid(wave_s);
+    if (part && tid < BK) {
+      mt = INT_MAX;
+      md = INT_MIN;
+      if (tid < ts.nrows) {
+        mt = ts.ver ? -1 : ts.row0 + tid;
+        md = tok_drop[ts.ver ? ver_src[ts.row0 + tid] : ts.row0 + tid];
+      }
+    }
+  }
+  __device__ __forceinline__ void stash_mask(int* mtok, int* mdrop) {
+    const int tid = local_tid(wave_s);
+    if (partial && tid < BK) {
+      mtok[tid] = mt;
+      mdrop[tid] = md;
     }
   }
   __device__ __forceinline__ void stash(uint16_t* lkb, uint16_t* lvb, int* mtok, int* mdrop) {
@@ -800,23 +889,35 @@ __global__ __launch_bounds__(64 * GROUP, 2) void seg_attn_bf16(AKV_ATTN_PARAMS) 
 // separated by workgroup barriers, so while one wave of a SIMD issues MFMAs
 // (PV of tile t and QK of tile t+1) its partner runs the softmax of its tile on
 // the VALU.  A K/V tile is read from LDS for three phases (its K and V^T in the
-// MFMA phase before its softmax, its mask in the softmax), so tiles rotate
-// through three LDS slots.  Tile t+3 is fetched to registers at the start of
-// iteration t's softmax phase and written to its slot at the start of the next
-// iteration's softmax phase: the slot then belongs to tile t, whose last reader
-// passed the barrier that closed the previous MFMA phase.  So the MFMA phase
-// issues only MFMAs and LDS reads; the staging's address arithmetic and waits
-// would otherwise stall it behind the partner wave's exp stream.  The loop is
-// unrolled over the three slots so every LDS slot address is a constant.
+// MFMA phase before its softmax, its mask in the softmax).
+//
+// Direct copies (version rows read from version buffers): tiles rotate through
+// four LDS slots.  In iteration t's MFMA phase every wave copies its eight rows of
+// tile t+3 from memory straight into LDS (global_load_lds), into the slot of tile
+// t-1, whose last reader passed an earlier barrier; each wave waits for its copies
+// of the iteration before (vmcnt) ahead of each barrier, so a copy has two phases
+// to land and the tile is whole before the barrier after which it is first read.
+// The copies cost the MFMA wave a few dozen issue slots between its MFMAs and
+// cost the softmax wave, whose phase was the longer one, nothing.
+//
+// Rotated staging (version rows rotated from their source keys): three slots;
+// tile t+3 is fetched to registers at the start of iteration t's softmax phase
+// and written (rotated) to its slot in the next iteration's softmax phase.
+//
+// The loop is unrolled over the slots so every LDS slot address is a constant.
 //
 // SAFE = false is the fast pass (offset 0, column sums on the matrix cores);
 // SAFE = true is the lazily-rescaled softmax with per-tile range checks.
 constexpr int kPPThreads = 512;
-constexpr int kPPSlots = 3;
-
+// LDS slots of the tile ring and their sizes: rotated staging (through registers,
+// padded rows) keeps three; direct copies (swizzled rows, 16 KB a tile) keep four.
+template <bool ROT>
 struct PPCtx {
-  uint16_t (*lk)[BK * KP];
-  uint16_t (*lv)[BK * VP];
+  static constexpr int NS = ROT ? 3 : 4;
+  static constexpr int KSZ = ROT ? BK * KP : BK * D;
+  static constexpr int VSZ = ROT ? BK * VP : BK * D;
+  uint16_t* lk[4];  // K and V tile of each slot (NS used)
+  uint16_t* lv[4];
   int (*mtok)[BK];
   int (*mdrop)[BK];
   const uint16_t* lqw;
@@ -831,22 +932,38 @@ struct PPCtx {
   __device__ __forceinline__ int entry(int t) const { return tiles[min(t, n - 1)]; }
 };
 
+// A tile copy issued from inside the MFMA phase (mfma_pv_read_k calls it).
+template <class Stage>
+struct TileCopy {
+  Stage& st;
+  const TileSrc& ts;
+  uint16_t *dk, *dv;
+  int hkv, hk;
+  static constexpr bool kActive = true;
+  __device__ __forceinline__ void operator()() const { st.dma(ts, hkv, hk, dk, dv); }
+};
+
 // One iteration of the ping-pong loop for tile i held in LDS slot S; ent holds
 // the entries of tiles i .. i+3 and is advanced by one.
 template <bool SAFE, int S, bool ROT>
 __device__ __forceinline__ void pp_step(WaveState& w, f32x4 (&ls)[2], bf16x8 sel, TileStage<kPPThreads, ROT>& st,
-                                        VFrag& vf, const PPCtx& c, int i, int (&ent)[4]) {
-  constexpr int S1 = (S + 1) % kPPSlots, S2 = (S + 2) % kPPSlots;
-  // phase 1 (VALU): tile i+2 (fetched one iteration ago) goes to the slot of tile
-  // i-1, tile i+3 is fetched, and the softmax of tile i runs.  Its V^T fragments
-  // were read between the QK MFMAs of the previous MFMA phase.  Without ROT the
-  // stash and fetch come first; with ROT the tile's (cos, sin) and the next tile's
+                                        VFrag& vf, const PPCtx<ROT>& c, int i, int (&ent)[4]) {
+  constexpr int NS = PPCtx<ROT>::NS;
+  constexpr int S1 = (S + 1) % NS, S2 = (S + 2) % NS, S3 = (S + 3) % NS;
+  // phase 1 (VALU): the softmax of tile i, whose V^T fragments were read between
+  // the QK MFMAs of the previous MFMA phase.  Without ROT the tiles arrive by
+  // direct copies issued in the MFMA phase, and this phase only moves a PARTIAL
+  // tile's mask metadata (loaded into registers one iteration before it is
+  // stored).  With ROT, tile i+2 (fetched one iteration ago) goes to the slot of
+  // tile i-1 and tile i+3 is fetched: the tile's (cos, sin) and the next tile's
   // source rows are requested first, and the stash (which rotates) and the fetch
   // (which gathers by those rows) come after the softmax, so that neither the
   // rotation values nor the rows cross the MFMA phase in registers.
+  constexpr bool SW = !ROT;
   if (!ROT) {
-    if (i + 2 < c.n) st.stash(c.lk[S2], c.lv[S2], c.mtok[S2], c.mdrop[S2]);
-    if (i + 3 < c.n) st.fetch(c.src(ent[3]), (ent[3] & 3) == AKV_TILE_PARTIAL, c.hkv, c.hk, c.tok_drop, c.ver_src);
+    // masks of tile i+2 (loaded one iteration ago) to its slot; tile i+3's loaded
+    if (i + 2 < c.n) st.stash_mask(c.mtok[S2], c.mdrop[S2]);
+    if (i + 3 < c.n) st.fetch_mask(c.src(ent[3]), (ent[3] & 3) == AKV_TILE_PARTIAL, c.tok_drop, c.ver_src);
   } else {
     if (i + 2 < c.n) st.load_rot(c.rot_tab);
     if (i + 3 < c.n) st.load_idx(c.src(ent[3]), c.ver_src, c.ver_run);
@@ -857,9 +974,17 @@ __device__ __forceinline__ void pp_step(WaveState& w, f32x4 (&ls)[2], bf16x8 sel
   const int ent_next = c.entry(i + 4);
   const bool part = (ent[0] & 3) == AKV_TILE_PARTIAL;
   if (SAFE)
-    tile_softmax<true>(w, part, c.mtok[S], c.mdrop[S], c.lk[S], c.lqw, c.q0, c.lq, c.lg);
+    tile_softmax<true, SW>(w, part, c.mtok[S], c.mdrop[S], c.lk[S], c.lqw, c.q0, c.lq, c.lg);
   else
     tile_softmax_fast(w, part, c.mtok[S], c.mdrop[S], c.q0, c.lq, c.lg);
+  if (!ROT) {
+    // the copies this wave issued two iterations ago (and earlier) have landed in
+    // LDS before the barrier after which other waves may read them; the previous
+    // iteration's copies (its last two vector-memory instructions before this
+    // phase's mask loads) may stay in flight
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(kWaitVm2);
+  }
   if (ROT) {
     __builtin_amdgcn_sched_barrier(0);
     if (i + 2 < c.n) {
@@ -875,11 +1000,26 @@ __device__ __forceinline__ void pp_step(WaveState& w, f32x4 (&ls)[2], bf16x8 sel
   __builtin_amdgcn_s_setprio(1);
   KFrag kf;
   bf16x8 qf[2][2];
-  mfma_pv_read_k<!SAFE>(w, vf, kf, qf, ls, sel, c.lk[S1], c.lqw, c.lq, c.lg);
+  if (SW) {
+    // Each wave copies its rows of tile i+3 into the slot of tile i-1, whose last
+    // reader (group B's softmax) passed a barrier before this phase.  The copy's
+    // instructions issue between the first PV MFMAs, where this wave's issue slots
+    // are free.  Past the last tile the entry is the last tile's, and its rows go
+    // to a slot that is not read again (no branch: a branch here lets the compiler
+    // sink the softmax's exps past the barrier into this phase).
+    const TileSrc ts = c.src(ent[3]);
+    const TileCopy<TileStage<kPPThreads, ROT>> copy{st, ts, c.lk[S3], c.lv[S3], c.hkv, c.hk};
+    mfma_pv_read_k<!SAFE, SW>(w, vf, kf, qf, ls, sel, c.lk[S1], c.lqw, c.lq, c.lg, copy);
+  } else {
+    mfma_pv_read_k<!SAFE, SW>(w, vf, kf, qf, ls, sel, c.lk[S1], c.lqw, c.lq, c.lg);
+  }
   __builtin_amdgcn_sched_barrier(0);
   // P of tile i is dead here, before the scores of tile i+1 are born: they share registers
-  if (i + 1 < c.n) mfma_qk_lq(w, kf, qf, c.lqw, c.lq, c.lg, vf, c.lv[S1], c.lane);
+  if (i + 1 < c.n) mfma_qk_lq<SW>(w, kf, qf, c.lqw, c.lq, c.lg, vf, c.lv[S1], c.lane);
   __builtin_amdgcn_s_setprio(0);
+  // every wave's copies of one iteration ago (and earlier) have landed before the
+  // barrier; this phase's stay in flight
+  if (SW) __builtin_amdgcn_s_waitcnt(kWaitVm2);
   lds_barrier();
   ent[0] = ent[1];
   ent[1] = ent[2];
@@ -889,12 +1029,30 @@ __device__ __forceinline__ void pp_step(WaveState& w, f32x4 (&ls)[2], bf16x8 sel
 
 template <bool SAFE, bool ROT>
 __device__ __forceinline__ void pp_pipeline(WaveState& w, f32x4 (&ls)[2], bf16x8 sel,
-                                            TileStage<kPPThreads, ROT>& st, const PPCtx& c, bool lag) {
-  // tiles 0 and 1 staged, tile 2 fetched
+                                            TileStage<kPPThreads, ROT>& st, const PPCtx<ROT>& c, bool lag) {
+  constexpr bool SW = !ROT;
   int ent[4] = {c.entry(0), c.entry(1), c.entry(2), c.entry(3)};
+  if (SW) {
+    // tiles 0, 1 and 2 copied, tile 2's mask loaded
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      if (j < c.n) {
+        const TileSrc ts = c.src(ent[j]);
+        st.fetch_mask(ts, (ent[j] & 3) == AKV_TILE_PARTIAL, c.tok_drop, c.ver_src);
+        st.dma(ts, c.hkv, c.hk, c.lk[j], c.lv[j]);
+        st.stash_mask(c.mtok[j], c.mdrop[j]);
+      }
+    }
+    if (c.n > 2) {
+      st.fetch_mask(c.src(ent[2]), (ent[2] & 3) == AKV_TILE_PARTIAL, c.tok_drop, c.ver_src);
+      st.dma(c.src(ent[2]), c.hkv, c.hk, c.lk[2], c.lv[2]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  }
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    if (j < c.n) {
+    if (!SW && j < c.n) {
       const TileSrc ts = c.src(ent[j]);
       st.load_idx(ts, c.ver_src, c.ver_run);
       st.fetch(ts, (ent[j] & 3) == AKV_TILE_PARTIAL, c.hkv, c.hk, c.tok_drop, c.ver_src);
@@ -903,23 +1061,30 @@ __device__ __forceinline__ void pp_pipeline(WaveState& w, f32x4 (&ls)[2], bf16x8
       st.stash(c.lk[j], c.lv[j], c.mtok[j], c.mdrop[j]);
     }
   }
-  if (c.n > 2) {
+  if (!SW && c.n > 2) {
     st.load_idx(c.src(ent[2]), c.ver_src, c.ver_run);
     st.fetch(c.src(ent[2]), (ent[2] & 3) == AKV_TILE_PARTIAL, c.hkv, c.hk, c.tok_drop, c.ver_src);
   }
   lds_barrier();
   if (lag) lds_barrier();
-  tile_qk<true>(w, c.lk[0], c.lqw, c.lq, c.lg);
+  tile_qk<true, SW>(w, c.lk[0], c.lqw, c.lq, c.lg);
   VFrag vf;
-  read_vt(vf, c.lv[0], c.lane);
+  read_vt<SW>(vf, c.lv[0], c.lane);
   lds_barrier();
-  for (int i = 0; i < c.n; i += 3) {
+  for (int i = 0; i < c.n; i += PPCtx<ROT>::NS) {
     pp_step<SAFE, 0, ROT>(w, ls, sel, st, vf, c, i, ent);
     if (i + 1 >= c.n) break;
     pp_step<SAFE, 1, ROT>(w, ls, sel, st, vf, c, i + 1, ent);
     if (i + 2 >= c.n) break;
     pp_step<SAFE, 2, ROT>(w, ls, sel, st, vf, c, i + 2, ent);
+    if (PPCtx<ROT>::NS == 4) {
+      if (i + 3 >= c.n) break;
+      pp_step<SAFE, 3 % PPCtx<ROT>::NS, ROT>(w, ls, sel, st, vf, c, i + 3, ent);
+    }
   }
+  // no copy (those past the last tile included) is still in flight when the
+  // slots are next written
+  if (SW) __builtin_amdgcn_s_waitcnt(kWaitVm0);
   if (!lag) lds_barrier();
 }
 
@@ -933,9 +1098,10 @@ template <bool ROT>
 __global__ __launch_bounds__(kPPThreads) void seg_attn_bf16_pp(AKV_ATTN_PARAMS, const int* __restrict__ ver_run,
                                                                const float* __restrict__ rot_tab) {
   constexpr int GROUP = 8;
-  __shared__ __attribute__((aligned(16))) uint16_t lk[kPPSlots][BK * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t lv[kPPSlots][BK * VP];
-  __shared__ int mtok[kPPSlots][BK], mdrop[kPPSlots][BK];
+  using Ctx = PPCtx<ROT>;
+  __shared__ __attribute__((aligned(16))) uint16_t lk[Ctx::NS][Ctx::KSZ];
+  __shared__ __attribute__((aligned(16))) uint16_t lv[Ctx::NS][Ctx::VSZ];
+  __shared__ int mtok[Ctx::NS][BK], mdrop[Ctx::NS][BK];
   __shared__ __attribute__((aligned(16))) uint16_t lqs[GROUP][64 * KP];
   __shared__ __attribute__((aligned(16))) float rtab[ROT ? GROUP * 640 : 4];  // ROT: 2.5 KB per wave
   __shared__ int redo;
@@ -964,9 +1130,12 @@ __global__ __launch_bounds__(kPPThreads) void seg_attn_bf16_pp(AKV_ATTN_PARAMS, 
   st.rl = rtab + (ROT ? st.wave_s * 640 : 0);
   const bf16x8 sel = colsum_selector(lane);
   f32x4 ls[2] = {};
-  PPCtx c;
-  c.lk = lk;
-  c.lv = lv;
+  Ctx c;
+#pragma unroll
+  for (int j = 0; j < Ctx::NS; ++j) {
+    c.lk[j] = lk[j];
+    c.lv[j] = lv[j];
+  }
   c.mtok = mtok;
   c.mdrop = mdrop;
   c.lqw = lqw;
