@@ -220,7 +220,7 @@ def main():
 
     ev_names = ["rope", "versions", "attn", "repos", "decode"]
     stage_ms = {n: [] for n in ev_names}
-    build_ms, upload_ms = [], []
+    build_ms, upload_ev = [], []
     keep_plans = []
     dev_plans = [torch.empty(int(plan0.info["device_bytes"]), dtype=torch.uint8, device=dev) for _ in range(2)]
     copy_stream = torch.cuda.Stream(device=dev)     # default priority
@@ -243,16 +243,18 @@ def main():
             buf = dev_plans[i % 2]
             if plan_free[i % 2] is not None:
                 copy_stream.wait_event(plan_free[i % 2])
+            up0 = torch.cuda.Event(enable_timing=True)
+            up0.record(copy_stream)
             akv._check(akv._lib.akv_plan_upload(plan.handle, buf.data_ptr(), buf.numel(), copy_stream.cuda_stream),
                        "akv_plan_upload")
-            uploaded = torch.cuda.Event()
+            uploaded = torch.cuda.Event(enable_timing=True)
             uploaded.record(copy_stream)
             torch.cuda.current_stream().wait_event(uploaded)
             plan._dev[str(dev)] = buf
             keep_plans.append(plan)
             del keep_plans[:-3]      # host images stay alive until their copies ran
             build_ms.append((t1 - t0) * 1e3)
-            upload_ms.append((time.perf_counter() - t1) * 1e3)
+            upload_ev.append((up0, uploaded))   # the copy itself, on the copy stream
             # One event between consecutive stages (each record is a marker packet
             # of a few microseconds on the GPU timeline): stage k runs from mark k to
             # mark k+1.
@@ -333,7 +335,8 @@ def main():
     # counters were taken on 64/8 with version buffers
     traffic = read_traffic(args.config) if hq // hkv == 8 and not fused else None
     comps = {"host_plan_build_ms": float(np.mean(build_ms)) if build_ms else None,
-             "host_plan_upload_ms": float(np.mean(upload_ms)) if upload_ms else None,
+             "host_plan_upload_ms": (float(np.mean([a.elapsed_time(b) for a, b in upload_ev]))
+                                     if upload_ev else None),
              "plan_device_bytes": int(plan0.info["device_bytes"])}
     for n in ev_names:
         comps[f"{n}_ms"] = avg[n]
