@@ -341,6 +341,24 @@ def test_edge_cases_bf16(name):
     _check_rows(tr, qkv, out, lse, bf16=True)
 
 
+@pytest.mark.parametrize("repos", [False, True])
+def test_short_items_every_tile_count(repos):
+    """Work items of 1 to 8 key tiles on the 8-head kernel, so that each one starts
+    and ends its tile ring differently (the prologue's copies, copies past the
+    last tile, the final waits): eight 64-token query tiles of one stretch, or a
+    repos after the first 256 tokens, whose version rows give a second stretch
+    with PARTIAL and ragged tiles.  Every row is checked, and the fused staging
+    equals the version buffers bit for bit."""
+    lens, rp = ([512], []) if not repos else ([256, 256], [0])
+    tr = workload.Trajectory(lens, ["x"] * len(lens), {}, rp, name=f"short-items-{repos}")
+    q, k, v = workload.prefill_tensors(tr.n_tokens, 16, 2, 64, seed=81)
+    plan, ((o0, l0), (o1, l1)) = _restore_both(tr, q, k, v, 16, 2)
+    counts = set(np.diff(plan.tables()["tile_ptr"]).tolist())
+    assert set(range(1, 5)) <= counts and (repos or set(range(1, 9)) <= counts)
+    assert torch.equal(o0.view(torch.int16), o1.view(torch.int16)) and torch.equal(l0, l1)
+    _check_rows(tr, (q, k, v), o0, l0, bf16=True)
+
+
 def test_empty_plan_and_unsupported():
     plan = akv.build_visibility([])
     x = torch.empty((0, 8, 64), dtype=torch.bfloat16, device="cuda")
