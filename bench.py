@@ -36,7 +36,7 @@ METRIC = "segment-attn restore TFLOP/s (% MFMA peak); repos+decode HBM GB/s (% p
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
 ATTN_SRCS = [os.path.join(ROOT, "segmented_attention_seq_amd", "csrc", f)
-             for f in ("attention.hip", "internal.h", "rope_angle.h")]
+             for f in ("attention.hip", "internal.h", "rope_angle.h", "plan.cpp")]
 TRAFFIC_FILES = {2: os.path.join(ROOT, "profiles", "segment_attention_48k_traffic.md"),
                  3: os.path.join(ROOT, "profiles", "segment_attention_300k_traffic.md"),
                  4: os.path.join(ROOT, "profiles", "segment_attention_192k_traffic.md")}
@@ -67,9 +67,10 @@ def parse_args():
 
 
 def attn_src_hash():
-    """Hash of the attention kernel's code: its source and the two local headers it
-    includes, with comments removed and whitespace collapsed, so an edit of the
-    comments alone keeps the counters that were taken on the same code."""
+    """Hash of the attention kernel's code: its source, the two local headers it
+    includes, and the plan builder (whose work order decides how much of the K/V
+    traffic the L2 absorbs), with comments removed and whitespace collapsed, so an
+    edit of the comments alone keeps the counters that were taken on the same code."""
     h = hashlib.sha256()
     for path in ATTN_SRCS:
         with open(path) as f:

@@ -140,7 +140,8 @@ typedef struct {
   const int32_t* items;        /* [n_items][2] stretch, q-tile */
   const int32_t* tile_ptr;     /* [n_items + 1] */
   const int32_t* tiles;        /* [n_tiles] k_tile * 4 + class */
-  const int32_t* item_order;   /* [n_items] launch order: descending tile count */
+  const int32_t* item_order;   /* [n_items] launch order: stretches by descending tile count (ties by
+                                  index), each stretch's items by descending tile count */
   const int32_t* final_tok;    /* [n_final] */
   const int32_t* final_pos;    /* [n_final] */
   const int32_t* ver_run;      /* [n_versions] run of each version row: a run is a maximal
