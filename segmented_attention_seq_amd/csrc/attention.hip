@@ -21,6 +21,10 @@
 //     element i of 4 consecutive rows);
 //   * the plan's tile list skips EMPTY tiles, FULL tiles run unmasked, PARTIAL
 //     tiles build the mask from per-key (token, drop) pairs staged in LDS;
+//   * the direct-copy kernel keeps Q' in registers for the whole tile loop and reads
+//     each PV quarter's V^T fragments one quarter ahead (the registers that frees
+//     pay for Q'), so its QK phase issues only MFMAs; the rotated-staging variant
+//     keeps Q' in per-wave LDS rows, read a d slice ahead;
 //   * K/V tiles reach LDS by direct global -> LDS copies (global_load_lds, 16
 //     bytes a lane) into unpadded rows whose 16-byte chunks are XOR-swizzled by
 //     row, so the K row reads and the transposing V reads stay free of bank
@@ -215,15 +219,29 @@ struct NoCopy {
   static constexpr bool kActive = false;
 };
 
-// tile_qk with the K fragments and the first two Q' slices (qf[0], qf[1]) already
-// in registers; the remaining Q' slices are read from LDS two d slices ahead of
-// their MFMAs, and after each d slice's MFMAs two of the next tile's V^T fragments
-// (vf, from lvb) are read, so those LDS reads issue between MFMAs instead of in
-// one block.
+// tile_qk with the K fragments already in registers.  SW (direct-copy kernel): Q'
+// is held in registers for the whole loop (w.qf) and the V^T fragments are read
+// inside PV, so QK issues only MFMAs.  Otherwise the first two Q' slices (qf[0],
+// qf[1]) come from PV and the remaining ones are read from LDS two d slices ahead
+// of their MFMAs, and after each d slice's MFMAs two of the next tile's V^T
+// fragments (vf, from lvb) are read, so those LDS reads issue between MFMAs
+// instead of in one block.
 template <bool SW>
 __device__ __forceinline__ void mfma_qk_lq(WaveState& w, const KFrag& f, const bf16x8 (&qf)[2][2], const uint16_t* lqw,
                                            int lq, int lg, VFrag& vf, const uint16_t* lvb, int lane) {
   const f32x16 zero = {};
+  if (SW) {  // Q' in registers; V^T fragments are read inside PV
+#pragma unroll
+    for (int ds = 0; ds < 4; ++ds) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+          w.s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[ds][kb], w.qf[qb][ds], ds ? w.s[kb][qb] : zero,
+                                                                0, 0, 0);
+    }
+    return;
+  }
   bf16x8 b[3][2];
   b[0][0] = qf[0][0];
   b[0][1] = qf[0][1];
@@ -415,14 +433,16 @@ __device__ __forceinline__ void mfma_pv(WaveState& w, const VFrag& f) {
 
 // mfma_pv with the next tile's K fragments read in between: after the 4 MFMAs of
 // each (kb, hf) quarter, whose V^T and P registers then die, the two K fragments
-// of one 16-wide d slice are read (and, after the second and the last quarter,
-// the first and the second Q' slice).  The reads' latency hides behind the MFMAs.
-// With SUMS, each quarter also adds its P slice into the column sums ls
-// (colsum_selector).
+// of one 16-wide d slice are read.  SW: before them, the next quarter's V^T
+// fragments of this tile (lvb; the first quarter's were read at the end of the
+// softmax phase).  Otherwise, after the second and the last quarter, the first and
+// the second Q' slice.  The reads' latency hides behind the MFMAs.  With SUMS, each
+// quarter also adds its P slice into the column sums ls (colsum_selector).
 template <bool SUMS, bool SW, class Copy = NoCopy>
-__device__ __forceinline__ void mfma_pv_read_k(WaveState& w, const VFrag& f, KFrag& kf, bf16x8 (&qf)[2][2],
+__device__ __forceinline__ void mfma_pv_read_k(WaveState& w, VFrag& f, KFrag& kf, bf16x8 (&qf)[2][2],
                                                f32x4 (&ls)[2], bf16x8 sel, const uint16_t* lkb,
-                                               const uint16_t* lqw, int lq, int lg, const Copy& copy = Copy()) {
+                                               const uint16_t* lqw, int lq, int lg, const uint16_t* lvb, int lane,
+                                               const Copy& copy = Copy()) {
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -438,6 +458,10 @@ __device__ __forceinline__ void mfma_pv_read_k(WaveState& w, const VFrag& f, KFr
           ls[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel, w.pb[kb][qb][hf], ls[qb], 0, 0, 0);
       }
       const int ds = kb * 2 + hf;
+      if (SW && ds < 3) {  // the next quarter's V^T fragments
+        read_vt_part<SW>(f, lvb, lane, 2 * (ds + 1));
+        read_vt_part<SW>(f, lvb, lane, 2 * (ds + 1) + 1);
+      }
       if (Copy::kActive && ds == 0) {
         copy();
 #pragma unroll
@@ -448,7 +472,7 @@ __device__ __forceinline__ void mfma_pv_read_k(WaveState& w, const VFrag& f, KFr
       }
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) kf.a[ds][kk] = k_frag<SW>(lkb, kk * 32 + lq, ds, lg);
-      if (ds == 1 || ds == 3) {
+      if (!SW && (ds == 1 || ds == 3)) {
         qf[ds >> 1][0] = row_frag(lqw, lq, ds >> 1, lg);
         qf[ds >> 1][1] = row_frag(lqw, 32 + lq, ds >> 1, lg);
       }
@@ -520,6 +544,20 @@ __device__ __forceinline__ void load_q(WaveState& w, uint16_t* lqw, const uint16
       else w.qf[qb][ds] = b;
     }
   }
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    w.ms[qb] = 0.f;
+    w.lrun[qb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) w.o[qb][db][i] = 0.f;
+  }
+  w.shifted = false;
+}
+
+// Output accumulators, exponent offsets and sums back to zero (a redo pass).
+__device__ __forceinline__ void reset_acc(WaveState& w) {
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     w.ms[qb] = 0.f;
@@ -950,8 +988,7 @@ __device__ __forceinline__ void pp_step(WaveState& w, f32x4 (&ls)[2], bf16x8 sel
                                         VFrag& vf, const PPCtx<ROT>& c, int i, int (&ent)[4]) {
   constexpr int NS = PPCtx<ROT>::NS;
   constexpr int S1 = (S + 1) % NS, S2 = (S + 2) % NS, S3 = (S + 3) % NS;
-  // phase 1 (VALU): the softmax of tile i, whose V^T fragments were read between
-  // the QK MFMAs of the previous MFMA phase.  Without ROT the tiles arrive by
+  // phase 1 (VALU): the softmax of tile i.  Without ROT the tiles arrive by
   // direct copies issued in the MFMA phase, and this phase only moves a PARTIAL
   // tile's mask metadata (loaded into registers one iteration before it is
   // stored).  With ROT, tile i+2 (fetched one iteration ago) goes to the slot of
@@ -974,7 +1011,7 @@ __device__ __forceinline__ void pp_step(WaveState& w, f32x4 (&ls)[2], bf16x8 sel
   const int ent_next = c.entry(i + 4);
   const bool part = (ent[0] & 3) == AKV_TILE_PARTIAL;
   if (SAFE)
-    tile_softmax<true, SW>(w, part, c.mtok[S], c.mdrop[S], c.lk[S], c.lqw, c.q0, c.lq, c.lg);
+    tile_softmax<!SW, SW>(w, part, c.mtok[S], c.mdrop[S], c.lk[S], c.lqw, c.q0, c.lq, c.lg);
   else
     tile_softmax_fast(w, part, c.mtok[S], c.mdrop[S], c.q0, c.lq, c.lg);
   if (!ROT) {
@@ -993,10 +1030,15 @@ __device__ __forceinline__ void pp_step(WaveState& w, f32x4 (&ls)[2], bf16x8 sel
     }
     if (i + 3 < c.n) st.fetch(c.src(ent[3]), (ent[3] & 3) == AKV_TILE_PARTIAL, c.hkv, c.hk, c.tok_drop, c.ver_src);
   }
+  if (SW) {  // the first PV quarter's V^T fragments; the others are read inside PV
+    read_vt_part<SW>(vf, c.lv[S], c.lane, 0);
+    read_vt_part<SW>(vf, c.lv[S], c.lane, 1);
+  }
   lds_barrier();
   // phase 2 (MFMA): PV of tile i with the K fragments of tile i+1 read between its
-  // MFMAs; QK of tile i+1 with its V^T fragments read between those MFMAs (after
-  // the last tile, slot S1 holds an older tile: its K reads are harmless and unused)
+  // MFMAs (and, without ROT, tile i's own V^T fragments one quarter ahead); QK of
+  // tile i+1 (with ROT, with its V^T fragments read between those MFMAs).  After the
+  // last tile, slot S1 holds an older tile: its K reads are harmless and unused.
   __builtin_amdgcn_s_setprio(1);
   KFrag kf;
   bf16x8 qf[2][2];
@@ -1009,9 +1051,9 @@ __device__ __forceinline__ void pp_step(WaveState& w, f32x4 (&ls)[2], bf16x8 sel
     // sink the softmax's exps past the barrier into this phase).
     const TileSrc ts = c.src(ent[3]);
     const TileCopy<TileStage<kPPThreads, ROT>> copy{st, ts, c.lk[S3], c.lv[S3], c.hkv, c.hk};
-    mfma_pv_read_k<!SAFE, SW>(w, vf, kf, qf, ls, sel, c.lk[S1], c.lqw, c.lq, c.lg, copy);
+    mfma_pv_read_k<!SAFE, SW>(w, vf, kf, qf, ls, sel, c.lk[S1], c.lqw, c.lq, c.lg, c.lv[S], c.lane, copy);
   } else {
-    mfma_pv_read_k<!SAFE, SW>(w, vf, kf, qf, ls, sel, c.lk[S1], c.lqw, c.lq, c.lg);
+    mfma_pv_read_k<!SAFE, SW>(w, vf, kf, qf, ls, sel, c.lk[S1], c.lqw, c.lq, c.lg, c.lv[S], c.lane);
   }
   __builtin_amdgcn_sched_barrier(0);
   // P of tile i is dead here, before the scores of tile i+1 are born: they share registers
@@ -1067,9 +1109,9 @@ __device__ __forceinline__ void pp_pipeline(WaveState& w, f32x4 (&ls)[2], bf16x8
   }
   lds_barrier();
   if (lag) lds_barrier();
-  tile_qk<true, SW>(w, c.lk[0], c.lqw, c.lq, c.lg);
+  tile_qk<!SW, SW>(w, c.lk[0], c.lqw, c.lq, c.lg);
   VFrag vf;
-  read_vt<SW>(vf, c.lv[0], c.lane);
+  if (!SW) read_vt<SW>(vf, c.lv[0], c.lane);
   lds_barrier();
   for (int i = 0; i < c.n; i += PPCtx<ROT>::NS) {
     pp_step<SAFE, 0, ROT>(w, ls, sel, st, vf, c, i, ent);
@@ -1123,7 +1165,10 @@ __global__ __launch_bounds__(kPPThreads) void seg_attn_bf16_pp(AKV_ATTN_PARAMS, 
   if (threadIdx.x == 0) redo = 0;  // published by the first barrier of the pipeline
 
   WaveState w;
-  load_q<true>(w, lqw, q, q0, q1, hq, h, lq, lg, sl2, tok_pos, rq);
+  if (ROT)
+    load_q<true>(w, lqw, q, q0, q1, hq, h, lq, lg, sl2, tok_pos, rq);
+  else
+    load_q<false>(w, lqw, q, q0, q1, hq, h, lq, lg, sl2, tok_pos, rq);
   TileStage<kPPThreads, ROT> st;
   st.wave_s = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   st.layout = rq.layout;
@@ -1174,7 +1219,7 @@ __global__ __launch_bounds__(kPPThreads) void seg_attn_bf16_pp(AKV_ATTN_PARAMS, 
   lds_barrier();
   if (__builtin_amdgcn_readfirstlane(redo)) {
     asm volatile("");  // rare: keep the second pipeline out of the common path
-    load_q<false>(w, nullptr, q, q0, q0, hq, h, lq, lg, 0.f, tok_pos, rq);  // resets O, offsets and sums (Q' stays in LDS)
+    reset_acc(w);  // O, offsets and sums (Q' stays where it is)
     pp_pipeline<true, ROT>(w, ls, sel, st, c, lag);
   } else {
 #pragma unroll
