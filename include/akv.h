@@ -239,9 +239,9 @@ int akv_segment_attention_rope(const akv_plan* plan, const void* dev_plan,
 
 /* ---------------------------------------------------------------- A3 + A4 fused
  *
- * Segment attention that builds no version buffers: each version row's key is
- * rotated from its source key as the attention stages its key tile, and its value
- * row is read from the source.  Review "single-prefill restore with segment-batch
+ * Segment attention that builds no version buffers: each version row's key and
+ * value are copied from its source token into the attention's key tile, and the
+ * key is rotated there.  Review "single-prefill restore with segment-batch
  * attention" (§4.2, App. A.1.1): the per-segment KV versions are temporary; key
  * rotation and value copy make them.  Version row v of a stretch is the key of
  * source token j = ver_src[v] moved from its append position tok_pos[j] to v, i.e.
@@ -252,8 +252,9 @@ int akv_segment_attention_rope(const akv_plan* plan, const void* dev_plan,
  * q_raw: raw queries [T][hq][d] (rotated on load as in akv_segment_attention_rope);
  * k: keys rotated to their append positions (akv_rope_apply); v: values.
  * ws: caller device memory of at least akv_rot_table_bytes(plan, d) bytes (may be
- * NULL when that is 0), overwritten.  bf16 only, d == 64, hq == 8 * hkv (other
- * shapes: AKV_EUNSUPPORTED; use the version-buffer path).  Other errors as
+ * NULL when that is 0), overwritten.  bf16 only, d == 64, hq == 8 * hkv, and k and
+ * v under 4 GiB each (T * hkv * d * 2 bytes < 2^32, T = the plan's token count);
+ * other shapes: AKV_EUNSUPPORTED, use the version-buffer path.  Other errors as
  * akv_segment_attention_rope, plus AKV_EINVAL for a short workspace.
  */
 uint64_t akv_rot_table_bytes(const akv_plan* plan, int32_t d);

@@ -297,6 +297,9 @@ int akv_segment_attention_fused(const akv_plan* p, const void* dev_plan, const v
     return fail(AKV_EINVAL, "rope_layout must be AKV_ROPE_HALF or AKV_ROPE_INTERLEAVED");
   if (dtype != AKV_BF16 || d != 64 || hkv < 1 || hq != 8 * hkv)
     return fail(AKV_EUNSUPPORTED, "fused version rotation needs bf16, d == 64 and hq == 8 * hkv");
+  // the kernel's gathered copies address k and v by 32-bit byte offsets
+  if ((uint64_t)p->T * (uint64_t)hkv * (uint64_t)d * 2 > 0xffffffffull)
+    return fail(AKV_EUNSUPPORTED, "fused version rotation needs k and v under 4 GiB each");
   const uint64_t need = akv_rot_table_bytes(p, d);
   if (ws_bytes < need || (need && !ws)) return fail(AKV_EINVAL, "rotation table workspace too small");
   akv::RopeQ rq{};

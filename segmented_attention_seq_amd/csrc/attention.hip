@@ -21,15 +21,17 @@
 //     element i of 4 consecutive rows);
 //   * the plan's tile list skips EMPTY tiles, FULL tiles run unmasked, PARTIAL
 //     tiles build the mask from per-key (token, drop) pairs staged in LDS;
-//   * the direct-copy kernel keeps Q' in registers for the whole tile loop and reads
+//   * the ping-pong kernel keeps Q' in registers for the whole tile loop and reads
 //     each PV quarter's V^T fragments one quarter ahead (the registers that frees
-//     pay for Q'), so its QK phase issues only MFMAs; the rotated-staging variant
-//     keeps Q' in per-wave LDS rows, read a d slice ahead;
+//     pay for Q'), so its QK phase issues only MFMAs; the variant without version
+//     buffers keeps Q' in per-wave LDS rows, read a d slice ahead, and spends those
+//     registers on rotating its version rows;
 //   * K/V tiles reach LDS by direct global -> LDS copies (global_load_lds, 16
 //     bytes a lane) into unpadded rows whose 16-byte chunks are XOR-swizzled by
 //     row, so the K row reads and the transposing V reads stay free of bank
-//     conflicts; the rotated-staging variant goes through registers into rows
-//     padded to 144 and 160 bytes;
+//     conflicts; without version buffers, a version tile's rows are gathered from
+//     their source tokens the same way and each wave turns its own key rows in
+//     place in LDS, between the QK MFMAs;
 //   * blockIdx -> (item, kv head) puts consecutive workgroups on different kv heads,
 //     so with 8 kv heads each XCD's L2 streams a single head's K/V;
 //   * 8 query heads per kv head (seg_attn_bf16_pp): two wave groups ping-pong
@@ -69,6 +71,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
 
 constexpr int D = 64;    // head dim
 constexpr int BK = 64;   // keys per tile (= 2 MFMA row blocks)
@@ -96,6 +99,7 @@ __device__ __forceinline__ float xhalf_sum(float x) {
 constexpr int kWaitLgkm0 = 0xC07F;  // s_waitcnt lgkmcnt(0), vmcnt and expcnt unconstrained
 constexpr int kWaitVm0 = 0x0F70;    // s_waitcnt vmcnt(0), expcnt and lgkmcnt unconstrained
 constexpr int kWaitVm2 = 0x0F72;    // s_waitcnt vmcnt(2), expcnt and lgkmcnt unconstrained
+constexpr int kWaitVm4 = 0x0F74;    // s_waitcnt vmcnt(4), expcnt and lgkmcnt unconstrained
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_sched_barrier(0);
   __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
@@ -435,10 +439,10 @@ __device__ __forceinline__ void mfma_pv(WaveState& w, const VFrag& f) {
 // each (kb, hf) quarter, whose V^T and P registers then die, the two K fragments
 // of one 16-wide d slice are read.  SW: before them, the next quarter's V^T
 // fragments of this tile (lvb; the first quarter's were read at the end of the
-// softmax phase).  Otherwise, after the second and the last quarter, the first and
-// the second Q' slice.  The reads' latency hides behind the MFMAs.  With SUMS, each
+// softmax phase).  QL (Q' in LDS): after the second and the last quarter, the
+// first and the second Q' slice.  The reads' latency hides behind the MFMAs.  With SUMS, each
 // quarter also adds its P slice into the column sums ls (colsum_selector).
-template <bool SUMS, bool SW, class Copy = NoCopy>
+template <bool SUMS, bool SW, class Copy = NoCopy, bool QL = !SW>
 __device__ __forceinline__ void mfma_pv_read_k(WaveState& w, VFrag& f, KFrag& kf, bf16x8 (&qf)[2][2],
                                                f32x4 (&ls)[2], bf16x8 sel, const uint16_t* lkb,
                                                const uint16_t* lqw, int lq, int lg, const uint16_t* lvb, int lane,
@@ -467,12 +471,12 @@ __device__ __forceinline__ void mfma_pv_read_k(WaveState& w, VFrag& f, KFrag& kf
 #pragma unroll
         for (int g = 0; g < 6; ++g) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002 | 0x004, 8, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002 | 0x004, Copy::kValu, 0);
         }
       }
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) kf.a[ds][kk] = k_frag<SW>(lkb, kk * 32 + lq, ds, lg);
-      if (!SW && (ds == 1 || ds == 3)) {
+      if (QL && (ds == 1 || ds == 3)) {
         qf[ds >> 1][0] = row_frag(lqw, lq, ds >> 1, lg);
         qf[ds >> 1][1] = row_frag(lqw, 32 + lq, ds >> 1, lg);
       }
@@ -627,19 +631,19 @@ __device__ __forceinline__ int local_tid(int wave_s) {
   return wave_s * 64 + lane;
 }
 
-// Cooperative global -> register -> LDS staging of one K/V tile and its mask metadata.
-// The tile's PARTIAL flag travels with the fetched registers to the stash.
+// Cooperative global -> register -> LDS staging of one K/V tile and its mask
+// metadata (fetch, stash; the 1/2/4-head kernel), and the ping-pong kernel's direct
+// copies (dma).  The tile's PARTIAL flag travels with its mask registers.
 //
-// With ROT, version rows are not read from version buffers: row v of a stretch is
-// the key of its source token ver_src[v] (rotated to its append position) turned
+// With ROT (the ping-pong kernel without version buffers), row v of a version tile
+// is the key of its source token ver_src[v] (rotated to its append position) turned
 // by the shift of its run, v - tok_pos[src], whose (cos, sin) per frequency come
-// from the run table rot; the value row is the source's, unchanged.  Thread tid
-// owns key tid / 8 and its four pairs 4p .. 4p+3 (p = tid % 8): in the half layout
-// the 8-byte pieces at elements 4p and 32 + 4p, in the interleaved one the 16 bytes
-// at element 8p.  The key's (source, run) are loaded ahead of the tile (load_idx),
-// the rows with the tile (fetch), the four (cos, sin) pairs of its run ahead of the
-// stash (load_rot), and the key is rotated as it is written to LDS (stash), with the
-// same arithmetic as the version builder.
+// from the run table; its value row is the source's, unchanged.  The rows are
+// gathered from the source keys and values by the same direct copies (dma_gather),
+// and each wave then turns its own eight key rows in place in LDS (rotate): lane l
+// rotates the four pairs 4p .. 4p+3 (p = l % 8) of row l / 8 with the arithmetic of
+// the version builder, in the half layout the 8-byte pieces at elements 4p and
+// 32 + 4p, in the interleaved one the 16 bytes at element 8p.
 // 16 bytes per lane from gbase + voff (bytes) into LDS at lds + 16 * lane, by the
 // memory pipe (global_load_lds_dwordx4; lds must be uniform).  Issued as inline
 // assembly so that the compiler, which cannot tell one tile slot from another,
@@ -651,69 +655,32 @@ __device__ __forceinline__ void lds_copy16(const void* gbase, uint32_t voff, con
                : "m0");
 }
 
+// As lds_copy16, from a 64-bit address per lane (gathered rows).
+__device__ __forceinline__ void lds_copy16_a(const void* addr, const void* lds) {
+  const uint32_t la = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(addr), "s"(la) : "m0");
+}
+
+// v[j] of eight wave-uniform values, for the lane's row j in 0..7.
+__device__ __forceinline__ int pick8(const int (&v)[8], int j) {
+  const int a = (j & 1) ? v[1] : v[0], b = (j & 1) ? v[3] : v[2];
+  const int c = (j & 1) ? v[5] : v[4], d = (j & 1) ? v[7] : v[6];
+  const int e = (j & 2) ? b : a, f = (j & 2) ? d : c;
+  return (j & 4) ? f : e;
+}
+
 template <int NT, bool ROT = false>
 struct TileStage {
   static constexpr int CPT = (BK * 8 + NT - 1) / NT;  // 16-byte chunks of K (and V) per thread
   static constexpr bool EXACT = CPT * NT == BK * 8;   // every thread owns exactly CPT chunks
-  static_assert(!ROT || CPT == 1, "rotated staging needs one chunk per thread");
+  static constexpr bool kRot = ROT;
   uint4 kx[CPT], vx[CPT];
   int mt, md;
   bool partial;
   int wave_s;  // this wave's index (uniform)
   // ROT only
-  bool rot;        // the fetched tile holds version rows
-  int isrc, irun;  // source row and run of the thread's key in the next version tile
-  int srun;        // run of the thread's key in the fetched tile (-1: past the tile's rows)
-  int mrow0, mnrows;  // the fetched tile's first row and row count (uniform), for its mask
-  int layout;      // AKV_ROPE_HALF or AKV_ROPE_INTERLEAVED
-  float* rl;       // this wave's 2.5 KB of LDS: (cos, sin) of its lanes' pairs, then their (source, run)
-
-  // With ROT the mask metadata of a PARTIAL tile is loaded just before the tile's
-  // stash rather than with its rows, so it holds no registers across the MFMA
-  // phase and the softmax in between (PARTIAL tiles are rare; their loads wait).
-  __device__ __forceinline__ void load_mask(const int* tok_drop, const int* ver_src) {
-    if (!ROT || !partial) return;
-    const int tid = local_tid(wave_s);
-    if (tid < BK) {
-      mt = INT_MAX;
-      md = INT_MIN;
-      if (tid < mnrows) {
-        mt = rot ? -1 : mrow0 + tid;
-        md = tok_drop[rot ? ver_src[mrow0 + tid] : mrow0 + tid];
-      }
-    }
-  }
-
-  // The (cos, sin) of the four pairs of the thread's key in the fetched version
-  // tile, requested ahead of its stash and copied by the memory pipe straight into
-  // the wave's LDS region (lane l's 32 bytes at l * 16 and 1024 + l * 16), so they
-  // hold no registers in between.  A key past the tile's rows reads run 0: its
-  // staged row is zero and stays zero.
-  __device__ __forceinline__ void load_rot(const float* rot_tab) {
-    if (!ROT || !rot) return;
-    const int pp = local_tid(wave_s) & 7;
-    const float* t = rot_tab + ((long long)(srun > 0 ? srun : 0) * (D / 2) + 4 * pp) * 2;
-    __builtin_amdgcn_global_load_lds((const void*)t, (lds_void*)rl, 16, 0, 0);
-    __builtin_amdgcn_global_load_lds((const void*)(t + 4), (lds_void*)(rl + 256), 16, 0, 0);
-  }
-
-  // (source, run) of this thread's key in a version tile, requested ahead of the
-  // tile's fetch and copied by the memory pipe into the wave's LDS (lane l's at
-  // 2048 + 4 l and 2304 + 4 l bytes), so they hold no registers across the softmax.
-  __device__ __forceinline__ void load_idx(const TileSrc& ts, const int* ver_src, const int* ver_run) {
-    if (!ROT || !ts.ver) return;
-    const int key = (local_tid(wave_s) >> 3) & (BK - 1);
-    const int row = ts.row0 + (key < ts.nrows ? key : ts.nrows - 1);
-    __builtin_amdgcn_global_load_lds((const void*)(ver_src + row), (lds_void*)(rl + 512), 4, 0, 0);
-    __builtin_amdgcn_global_load_lds((const void*)(ver_run + row), (lds_void*)(rl + 576), 4, 0, 0);
-  }
-  // The (source, run) copied by load_idx, into registers for the fetch.
-  __device__ __forceinline__ void read_idx() {
-    const int lane = local_tid(wave_s) & 63;
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);
-    isrc = ((const int*)rl)[512 + lane];
-    irun = ((const int*)rl)[576 + lane];
-  }
+  int gsrc[8], grun[8];  // source token and run of this wave's eight rows of the next tile (uniform)
+  float* rl;             // this wave's 2 KB of LDS: the (cos, sin) of its lanes' pairs
 
   // Chunk c of a tile is 16-byte piece c % 8 of key row c / 8 (the masks tell the
   // compiler that the key index is below 64, so its products are 24-bit).
@@ -721,33 +688,6 @@ struct TileStage {
                                         const int* ver_src) {
     partial = part;
     const int tid = local_tid(wave_s);
-    if (ROT && ts.ver) {
-      rot = true;
-      read_idx();
-      const int key = (tid >> 3) & (BK - 1), pp = tid & 7;
-      kx[0] = make_uint4(0, 0, 0, 0);
-      vx[0] = make_uint4(0, 0, 0, 0);
-      srun = key < ts.nrows ? irun : -1;
-      if (key < ts.nrows) {
-        const uint16_t* kr = ts.k + ((long long)isrc * hkv + hk) * D;
-        const uint16_t* vr = ts.v + ((long long)isrc * hkv + hk) * D;
-        if (layout == AKV_ROPE_HALF) {
-          const uint2 lo = *(const uint2*)(kr + 4 * pp), hi = *(const uint2*)(kr + D / 2 + 4 * pp);
-          kx[0] = make_uint4(lo.x, lo.y, hi.x, hi.y);
-        } else {
-          kx[0] = *(const uint4*)(kr + 8 * pp);
-        }
-        vx[0] = *(const uint4*)(vr + 8 * pp);
-      }
-      mrow0 = ts.row0;
-      mnrows = ts.nrows;
-      return;
-    }
-    if (ROT) {
-      rot = false;
-      mrow0 = ts.row0;
-      mnrows = ts.nrows;
-    }
     // row0's head-hk row as a uniform base; the per-thread byte offset is 32-bit
     const long long base = ((long long)ts.row0 * hkv + hk) * D;
     const char* kb = (const char*)(ts.k + base);
@@ -777,7 +717,7 @@ struct TileStage {
         }
       }
     }
-    if (!ROT && part && tid < BK) {
+    if (part && tid < BK) {
       const int key = tid;
       mt = INT_MAX;
       md = INT_MIN;
@@ -804,6 +744,81 @@ struct TileStage {
     lds_copy16(ts.k + base, ok, lkb + 8 * wave_s * D);
     lds_copy16(ts.v + base, ov, lvb + 8 * wave_s * D);
   }
+  // ROT: (source, run) of this wave's eight rows of tile ts when it is a version
+  // tile, by scalar loads (the barrier that ends the phase waits for them); for
+  // another tile the first eight entries, unused.  The version tables carry 64
+  // entries of padding, so the rows past a ragged tile's end (and the first eight,
+  // with no version rows at all) read valid entries; a tile's mask hides its rows
+  // past the end.
+  __device__ __forceinline__ void load_gather(const TileSrc& ts, const int* ver_src, const int* ver_run) {
+    const int base = ts.ver ? ts.row0 + 8 * wave_s : 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      gsrc[j] = ver_src[base + j];
+      grun[j] = ver_run[base + j];
+    }
+  }
+  // ROT: dma with a version tile's rows gathered from their source tokens (gsrc).
+  // The lane's byte offset from head hk's row of token 0 is 32-bit (the host keeps
+  // the key and value arrays under 4 GiB), so one form serves both kinds of tile.
+  __device__ __forceinline__ void dma_gather(const TileSrc& ts, int hkv, int hk, uint16_t* lkb, uint16_t* lvb) {
+    const int lane = local_tid(wave_s) & 63;
+    const int j = lane >> 3, row = 8 * wave_s + j, p = lane & 7;
+    const int tok = ts.ver ? pick8(gsrc, j) : ts.row0 + (row < ts.nrows ? row : ts.nrows - 1);
+    const uint32_t rb = (uint32_t)tok * ((uint32_t)hkv * (D * 2));
+    lds_copy16(ts.k + hk * D, rb + ((uint32_t)(p ^ swz_k(row)) << 4), lkb + 8 * wave_s * D);
+    lds_copy16(ts.v + hk * D, rb + ((uint32_t)(p ^ swz_v(row)) << 4), lvb + 8 * wave_s * D);
+  }
+  __device__ __forceinline__ void dma_tile(const TileSrc& ts, int hkv, int hk, uint16_t* lkb, uint16_t* lvb) {
+    if constexpr (ROT)
+      dma_gather(ts, hkv, hk, lkb, lvb);
+    else
+      dma(ts, hkv, hk, lkb, lvb);
+  }
+  // ROT: the (cos, sin) of the four pairs of each lane's key in the version tile
+  // whose runs load_gather holds, copied by the memory pipe into the wave's region
+  // rl (lane l's 32 bytes at 16 l and 1024 + 16 l).
+  __device__ __forceinline__ void dma_rot(const float* rot_tab) {
+    const int lane = local_tid(wave_s) & 63;
+    const float* t = rot_tab + ((long long)pick8(grun, lane >> 3) * (D / 2) + 4 * (lane & 7)) * 2;
+    lds_copy16_a(t, rl);
+    lds_copy16_a(t + 4, rl + 256);
+  }
+  // ROT: this wave's eight key rows of the version tile in slot lkb turned in place
+  // by the (cos, sin) that dma_rot copied (the caller has waited for both copies).
+  template <int RL>
+  __device__ __forceinline__ void rotate(uint16_t* lkb) const {
+    const int lane = local_tid(wave_s) & 63;
+    const int row = 8 * wave_s + (lane >> 3), p = lane & 7, sw = swz_k(row);
+    const float4 r0 = *(const float4*)(rl + 4 * lane), r1 = *(const float4*)(rl + 256 + 4 * lane);
+    const float cs[4] = {r0.x, r0.z, r1.x, r1.z}, sn[4] = {r0.y, r0.w, r1.y, r1.w};
+    uint16_t* rp = lkb + row * D;
+    if (RL == AKV_ROPE_HALF) {  // pair 4p + i: elements 4p + i and 32 + 4p + i
+      uint2* pa = (uint2*)(rp + (((p >> 1) ^ sw) << 3) + 4 * (p & 1));
+      uint2* pb = (uint2*)(rp + (((4 + (p >> 1)) ^ sw) << 3) + 4 * (p & 1));
+      const bf16x4 xa = __builtin_bit_cast(bf16x4, *pa), xb = __builtin_bit_cast(bf16x4, *pb);
+      bf16x4 ya, yb;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float a = (float)xa[i], b = (float)xb[i];
+        ya[i] = (__bf16)rot_first(a, b, cs[i], sn[i]);
+        yb[i] = (__bf16)rot_second(a, b, cs[i], sn[i]);
+      }
+      *pa = __builtin_bit_cast(uint2, ya);
+      *pb = __builtin_bit_cast(uint2, yb);
+    } else {  // pair 4p + i: elements 8p + 2i and 8p + 2i + 1
+      bf16x8* px = (bf16x8*)(rp + ((p ^ sw) << 3));
+      const bf16x8 x = *px;
+      bf16x8 y;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float a = (float)x[2 * i], b = (float)x[2 * i + 1];
+        y[2 * i] = (__bf16)rot_first(a, b, cs[i], sn[i]);
+        y[2 * i + 1] = (__bf16)rot_second(a, b, cs[i], sn[i]);
+      }
+      *px = y;
+    }
+  }
   // The mask metadata of a PARTIAL tile into registers (wave 0), for stash_mask.
   __device__ __forceinline__ void fetch_mask(const TileSrc& ts, bool part, const int* tok_drop, const int* ver_src) {
     partial = part;
@@ -826,43 +841,13 @@ struct TileStage {
   }
   __device__ __forceinline__ void stash(uint16_t* lkb, uint16_t* lvb, int* mtok, int* mdrop) {
     const int tid = local_tid(wave_s);
-    if (ROT && rot) {
-      const int key = (tid >> 3) & (BK - 1), pp = tid & 7, lane = tid & 63;
-      // the copies into LDS (load_rot) count as vector-memory loads of this wave
-      __builtin_amdgcn_s_waitcnt(kWaitVm0);
-      const float4 r0 = *(const float4*)(rl + 4 * lane), r1 = *(const float4*)(rl + 256 + 4 * lane);
-      const float cs[4] = {r0.x, r0.z, r1.x, r1.z}, sn[4] = {r0.y, r0.w, r1.y, r1.w};
-      const bf16x8 x = __builtin_bit_cast(bf16x8, kx[0]);
-      bf16x8 y;
-      if (layout == AKV_ROPE_HALF) {  // x[i] and x[4 + i] are the two members of pair 4p + i
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float a = (float)x[i], b = (float)x[4 + i];
-          y[i] = (__bf16)rot_first(a, b, cs[i], sn[i]);
-          y[4 + i] = (__bf16)rot_second(a, b, cs[i], sn[i]);
-        }
-        const uint4 u = __builtin_bit_cast(uint4, y);
-        *(uint2*)(lkb + key * KP + 4 * pp) = make_uint2(u.x, u.y);
-        *(uint2*)(lkb + key * KP + D / 2 + 4 * pp) = make_uint2(u.z, u.w);
-      } else {  // x[2i], x[2i+1] are pair 4p + i
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float a = (float)x[2 * i], b = (float)x[2 * i + 1];
-          y[2 * i] = (__bf16)rot_first(a, b, cs[i], sn[i]);
-          y[2 * i + 1] = (__bf16)rot_second(a, b, cs[i], sn[i]);
-        }
-        *(bf16x8*)(lkb + key * KP + 8 * pp) = y;
-      }
-      *(uint4*)(lvb + key * VP + 8 * pp) = vx[0];
-    } else {
-#pragma unroll
-      for (int j = 0; j < CPT; ++j) {
-        const int c = tid + j * NT;
-        if (EXACT || c < BK * 8) {
-          const int key = (c >> 3) & (BK - 1), ch = c & 7;
-          *(uint4*)(lkb + key * KP + ch * 8) = kx[j];
-          *(uint4*)(lvb + key * VP + ch * 8) = vx[j];
-        }
+    for (int j = 0; j < CPT; ++j) {
+      const int c = tid + j * NT;
+      if (EXACT || c < BK * 8) {
+        const int key = (c >> 3) & (BK - 1), ch = c & 7;
+        *(uint4*)(lkb + key * KP + ch * 8) = kx[j];
+        *(uint4*)(lvb + key * VP + ch * 8) = vx[j];
       }
     }
     if (partial && tid < BK) {
@@ -929,8 +914,7 @@ __global__ __launch_bounds__(64 * GROUP, 2) void seg_attn_bf16(AKV_ATTN_PARAMS) 
 // the VALU.  A K/V tile is read from LDS for three phases (its K and V^T in the
 // MFMA phase before its softmax, its mask in the softmax).
 //
-// Direct copies (version rows read from version buffers): tiles rotate through
-// four LDS slots.  In iteration t's MFMA phase every wave copies its eight rows of
+// Direct copies: tiles rotate through four LDS slots.  In iteration t's MFMA phase every wave copies its eight rows of
 // tile t+3 from memory straight into LDS (global_load_lds), into the slot of tile
 // t-1, whose last reader passed an earlier barrier; each wave waits for its copies
 // of the iteration before (vmcnt) ahead of each barrier, so a copy has two phases
@@ -938,36 +922,39 @@ __global__ __launch_bounds__(64 * GROUP, 2) void seg_attn_bf16(AKV_ATTN_PARAMS) 
 // The copies cost the MFMA wave a few dozen issue slots between its MFMAs and
 // cost the softmax wave, whose phase was the longer one, nothing.
 //
-// Rotated staging (version rows rotated from their source keys): three slots;
-// tile t+3 is fetched to registers at the start of iteration t's softmax phase
-// and written (rotated) to its slot in the next iteration's softmax phase.
+// Without version buffers (ROT) a version tile's rows are gathered from their
+// source tokens by the same copies, with the (cos, sin) of their runs copied after
+// them; in iteration t's MFMA phase each wave turns its own eight key rows of tile
+// t+2 (copied in iteration t-1) in place, between the QK MFMAs, before the
+// barriers after which tile t+2 is first read.
 //
 // The loop is unrolled over the slots so every LDS slot address is a constant.
 //
 // SAFE = false is the fast pass (offset 0, column sums on the matrix cores);
 // SAFE = true is the lazily-rescaled softmax with per-tile range checks.
 constexpr int kPPThreads = 512;
-// LDS slots of the tile ring and their sizes: rotated staging (through registers,
-// padded rows) keeps three; direct copies (swizzled rows, 16 KB a tile) keep four.
+// The tile ring: four LDS slots of 16 KB (K and V, swizzled unpadded rows), filled
+// by direct copies.
 template <bool ROT>
 struct PPCtx {
-  static constexpr int NS = ROT ? 3 : 4;
-  static constexpr int KSZ = ROT ? BK * KP : BK * D;
-  static constexpr int VSZ = ROT ? BK * VP : BK * D;
-  uint16_t* lk[4];  // K and V tile of each slot (NS used)
-  uint16_t* lv[4];
+  static constexpr int NS = 4;
+  static constexpr int KSZ = BK * D;
+  static constexpr int VSZ = BK * D;
+  uint16_t* lk[NS];  // K and V tile of each slot
+  uint16_t* lv[NS];
   int (*mtok)[BK];
   int (*mdrop)[BK];
   const uint16_t* lqw;
   const int* tiles;  // this work item's tile entries
   const uint16_t *k, *v, *kver, *vver;
   const int *tok_drop, *ver_src;
-  const int* ver_run;   // rotated staging: run of each version row
-  const float* rot_tab; // rotated staging: (cos, sin) per run and frequency
+  const int* ver_run;   // ROT: run of each version row
+  const float* rot_tab; // ROT: (cos, sin) per run and frequency
   int n, nvt, voff, r, tb, te, hkv, hk, q0, lq, lg, lane;
   __device__ __forceinline__ TileSrc src(int ent) const { return tile_src(ent, nvt, voff, r, tb, te, k, v, kver, vver); }
   // entry of tile t, or of the last tile past the end (n >= 1; the caller ignores it)
   __device__ __forceinline__ int entry(int t) const { return tiles[min(t, n - 1)]; }
+  __device__ __forceinline__ bool ver(int ent) const { return (ent >> 2) < nvt; }
 };
 
 // A tile copy issued from inside the MFMA phase (mfma_pv_read_k calls it).
@@ -978,71 +965,104 @@ struct TileCopy {
   uint16_t *dk, *dv;
   int hkv, hk;
   static constexpr bool kActive = true;
-  __device__ __forceinline__ void operator()() const { st.dma(ts, hkv, hk, dk, dv); }
+  static constexpr int kValu = Stage::kRot ? 10 : 8;  // ALU instructions between two of its MFMAs
+  __device__ __forceinline__ void operator()() const { st.dma_tile(ts, hkv, hk, dk, dv); }
 };
+
+// QK of the ROT kernel, which keeps Q' in the wave's LDS rows: the first two d
+// slices come from PV (qf), the others are read two slices ahead of their MFMAs.
+// With ROTATE the in-place rotation of a version tile's key rows is woven between
+// the MFMAs: this wave's eight rows of the tile in slot lkr, copied one iteration
+// ago together with their (cos, sin), are turned here; the tile is first read
+// after the barriers that end this iteration.
+template <bool ROTATE, int RL, class Stage>
+__device__ __forceinline__ void mfma_qk_ql(WaveState& w, const KFrag& f, const bf16x8 (&qf)[2][2],
+                                           const uint16_t* lqw, int lq, int lg, const Stage& st, uint16_t* lkr) {
+  if (ROTATE) {
+    // only this iteration's tile copies (the two latest vector-memory
+    // instructions) may still be in flight; the LDS reads stay below the wait
+    __builtin_amdgcn_s_waitcnt(kWaitVm2);
+    asm volatile("" ::: "memory");
+    st.template rotate<RL>(lkr);
+  }
+  const f32x16 zero = {};
+  bf16x8 b[3][2];
+  b[0][0] = qf[0][0];
+  b[0][1] = qf[0][1];
+  b[1][0] = qf[1][0];
+  b[1][1] = qf[1][1];
+#pragma unroll
+  for (int ds = 0; ds < 4; ++ds) {
+    if (ds + 2 < 4) {
+      b[(ds + 2) % 3][0] = row_frag(lqw, lq, ds + 2, lg);
+      b[(ds + 2) % 3][1] = row_frag(lqw, 32 + lq, ds + 2, lg);
+    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+        w.s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[ds][kb], b[ds % 3][qb], ds ? w.s[kb][qb] : zero,
+                                                              0, 0, 0);
+  }
+}
 
 // One iteration of the ping-pong loop for tile i held in LDS slot S; ent holds
 // the entries of tiles i .. i+3 and is advanced by one.
-template <bool SAFE, int S, bool ROT>
+template <bool SAFE, int S, bool ROT, int RL>
 __device__ __forceinline__ void pp_step(WaveState& w, f32x4 (&ls)[2], bf16x8 sel, TileStage<kPPThreads, ROT>& st,
                                         VFrag& vf, const PPCtx<ROT>& c, int i, int (&ent)[4]) {
   constexpr int NS = PPCtx<ROT>::NS;
   constexpr int S1 = (S + 1) % NS, S2 = (S + 2) % NS, S3 = (S + 3) % NS;
-  // phase 1 (VALU): the softmax of tile i.  Without ROT the tiles arrive by
-  // direct copies issued in the MFMA phase, and this phase only moves a PARTIAL
-  // tile's mask metadata (loaded into registers one iteration before it is
-  // stored).  With ROT, tile i+2 (fetched one iteration ago) goes to the slot of
-  // tile i-1 and tile i+3 is fetched: the tile's (cos, sin) and the next tile's
-  // source rows are requested first, and the stash (which rotates) and the fetch
-  // (which gathers by those rows) come after the softmax, so that neither the
-  // rotation values nor the rows cross the MFMA phase in registers.
-  constexpr bool SW = !ROT;
-  if (!ROT) {
-    // masks of tile i+2 (loaded one iteration ago) to its slot; tile i+3's loaded
-    if (i + 2 < c.n) st.stash_mask(c.mtok[S2], c.mdrop[S2]);
-    if (i + 3 < c.n) st.fetch_mask(c.src(ent[3]), (ent[3] & 3) == AKV_TILE_PARTIAL, c.tok_drop, c.ver_src);
-  } else {
-    if (i + 2 < c.n) st.load_rot(c.rot_tab);
-    if (i + 3 < c.n) st.load_idx(c.src(ent[3]), c.ver_src, c.ver_run);
-  }
+  // phase 1 (VALU): the softmax of tile i.  The tiles arrive by direct copies
+  // issued in the MFMA phase, so this phase only moves a PARTIAL tile's mask
+  // metadata (loaded into registers one iteration before it is stored) and, with
+  // ROT, requests the (source, run) of tile i+3's rows for its copy (past the last
+  // tile, the last tile's again).
+  if (i + 2 < c.n) st.stash_mask(c.mtok[S2], c.mdrop[S2]);
+  if (i + 3 < c.n) st.fetch_mask(c.src(ent[3]), (ent[3] & 3) == AKV_TILE_PARTIAL, c.tok_drop, c.ver_src);
+  if (ROT) st.load_gather(c.src(ent[3]), c.ver_src, c.ver_run);
   __builtin_amdgcn_sched_barrier(0);
   // the entry the next iteration loads by, requested here: its scalar load is
   // waited for only at the barrier that ends this phase
   const int ent_next = c.entry(i + 4);
   const bool part = (ent[0] & 3) == AKV_TILE_PARTIAL;
   if (SAFE)
-    tile_softmax<!SW, SW>(w, part, c.mtok[S], c.mdrop[S], c.lk[S], c.lqw, c.q0, c.lq, c.lg);
+    tile_softmax<ROT, true>(w, part, c.mtok[S], c.mdrop[S], c.lk[S], c.lqw, c.q0, c.lq, c.lg);
   else
     tile_softmax_fast(w, part, c.mtok[S], c.mdrop[S], c.q0, c.lq, c.lg);
-  if (!ROT) {
-    // the copies this wave issued two iterations ago (and earlier) have landed in
-    // LDS before the barrier after which other waves may read them; the previous
-    // iteration's copies (its last two vector-memory instructions before this
-    // phase's mask loads) may stay in flight
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(kWaitVm2);
-  }
   if (ROT) {
-    __builtin_amdgcn_sched_barrier(0);
-    if (i + 2 < c.n) {
-      st.load_mask(c.tok_drop, c.ver_src);   // PARTIAL tiles only (rare): its wait is short-lived
-      st.stash(c.lk[S2], c.lv[S2], c.mtok[S2], c.mdrop[S2]);
-    }
-    if (i + 3 < c.n) st.fetch(c.src(ent[3]), (ent[3] & 3) == AKV_TILE_PARTIAL, c.hkv, c.hk, c.tok_drop, c.ver_src);
+    // P is complete here: the branches of this kernel's MFMA phase would otherwise
+    // let the compiler sink the exps past the barrier to their use in PV, where the
+    // MFMA wave would issue them itself
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          u32x4 t = __builtin_bit_cast(u32x4, w.pb[kb][qb][hf]);
+          asm volatile("" : "+v"(t));
+          w.pb[kb][qb][hf] = __builtin_bit_cast(bf16x8, t);
+        }
   }
-  if (SW) {  // the first PV quarter's V^T fragments; the others are read inside PV
-    read_vt_part<SW>(vf, c.lv[S], c.lane, 0);
-    read_vt_part<SW>(vf, c.lv[S], c.lane, 1);
-  }
+  // the copies this wave issued two iterations ago (and earlier) have landed in
+  // LDS before the barrier after which other waves may read them; the previous
+  // iteration's (its last two vector-memory instructions before this phase's mask
+  // loads, with ROT four when it also copied (cos, sin)) may stay in flight
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(ROT ? kWaitVm4 : kWaitVm2);
+  // the first PV quarter's V^T fragments; the others are read inside PV
+  read_vt_part<true>(vf, c.lv[S], c.lane, 0);
+  read_vt_part<true>(vf, c.lv[S], c.lane, 1);
   lds_barrier();
-  // phase 2 (MFMA): PV of tile i with the K fragments of tile i+1 read between its
-  // MFMAs (and, without ROT, tile i's own V^T fragments one quarter ahead); QK of
-  // tile i+1 (with ROT, with its V^T fragments read between those MFMAs).  After the
-  // last tile, slot S1 holds an older tile: its K reads are harmless and unused.
+  // phase 2 (MFMA): PV of tile i with the K fragments of tile i+1 and tile i's own
+  // V^T fragments (one quarter ahead) read between its MFMAs; QK of tile i+1, with
+  // ROT and a version tile i+2 woven with that tile's rotation.  After the last
+  // tile, slot S1 holds an older tile: its K reads are harmless and unused.
   __builtin_amdgcn_s_setprio(1);
   KFrag kf;
   bf16x8 qf[2][2];
-  if (SW) {
+  {
     // Each wave copies its rows of tile i+3 into the slot of tile i-1, whose last
     // reader (group B's softmax) passed a barrier before this phase.  The copy's
     // instructions issue between the first PV MFMAs, where this wave's issue slots
@@ -1051,17 +1071,34 @@ __device__ __forceinline__ void pp_step(WaveState& w, f32x4 (&ls)[2], bf16x8 sel
     // sink the softmax's exps past the barrier into this phase).
     const TileSrc ts = c.src(ent[3]);
     const TileCopy<TileStage<kPPThreads, ROT>> copy{st, ts, c.lk[S3], c.lv[S3], c.hkv, c.hk};
-    mfma_pv_read_k<!SAFE, SW>(w, vf, kf, qf, ls, sel, c.lk[S1], c.lqw, c.lq, c.lg, c.lv[S], c.lane, copy);
-  } else {
-    mfma_pv_read_k<!SAFE, SW>(w, vf, kf, qf, ls, sel, c.lk[S1], c.lqw, c.lq, c.lg, c.lv[S], c.lane);
+    mfma_pv_read_k<!SAFE, true, TileCopy<TileStage<kPPThreads, ROT>>, ROT>(w, vf, kf, qf, ls, sel, c.lk[S1],
+                                                                            c.lqw, c.lq, c.lg, c.lv[S], c.lane, copy);
   }
   __builtin_amdgcn_sched_barrier(0);
   // P of tile i is dead here, before the scores of tile i+1 are born: they share registers
-  if (i + 1 < c.n) mfma_qk_lq<SW>(w, kf, qf, c.lqw, c.lq, c.lg, vf, c.lv[S1], c.lane);
+  if (i + 1 < c.n) {
+    if (!ROT)
+      mfma_qk_lq<true>(w, kf, qf, c.lqw, c.lq, c.lg, vf, c.lv[S1], c.lane);
+    else if (c.ver(ent[2]))
+      mfma_qk_ql<true, RL>(w, kf, qf, c.lqw, c.lq, c.lg, st, c.lk[S2]);
+    else
+      mfma_qk_ql<false, RL>(w, kf, qf, c.lqw, c.lq, c.lg, st, c.lk[S2]);
+  }
+  // ROT: the (cos, sin) of tile i+3's version rows, for their rotation in the next
+  // iteration; issued after this iteration's rotation has read the region
+  const bool ver3 = ROT && c.ver(ent[3]);
+  if (ver3) {
+    __builtin_amdgcn_sched_barrier(0);
+    st.dma_rot(c.rot_tab);
+  }
   __builtin_amdgcn_s_setprio(0);
   // every wave's copies of one iteration ago (and earlier) have landed before the
   // barrier; this phase's stay in flight
-  if (SW) __builtin_amdgcn_s_waitcnt(kWaitVm2);
+  __builtin_amdgcn_sched_barrier(0);
+  if (ver3)
+    __builtin_amdgcn_s_waitcnt(kWaitVm4);
+  else
+    __builtin_amdgcn_s_waitcnt(kWaitVm2);
   lds_barrier();
   ent[0] = ent[1];
   ent[1] = ent[2];
@@ -1069,64 +1106,69 @@ __device__ __forceinline__ void pp_step(WaveState& w, f32x4 (&ls)[2], bf16x8 sel
   ent[3] = ent_next;
 }
 
-template <bool SAFE, bool ROT>
+template <bool SAFE, bool ROT, int RL>
 __device__ __forceinline__ void pp_pipeline(WaveState& w, f32x4 (&ls)[2], bf16x8 sel,
                                             TileStage<kPPThreads, ROT>& st, const PPCtx<ROT>& c, bool lag) {
-  constexpr bool SW = !ROT;
   int ent[4] = {c.entry(0), c.entry(1), c.entry(2), c.entry(3)};
-  if (SW) {
-    // tiles 0, 1 and 2 copied, tile 2's mask loaded
+  // Tiles 0, 1 and 2 copied and tile 2's mask loaded.  With ROT the version rows of
+  // tiles 0 and 1 are rotated here, one tile at a time through the wave's (cos,
+  // sin) region, and tile 2's by the first iteration; tile 2 is then copied (the
+  // last tile's rows past the end) even when it does not exist, as the loop does.
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      if (j < c.n) {
-        const TileSrc ts = c.src(ent[j]);
-        st.fetch_mask(ts, (ent[j] & 3) == AKV_TILE_PARTIAL, c.tok_drop, c.ver_src);
-        st.dma(ts, c.hkv, c.hk, c.lk[j], c.lv[j]);
-        st.stash_mask(c.mtok[j], c.mdrop[j]);
+  for (int j = 0; j < 2; ++j) {
+    if (j < c.n) {
+      const TileSrc ts = c.src(ent[j]);
+      st.fetch_mask(ts, (ent[j] & 3) == AKV_TILE_PARTIAL, c.tok_drop, c.ver_src);
+      if (ROT) st.load_gather(ts, c.ver_src, c.ver_run);
+      st.dma_tile(ts, c.hkv, c.hk, c.lk[j], c.lv[j]);
+      if (ROT && ts.ver) {
+        st.dma_rot(c.rot_tab);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);
+        asm volatile("" ::: "memory");
+        st.template rotate<RL>(c.lk[j]);
+        __builtin_amdgcn_sched_barrier(0);
       }
+      st.stash_mask(c.mtok[j], c.mdrop[j]);
     }
+  }
+  if (ROT) {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    const TileSrc ts = c.src(ent[2]);
+    if (c.n > 2) st.fetch_mask(ts, (ent[2] & 3) == AKV_TILE_PARTIAL, c.tok_drop, c.ver_src);
+    st.load_gather(ts, c.ver_src, c.ver_run);
+    st.dma_tile(ts, c.hkv, c.hk, c.lk[2], c.lv[2]);
+    if (ts.ver) {
+      __builtin_amdgcn_sched_barrier(0);
+      st.dma_rot(c.rot_tab);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  } else {
     if (c.n > 2) {
       st.fetch_mask(c.src(ent[2]), (ent[2] & 3) == AKV_TILE_PARTIAL, c.tok_drop, c.ver_src);
-      st.dma(c.src(ent[2]), c.hkv, c.hk, c.lk[2], c.lv[2]);
+      st.dma_tile(c.src(ent[2]), c.hkv, c.hk, c.lk[2], c.lv[2]);
     }
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
   }
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    if (!SW && j < c.n) {
-      const TileSrc ts = c.src(ent[j]);
-      st.load_idx(ts, c.ver_src, c.ver_run);
-      st.fetch(ts, (ent[j] & 3) == AKV_TILE_PARTIAL, c.hkv, c.hk, c.tok_drop, c.ver_src);
-      st.load_rot(c.rot_tab);
-      st.load_mask(c.tok_drop, c.ver_src);
-      st.stash(c.lk[j], c.lv[j], c.mtok[j], c.mdrop[j]);
-    }
-  }
-  if (!SW && c.n > 2) {
-    st.load_idx(c.src(ent[2]), c.ver_src, c.ver_run);
-    st.fetch(c.src(ent[2]), (ent[2] & 3) == AKV_TILE_PARTIAL, c.hkv, c.hk, c.tok_drop, c.ver_src);
-  }
   lds_barrier();
   if (lag) lds_barrier();
-  tile_qk<!SW, SW>(w, c.lk[0], c.lqw, c.lq, c.lg);
+  tile_qk<ROT, true>(w, c.lk[0], c.lqw, c.lq, c.lg);
   VFrag vf;
-  if (!SW) read_vt<SW>(vf, c.lv[0], c.lane);
   lds_barrier();
   for (int i = 0; i < c.n; i += PPCtx<ROT>::NS) {
-    pp_step<SAFE, 0, ROT>(w, ls, sel, st, vf, c, i, ent);
+    pp_step<SAFE, 0, ROT, RL>(w, ls, sel, st, vf, c, i, ent);
     if (i + 1 >= c.n) break;
-    pp_step<SAFE, 1, ROT>(w, ls, sel, st, vf, c, i + 1, ent);
+    pp_step<SAFE, 1, ROT, RL>(w, ls, sel, st, vf, c, i + 1, ent);
     if (i + 2 >= c.n) break;
-    pp_step<SAFE, 2, ROT>(w, ls, sel, st, vf, c, i + 2, ent);
-    if (PPCtx<ROT>::NS == 4) {
-      if (i + 3 >= c.n) break;
-      pp_step<SAFE, 3 % PPCtx<ROT>::NS, ROT>(w, ls, sel, st, vf, c, i + 3, ent);
-    }
+    pp_step<SAFE, 2, ROT, RL>(w, ls, sel, st, vf, c, i + 2, ent);
+    if (i + 3 >= c.n) break;
+    pp_step<SAFE, 3, ROT, RL>(w, ls, sel, st, vf, c, i + 3, ent);
   }
   // no copy (those past the last tile included) is still in flight when the
   // slots are next written
-  if (SW) __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
   if (!lag) lds_barrier();
 }
 
@@ -1134,9 +1176,10 @@ __device__ __forceinline__ void pp_pipeline(WaveState& w, f32x4 (&ls)[2], bf16x8
 // product and accumulation of the PV step far from overflow.
 constexpr float kFastHi = 1.2676506002282294e30f;  // 2^100
 
-// ROT: version rows are rotated from the source keys while tiles are staged
-// (TileStage), with ver_run / rot_tab, instead of read from version buffers.
-template <bool ROT>
+// ROT: version rows are gathered from the source keys and values and their keys
+// rotated in LDS (TileStage), with ver_run / rot_tab, instead of read from version
+// buffers; RL is then the pair layout.
+template <bool ROT, int RL = AKV_ROPE_HALF>
 __global__ __launch_bounds__(kPPThreads) void seg_attn_bf16_pp(AKV_ATTN_PARAMS, const int* __restrict__ ver_run,
                                                                const float* __restrict__ rot_tab) {
   constexpr int GROUP = 8;
@@ -1145,7 +1188,7 @@ __global__ __launch_bounds__(kPPThreads) void seg_attn_bf16_pp(AKV_ATTN_PARAMS, 
   __shared__ __attribute__((aligned(16))) uint16_t lv[Ctx::NS][Ctx::VSZ];
   __shared__ int mtok[Ctx::NS][BK], mdrop[Ctx::NS][BK];
   __shared__ __attribute__((aligned(16))) uint16_t lqs[GROUP][64 * KP];
-  __shared__ __attribute__((aligned(16))) float rtab[ROT ? GROUP * 640 : 4];  // ROT: 2.5 KB per wave
+  __shared__ __attribute__((aligned(16))) float rtab[ROT ? GROUP * 512 : 4];  // ROT: 2 KB per wave
   __shared__ int redo;
 
   const int hk = blockIdx.x % hkv;
@@ -1165,14 +1208,10 @@ __global__ __launch_bounds__(kPPThreads) void seg_attn_bf16_pp(AKV_ATTN_PARAMS, 
   if (threadIdx.x == 0) redo = 0;  // published by the first barrier of the pipeline
 
   WaveState w;
-  if (ROT)
-    load_q<true>(w, lqw, q, q0, q1, hq, h, lq, lg, sl2, tok_pos, rq);
-  else
-    load_q<false>(w, lqw, q, q0, q1, hq, h, lq, lg, sl2, tok_pos, rq);
+  load_q<ROT>(w, lqw, q, q0, q1, hq, h, lq, lg, sl2, tok_pos, rq);  // ROT: Q' in LDS
   TileStage<kPPThreads, ROT> st;
   st.wave_s = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  st.layout = rq.layout;
-  st.rl = rtab + (ROT ? st.wave_s * 640 : 0);
+  st.rl = rtab + (ROT ? st.wave_s * 512 : 0);
   const bf16x8 sel = colsum_selector(lane);
   f32x4 ls[2] = {};
   Ctx c;
@@ -1187,7 +1226,7 @@ __global__ __launch_bounds__(kPPThreads) void seg_attn_bf16_pp(AKV_ATTN_PARAMS, 
   c.tiles = tiles + t0;
   c.k = k;
   c.v = v;
-  c.kver = ROT ? k : kver;   // rotated staging gathers version rows from the source keys
+  c.kver = ROT ? k : kver;   // ROT gathers version rows from the source keys
   c.vver = ROT ? v : vver;
   c.tok_drop = tok_drop;
   c.ver_src = ver_src;
@@ -1205,7 +1244,7 @@ __global__ __launch_bounds__(kPPThreads) void seg_attn_bf16_pp(AKV_ATTN_PARAMS, 
   c.lq = lq;
   c.lg = lg;
   c.lane = lane;
-  pp_pipeline<false, ROT>(w, ls, sel, st, c, lag);
+  pp_pipeline<false, ROT, RL>(w, ls, sel, st, c, lag);
   // Accept the fast pass when every real query column's sum lies in [2^-40, 2^100]
   // (also false for inf/NaN); otherwise the workgroup redoes the item with the
   // rescaling softmax.
@@ -1220,7 +1259,7 @@ __global__ __launch_bounds__(kPPThreads) void seg_attn_bf16_pp(AKV_ATTN_PARAMS, 
   if (__builtin_amdgcn_readfirstlane(redo)) {
     asm volatile("");  // rare: keep the second pipeline out of the common path
     reset_acc(w);  // O, offsets and sums (Q' stays where it is)
-    pp_pipeline<true, ROT>(w, ls, sel, st, c, lag);
+    pp_pipeline<true, ROT, RL>(w, ls, sel, st, c, lag);
   } else {
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) w.lrun[qb] = ls[qb][0];
@@ -1341,7 +1380,9 @@ int launch_segment_attention(const AttnArgs& a, void* stream) {
             hipLaunchKernelGGL(rot_table_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a.run_delta,
                                a.n_runs, a.d / 2, a.rq, a.rot_tab);
           }
-          hipLaunchKernelGGL(seg_attn_bf16_pp<true>, dim3((unsigned)blocks), dim3(512), 0, s, (const uint16_t*)a.q,
+          auto kern = a.rq.layout == AKV_ROPE_HALF ? seg_attn_bf16_pp<true, AKV_ROPE_HALF>
+                                                   : seg_attn_bf16_pp<true, AKV_ROPE_INTERLEAVED>;
+          hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(512), 0, s, (const uint16_t*)a.q,
                              (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.k_ver,
                              (const uint16_t*)a.v_ver, a.item_desc, a.tiles, a.order, a.tok_drop, a.ver_src,
                              (uint16_t*)a.out, a.lse, a.hq, a.hkv, a.scale, a.tok_pos, a.rq, a.ver_run,

@@ -347,14 +347,18 @@ int build_plan(const akv_op* ops, int64_t n_ops, int32_t bq, int32_t bk, akv_pla
     }
 
     // Device image layout.  Version rows carry only (src, to, run); kernels read the
-    // source's append position and drop boundary through tok_pos / tok_drop.
+    // source's append position and drop boundary through tok_pos / tok_drop.  The
+    // src and run tables are followed by kVerPad zero entries: the fused attention
+    // loads them eight rows at a time from a tile's first row, past a ragged last
+    // tile's end.
     uint64_t off = 0;
     auto place = [&](uint64_t bytes) { uint64_t o = off; off += (bytes + 255) & ~uint64_t(255); return o; };
     p->off_tok_pos = place(4 * T);
     p->off_tok_drop = place(4 * T);
-    p->off_ver_src = place(4 * ver_total);
+    constexpr uint64_t kVerPad = 64;
+    p->off_ver_src = place(4 * ((uint64_t)ver_total + kVerPad));
     p->off_ver_to = place(4 * ver_total);
-    p->off_ver_run = place(4 * ver_total);
+    p->off_ver_run = place(4 * ((uint64_t)ver_total + kVerPad));
     p->off_run_delta = place(4 * (uint64_t)p->n_runs);
     p->off_item_desc = place(4 * (uint64_t)n_items * ID_WORDS);
     p->off_tiles = place(4 * (uint64_t)n_tiles);
@@ -373,6 +377,8 @@ int build_plan(const akv_op* ops, int64_t n_ops, int32_t bq, int32_t bk, akv_pla
       std::memcpy(p->image.get() + p->off_ver_run + 4 * lo, p->ver_run.data() + lo, 4 * (hi - lo));
     });
     if (p->n_runs) std::memcpy(p->image.get() + p->off_run_delta, p->run_delta.data(), 4 * p->n_runs);
+    std::memset(p->image.get() + p->off_ver_src + 4 * ver_total, 0, 4 * kVerPad);
+    std::memset(p->image.get() + p->off_ver_run + 4 * ver_total, 0, 4 * kVerPad);
 
     // T6 tile lists, items and item descriptors.
     p->tiles.resize(n_tiles);
