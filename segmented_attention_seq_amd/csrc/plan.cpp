@@ -413,19 +413,22 @@ int build_plan(const akv_op* ops, int64_t n_ops, int32_t bq, int32_t bk, akv_pla
     });
     p->tile_ptr[n_items] = (int32_t)n_tiles;
 
-    // Work order: stretch by stretch, the stretch with the most tiles first (ties in
-    // stretch order), and within a stretch its items longest first (stable).  The
+    // Work order: stretch by stretch, the stretch with the longest item first (ties
+    // in stretch order), and within a stretch its items longest first (stable).  The
     // workgroups an XCD runs at once then mostly belong to one stretch and walk the
-    // same K/V tiles, so more of those reads hit its L2; the last items are short
-    // ones of small stretches, which keeps the tail of the launch short.
+    // same K/V tiles, so more of those reads hit its L2; the order ends with the
+    // shortest items of the stretch whose items are shortest, which keeps the tail
+    // of the launch short.
     p->item_order.resize(n_items);
     std::iota(p->item_order.begin(), p->item_order.end(), 0);
     {
       std::vector<int64_t> work(S, 0);
       std::vector<int32_t> st_of(n_items);
       for (int64_t e = 0; e < S; ++e) {
-        work[e] = cnt[item[e + 1]] - cnt[item[e]];
-        for (int64_t it = item[e]; it < item[e + 1]; ++it) st_of[it] = (int32_t)e;
+        for (int64_t it = item[e]; it < item[e + 1]; ++it) {
+          st_of[it] = (int32_t)e;
+          work[e] = std::max<int64_t>(work[e], cnt[it + 1] - cnt[it]);
+        }
       }
       std::stable_sort(p->item_order.begin(), p->item_order.end(), [&](int32_t a, int32_t b) {
         const int32_t ea = st_of[a], eb = st_of[b];

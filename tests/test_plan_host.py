@@ -99,10 +99,12 @@ def _compare(lens, drop, repos, bq, bk, tiles="full", rng=None):
     order = t["item_order"]
     assert sorted(order.tolist()) == list(range(n_items))
     cnt = np.diff(t["tile_ptr"])
-    # stretch by stretch (most tiles first, ties by index), items longest first inside
+    # stretch by stretch (longest item first, ties by index), items longest first inside
     st = t["items"].reshape(-1, 2)[:, 0]
-    work = np.bincount(st, weights=cnt, minlength=int(st.max()) + 1 if st.size else 0)
-    key = sorted(range(n_items), key=lambda i: (-work[st[i]], st[i], -cnt[i], i))
+    longest = {}
+    for i in range(n_items):
+        longest[st[i]] = max(longest.get(st[i], 0), cnt[i])
+    key = sorted(range(n_items), key=lambda i: (-longest[st[i]], st[i], -cnt[i], i))
     assert order.tolist() == key
     kt, cls = t["tiles"] >> 2, t["tiles"] & 3
     assert info["n_full"] == int((cls == akv.TILE_FULL).sum())
