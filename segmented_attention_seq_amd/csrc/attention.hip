@@ -933,15 +933,17 @@ __global__ __launch_bounds__(64 * GROUP, 2) void seg_attn_bf16(AKV_ATTN_PARAMS) 
 // SAFE = false is the fast pass (offset 0, column sums on the matrix cores);
 // SAFE = true is the lazily-rescaled softmax with per-tile range checks.
 constexpr int kPPThreads = 512;
-// The tile ring: four LDS slots of 16 KB (K and V, swizzled unpadded rows), filled
-// by direct copies.
-template <bool ROT>
+// The tile ring: four LDS slots of HPW x 16 KB (K and V of each of the workgroup's
+// HPW kv heads, swizzled unpadded rows), filled by direct copies.  A wave reads the
+// tiles of its own kv head (koff into each slot).
+template <bool ROT, int HPW = 1>
 struct PPCtx {
   static constexpr int NS = 4;
   static constexpr int KSZ = BK * D;
   static constexpr int VSZ = BK * D;
-  uint16_t* lk[NS];  // K and V tile of each slot
+  uint16_t* lk[NS];  // K and V tiles of each slot (the first head's; the next head's KSZ / VSZ on)
   uint16_t* lv[NS];
+  int koff;          // this wave's head within the slot times KSZ (0 with one head)
   int (*mtok)[BK];
   int (*mdrop)[BK];
   const uint16_t* lqw;
@@ -950,15 +952,20 @@ struct PPCtx {
   const int *tok_drop, *ver_src;
   const int* ver_run;   // ROT: run of each version row
   const float* rot_tab; // ROT: (cos, sin) per run and frequency
-  int n, nvt, voff, r, tb, te, hkv, hk, q0, lq, lg, lane;
+  int n, nvt, voff, r, tb, te, hkv, hk, q0, lq, lg, lane;  // hk: the workgroup's first kv head
   __device__ __forceinline__ TileSrc src(int ent) const { return tile_src(ent, nvt, voff, r, tb, te, k, v, kver, vver); }
+  // this wave's K and V tile in slot j
+  __device__ __forceinline__ uint16_t* rk(int j) const { return HPW == 1 ? lk[j] : lk[j] + koff; }
+  __device__ __forceinline__ uint16_t* rv(int j) const { return HPW == 1 ? lv[j] : lv[j] + koff; }
   // entry of tile t, or of the last tile past the end (n >= 1; the caller ignores it)
   __device__ __forceinline__ int entry(int t) const { return tiles[min(t, n - 1)]; }
   __device__ __forceinline__ bool ver(int ent) const { return (ent >> 2) < nvt; }
 };
 
 // A tile copy issued from inside the MFMA phase (mfma_pv_read_k calls it).
-template <class Stage>
+// With HPW kv heads per workgroup, the rows of every head are copied into their
+// part of the slot.
+template <class Stage, int HPW = 1>
 struct TileCopy {
   Stage& st;
   const TileSrc& ts;
@@ -966,7 +973,10 @@ struct TileCopy {
   int hkv, hk;
   static constexpr bool kActive = true;
   static constexpr int kValu = Stage::kRot ? 10 : 8;  // ALU instructions between two of its MFMAs
-  __device__ __forceinline__ void operator()() const { st.dma_tile(ts, hkv, hk, dk, dv); }
+  __device__ __forceinline__ void operator()() const {
+#pragma unroll
+    for (int e = 0; e < HPW; ++e) st.dma_tile(ts, hkv, hk + e, dk + e * BK * D, dv + e * BK * D);
+  }
 };
 
 // QK of the ROT kernel, which keeps Q' in the wave's LDS rows: the first two d
@@ -1008,10 +1018,12 @@ __device__ __forceinline__ void mfma_qk_ql(WaveState& w, const KFrag& f, const b
 
 // One iteration of the ping-pong loop for tile i held in LDS slot S; ent holds
 // the entries of tiles i .. i+3 and is advanced by one.
-template <bool SAFE, int S, bool ROT, int RL>
+template <bool SAFE, int S, bool ROT, int RL, int HPW = 1>
 __device__ __forceinline__ void pp_step(WaveState& w, f32x4 (&ls)[2], bf16x8 sel, TileStage<kPPThreads, ROT>& st,
-                                        VFrag& vf, const PPCtx<ROT>& c, int i, int (&ent)[4]) {
-  constexpr int NS = PPCtx<ROT>::NS;
+                                        VFrag& vf, const PPCtx<ROT, HPW>& c, int i, int (&ent)[4]) {
+  constexpr int NS = PPCtx<ROT, HPW>::NS;
+  // vector-memory instructions of one iteration's tile copies (two per head)
+  constexpr int kWaitIter = (ROT || HPW == 2) ? kWaitVm4 : kWaitVm2;
   constexpr int S1 = (S + 1) % NS, S2 = (S + 2) % NS, S3 = (S + 3) % NS;
   // phase 1 (VALU): the softmax of tile i.  The tiles arrive by direct copies
   // issued in the MFMA phase, so this phase only moves a PARTIAL tile's mask
@@ -1027,7 +1039,7 @@ __device__ __forceinline__ void pp_step(WaveState& w, f32x4 (&ls)[2], bf16x8 sel
   const int ent_next = c.entry(i + 4);
   const bool part = (ent[0] & 3) == AKV_TILE_PARTIAL;
   if (SAFE)
-    tile_softmax<ROT, true>(w, part, c.mtok[S], c.mdrop[S], c.lk[S], c.lqw, c.q0, c.lq, c.lg);
+    tile_softmax<ROT, true>(w, part, c.mtok[S], c.mdrop[S], c.rk(S), c.lqw, c.q0, c.lq, c.lg);
   else
     tile_softmax_fast(w, part, c.mtok[S], c.mdrop[S], c.q0, c.lq, c.lg);
   if (ROT) {
@@ -1048,12 +1060,13 @@ __device__ __forceinline__ void pp_step(WaveState& w, f32x4 (&ls)[2], bf16x8 sel
   // the copies this wave issued two iterations ago (and earlier) have landed in
   // LDS before the barrier after which other waves may read them; the previous
   // iteration's (its last two vector-memory instructions before this phase's mask
-  // loads, with ROT four when it also copied (cos, sin)) may stay in flight
+  // loads, four with ROT when it also copied (cos, sin), or with two kv heads) may
+  // stay in flight
   __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_waitcnt(ROT ? kWaitVm4 : kWaitVm2);
+  __builtin_amdgcn_s_waitcnt(kWaitIter);
   // the first PV quarter's V^T fragments; the others are read inside PV
-  read_vt_part<true>(vf, c.lv[S], c.lane, 0);
-  read_vt_part<true>(vf, c.lv[S], c.lane, 1);
+  read_vt_part<true>(vf, c.rv(S), c.lane, 0);
+  read_vt_part<true>(vf, c.rv(S), c.lane, 1);
   lds_barrier();
   // phase 2 (MFMA): PV of tile i with the K fragments of tile i+1 and tile i's own
   // V^T fragments (one quarter ahead) read between its MFMAs; QK of tile i+1, with
@@ -1070,15 +1083,16 @@ __device__ __forceinline__ void pp_step(WaveState& w, f32x4 (&ls)[2], bf16x8 sel
     // to a slot that is not read again (no branch: a branch here lets the compiler
     // sink the softmax's exps past the barrier into this phase).
     const TileSrc ts = c.src(ent[3]);
-    const TileCopy<TileStage<kPPThreads, ROT>> copy{st, ts, c.lk[S3], c.lv[S3], c.hkv, c.hk};
-    mfma_pv_read_k<!SAFE, true, TileCopy<TileStage<kPPThreads, ROT>>, ROT>(w, vf, kf, qf, ls, sel, c.lk[S1],
-                                                                            c.lqw, c.lq, c.lg, c.lv[S], c.lane, copy);
+    const TileCopy<TileStage<kPPThreads, ROT>, HPW> copy{st, ts, c.lk[S3], c.lv[S3], c.hkv, c.hk};
+    mfma_pv_read_k<!SAFE, true, TileCopy<TileStage<kPPThreads, ROT>, HPW>, ROT>(w, vf, kf, qf, ls, sel, c.rk(S1),
+                                                                                 c.lqw, c.lq, c.lg, c.rv(S), c.lane,
+                                                                                 copy);
   }
   __builtin_amdgcn_sched_barrier(0);
   // P of tile i is dead here, before the scores of tile i+1 are born: they share registers
   if (i + 1 < c.n) {
     if (!ROT)
-      mfma_qk_lq<true>(w, kf, qf, c.lqw, c.lq, c.lg, vf, c.lv[S1], c.lane);
+      mfma_qk_lq<true>(w, kf, qf, c.lqw, c.lq, c.lg, vf, c.rv(S1), c.lane);
     else if (c.ver(ent[2]))
       mfma_qk_ql<true, RL>(w, kf, qf, c.lqw, c.lq, c.lg, st, c.lk[S2]);
     else
@@ -1098,7 +1112,7 @@ __device__ __forceinline__ void pp_step(WaveState& w, f32x4 (&ls)[2], bf16x8 sel
   if (ver3)
     __builtin_amdgcn_s_waitcnt(kWaitVm4);
   else
-    __builtin_amdgcn_s_waitcnt(kWaitVm2);
+    __builtin_amdgcn_s_waitcnt(kWaitIter == kWaitVm4 && !ROT ? kWaitVm4 : kWaitVm2);
   lds_barrier();
   ent[0] = ent[1];
   ent[1] = ent[2];
@@ -1106,9 +1120,9 @@ __device__ __forceinline__ void pp_step(WaveState& w, f32x4 (&ls)[2], bf16x8 sel
   ent[3] = ent_next;
 }
 
-template <bool SAFE, bool ROT, int RL>
+template <bool SAFE, bool ROT, int RL, int HPW = 1>
 __device__ __forceinline__ void pp_pipeline(WaveState& w, f32x4 (&ls)[2], bf16x8 sel,
-                                            TileStage<kPPThreads, ROT>& st, const PPCtx<ROT>& c, bool lag) {
+                                            TileStage<kPPThreads, ROT>& st, const PPCtx<ROT, HPW>& c, bool lag) {
   int ent[4] = {c.entry(0), c.entry(1), c.entry(2), c.entry(3)};
   // Tiles 0, 1 and 2 copied and tile 2's mask loaded.  With ROT the version rows of
   // tiles 0 and 1 are rotated here, one tile at a time through the wave's (cos,
@@ -1120,7 +1134,8 @@ __device__ __forceinline__ void pp_pipeline(WaveState& w, f32x4 (&ls)[2], bf16x8
       const TileSrc ts = c.src(ent[j]);
       st.fetch_mask(ts, (ent[j] & 3) == AKV_TILE_PARTIAL, c.tok_drop, c.ver_src);
       if (ROT) st.load_gather(ts, c.ver_src, c.ver_run);
-      st.dma_tile(ts, c.hkv, c.hk, c.lk[j], c.lv[j]);
+#pragma unroll
+      for (int e = 0; e < HPW; ++e) st.dma_tile(ts, c.hkv, c.hk + e, c.lk[j] + e * BK * D, c.lv[j] + e * BK * D);
       if (ROT && ts.ver) {
         st.dma_rot(c.rot_tab);
         __builtin_amdgcn_sched_barrier(0);
@@ -1147,24 +1162,26 @@ __device__ __forceinline__ void pp_pipeline(WaveState& w, f32x4 (&ls)[2], bf16x8
   } else {
     if (c.n > 2) {
       st.fetch_mask(c.src(ent[2]), (ent[2] & 3) == AKV_TILE_PARTIAL, c.tok_drop, c.ver_src);
-      st.dma_tile(c.src(ent[2]), c.hkv, c.hk, c.lk[2], c.lv[2]);
+#pragma unroll
+      for (int e = 0; e < HPW; ++e)
+        st.dma_tile(c.src(ent[2]), c.hkv, c.hk + e, c.lk[2] + e * BK * D, c.lv[2] + e * BK * D);
     }
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
   }
   lds_barrier();
   if (lag) lds_barrier();
-  tile_qk<ROT, true>(w, c.lk[0], c.lqw, c.lq, c.lg);
+  tile_qk<ROT, true>(w, c.rk(0), c.lqw, c.lq, c.lg);
   VFrag vf;
   lds_barrier();
-  for (int i = 0; i < c.n; i += PPCtx<ROT>::NS) {
-    pp_step<SAFE, 0, ROT, RL>(w, ls, sel, st, vf, c, i, ent);
+  for (int i = 0; i < c.n; i += PPCtx<ROT, HPW>::NS) {
+    pp_step<SAFE, 0, ROT, RL, HPW>(w, ls, sel, st, vf, c, i, ent);
     if (i + 1 >= c.n) break;
-    pp_step<SAFE, 1, ROT, RL>(w, ls, sel, st, vf, c, i + 1, ent);
+    pp_step<SAFE, 1, ROT, RL, HPW>(w, ls, sel, st, vf, c, i + 1, ent);
     if (i + 2 >= c.n) break;
-    pp_step<SAFE, 2, ROT, RL>(w, ls, sel, st, vf, c, i + 2, ent);
+    pp_step<SAFE, 2, ROT, RL, HPW>(w, ls, sel, st, vf, c, i + 2, ent);
     if (i + 3 >= c.n) break;
-    pp_step<SAFE, 3, ROT, RL>(w, ls, sel, st, vf, c, i + 3, ent);
+    pp_step<SAFE, 3, ROT, RL, HPW>(w, ls, sel, st, vf, c, i + 3, ent);
   }
   // no copy (those past the last tile included) is still in flight when the
   // slots are next written
@@ -1179,27 +1196,36 @@ constexpr float kFastHi = 1.2676506002282294e30f;  // 2^100
 // ROT: version rows are gathered from the source keys and values and their keys
 // rotated in LDS (TileStage), with ver_run / rot_tab, instead of read from version
 // buffers; RL is then the pair layout.
-template <bool ROT, int RL = AKV_ROPE_HALF>
+//
+// HPW = 2 (4 query heads per kv head, no ROT): the workgroup takes two kv heads,
+// group A (waves 0-3) the first one's four query heads and group B (waves 4-7) the
+// second one's; each slot of the ring holds both heads' tiles, so the K/V ring
+// takes 128 KB and the output is stored straight from the accumulators.
+template <bool ROT, int RL = AKV_ROPE_HALF, int HPW = 1>
 __global__ __launch_bounds__(kPPThreads) void seg_attn_bf16_pp(AKV_ATTN_PARAMS, const int* __restrict__ ver_run,
                                                                const float* __restrict__ rot_tab) {
-  constexpr int GROUP = 8;
-  using Ctx = PPCtx<ROT>;
-  __shared__ __attribute__((aligned(16))) uint16_t lk[Ctx::NS][Ctx::KSZ];
-  __shared__ __attribute__((aligned(16))) uint16_t lv[Ctx::NS][Ctx::VSZ];
+  static_assert(HPW == 1 || (HPW == 2 && !ROT), "two kv heads per workgroup only with version buffers");
+  constexpr int GROUP = 8 / HPW;  // query heads per kv head
+  using Ctx = PPCtx<ROT, HPW>;
+  __shared__ __attribute__((aligned(16))) uint16_t lk[Ctx::NS][HPW * Ctx::KSZ];
+  __shared__ __attribute__((aligned(16))) uint16_t lv[Ctx::NS][HPW * Ctx::VSZ];
   __shared__ int mtok[Ctx::NS][BK], mdrop[Ctx::NS][BK];
-  __shared__ __attribute__((aligned(16))) uint16_t lqs[GROUP][64 * KP];
+  __shared__ __attribute__((aligned(16))) uint16_t lqs[HPW == 1 ? GROUP : 1][64 * KP];
   __shared__ __attribute__((aligned(16))) float rtab[ROT ? GROUP * 512 : 4];  // ROT: 2 KB per wave
   __shared__ int redo;
 
-  const int hk = blockIdx.x % hkv;
-  const int item = order[blockIdx.x / hkv];
+  const int npair = hkv / HPW;
+  const int hk0 = (blockIdx.x % npair) * HPW;  // the workgroup's first kv head
+  const int item = order[blockIdx.x / npair];
   const int* dsc = item_desc + item * ID_WORDS;
   const int q0 = dsc[ID_QBEGIN], q1 = dsc[ID_QEND], tb = dsc[ID_TB], te = dsc[ID_TE];
   const int r = dsc[ID_R], voff = dsc[ID_VEROFF], t0 = dsc[ID_TILE0], t1 = dsc[ID_TILE1];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int h = hk * GROUP + wave;
+  const int hsel = HPW == 1 ? 0 : wave >> 2;  // this wave's kv head within the workgroup
+  const int hk = hk0 + hsel;
+  const int h = hk * GROUP + (wave & (GROUP - 1));
   const int lq = lane & 31, lg = lane >> 5;
-  uint16_t* lqw = lqs[wave];  // this wave's Q' rows (written and read by this wave only)
+  uint16_t* lqw = lqs[HPW == 1 ? wave : 0];  // this wave's Q' rows (written and read by this wave only)
   const bool lag = wave >= 4;  // group B
   const int nvt = (r + BK - 1) / BK;
   const float sl2 = scale * kLog2e;
@@ -1239,12 +1265,13 @@ __global__ __launch_bounds__(kPPThreads) void seg_attn_bf16_pp(AKV_ATTN_PARAMS, 
   c.tb = tb;
   c.te = te;
   c.hkv = hkv;
-  c.hk = hk;
+  c.hk = hk0;
+  c.koff = hsel * Ctx::KSZ;
   c.q0 = q0;
   c.lq = lq;
   c.lg = lg;
   c.lane = lane;
-  pp_pipeline<false, ROT, RL>(w, ls, sel, st, c, lag);
+  pp_pipeline<false, ROT, RL, HPW>(w, ls, sel, st, c, lag);
   // Accept the fast pass when every real query column's sum lies in [2^-40, 2^100]
   // (also false for inf/NaN); otherwise the workgroup redoes the item with the
   // rescaling softmax.
@@ -1259,12 +1286,12 @@ __global__ __launch_bounds__(kPPThreads) void seg_attn_bf16_pp(AKV_ATTN_PARAMS, 
   if (__builtin_amdgcn_readfirstlane(redo)) {
     asm volatile("");  // rare: keep the second pipeline out of the common path
     reset_acc(w);  // O, offsets and sums (Q' stays where it is)
-    pp_pipeline<true, ROT, RL>(w, ls, sel, st, c, lag);
+    pp_pipeline<true, ROT, RL, HPW>(w, ls, sel, st, c, lag);
   } else {
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) w.lrun[qb] = ls[qb][0];
   }
-  store_out<true>(w, out, lse, q0, q1, hq, h, lq, lg, lqw, lane);
+  store_out<HPW == 1>(w, out, lse, q0, q1, hq, h, lq, lg, lqw, lane);
 }
 
 // (cos, sin) of every version run's shift for every frequency: table[run][i] =
@@ -1372,7 +1399,17 @@ int launch_segment_attention(const AttnArgs& a, void* stream) {
     switch (grp) {
       case 1: AKV_LAUNCH_BF16(1); break;
       case 2: AKV_LAUNCH_BF16(2); break;
-      case 4: AKV_LAUNCH_BF16(4); break;
+      case 4:
+        if (a.hkv % 2 == 0) {  // two kv heads per workgroup: the ping-pong pipeline
+          hipLaunchKernelGGL((seg_attn_bf16_pp<false, AKV_ROPE_HALF, 2>), dim3((unsigned)(blocks / 2)), dim3(512), 0, s,
+                             (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                             (const uint16_t*)a.k_ver, (const uint16_t*)a.v_ver, a.item_desc, a.tiles, a.order,
+                             a.tok_drop, a.ver_src, (uint16_t*)a.out, a.lse, a.hq, a.hkv, a.scale, a.tok_pos, a.rq,
+                             nullptr, nullptr);
+        } else {
+          AKV_LAUNCH_BF16(4);
+        }
+        break;
       case 8:
         if (a.fused) {
           if (a.n_runs > 0) {

@@ -303,6 +303,8 @@ SMALL = [
     (8, 3100, 3, "every", 16, 4),
     (5, 1234, 1, "every", 8, 8),
     (4, 999, 2, "every", 16, 8),
+    (4, 2000, 1, "every", 32, 8),   # 4 query heads per kv head: two kv heads per workgroup
+    (5, 1600, 2, "every", 12, 3),   # 4 per kv head with an odd kv head count: one-wave-per-head kernel
 ]
 
 
@@ -333,11 +335,12 @@ EDGE = {
 }
 
 
+@pytest.mark.parametrize("hq", [16, 8])
 @pytest.mark.parametrize("name", sorted(EDGE))
-def test_edge_cases_bf16(name):
+def test_edge_cases_bf16(name, hq):
     tr = EDGE[name]
     tr.name = name
-    plan, qkv, out, lse = _run_restore(tr, 16, 2, 64, bf16=True, seed=71)
+    plan, qkv, out, lse = _run_restore(tr, hq, 2, 64, bf16=True, seed=71)
     _check_rows(tr, qkv, out, lse, bf16=True)
 
 
@@ -357,6 +360,19 @@ def test_short_items_every_tile_count(repos):
     assert set(range(1, 5)) <= counts and (repos or set(range(1, 9)) <= counts)
     assert torch.equal(o0.view(torch.int16), o1.view(torch.int16)) and torch.equal(l0, l1)
     _check_rows(tr, (q, k, v), o0, l0, bf16=True)
+
+
+@pytest.mark.parametrize("repos", [False, True])
+def test_two_kv_heads_per_workgroup_every_tile_count(repos):
+    """4 query heads per kv head run the ping-pong kernel with two kv heads per
+    workgroup (each slot of the tile ring holds both heads' tiles): work items of 1
+    to 8 key tiles, with and without version rows, every row checked."""
+    lens, rp = ([512], []) if not repos else ([256, 256], [0])
+    tr = workload.Trajectory(lens, ["x"] * len(lens), {}, rp, name=f"two-heads-{repos}")
+    plan, qkv, out, lse = _run_restore(tr, 8, 2, 64, bf16=True, seed=83)
+    counts = set(np.diff(plan.tables()["tile_ptr"]).tolist())
+    assert set(range(1, 5)) <= counts and (repos or set(range(1, 9)) <= counts)
+    _check_rows(tr, qkv, out, lse, bf16=True)
 
 
 def test_empty_plan_and_unsupported():
