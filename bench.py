@@ -376,6 +376,8 @@ def main():
         "roofline": {"bound": "mfma", "kernel": ("segment attention (seg_attn_bf16_pp, 8 query heads per kv head"
                                                    + (", version rows rotated at staging)" if fused else ")")
                                                    if hq // hkv == 8 else
+                                                   "segment attention (seg_attn_bf16_pp, 4 query heads per kv head, "
+                                                   "two kv heads per workgroup)" if hq // hkv == 4 and hkv % 2 == 0 else
                                                    f"segment attention (seg_attn_bf16<{hq // hkv}>)"),
                      "achieved": attn_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": (attn_tflops / PEAK_BF16_TFLOPS) if attn_tflops else None,
