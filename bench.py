@@ -53,6 +53,8 @@ def parse_args():
     ap.add_argument("--hq", type=int, default=64, choices=[8, 16, 32, 64],
                     help="query heads of the restore (8 kv heads): 64 is the workloads' 64/8 GQA; "
                          "32, 16 and 8 run the 4-, 2- and 1-head-group kernel on seeded synthetic queries")
+    ap.add_argument("--bq", type=int, default=0,
+                    help="query tile of the plan (0: the library's choice for the head counts)")
     ap.add_argument("--fused-versions", action="store_true",
                     help="build no version buffers: the attention rotates version rows as it stages key tiles")
     ap.add_argument("--repos-sets", type=int, default=4, help="repos buffer sets rotated per step")
@@ -64,6 +66,21 @@ def parse_args():
                     help="before timing, run an elementwise multiply reading and writing this many MiB "
                          "(3 times) so hardware byte counters can be scaled against a known transfer")
     return ap.parse_args()
+
+
+def attn_kernel_name(hq, hkv, bq, fused):
+    """The segment-attention kernel the library launches for these heads and plan
+    query tile (its launcher's choice)."""
+    g = hq // hkv
+    if g == 8:
+        return ("segment attention (seg_attn_bf16_pp, 8 query heads per kv head"
+                + (", version rows rotated at staging)" if fused else ")"))
+    if bq != 64:
+        return (f"segment attention (seg_attn_bf16_pp, {g} query heads per kv head, query tiles of {bq} "
+                f"tokens in {bq // 64} parts)")
+    if g == 4 and hkv % 2 == 0:
+        return "segment attention (seg_attn_bf16_pp, 4 query heads per kv head, two kv heads per workgroup)"
+    return f"segment attention (seg_attn_bf16<{g}>)"
 
 
 def attn_src_hash():
@@ -170,7 +187,8 @@ def main():
     hkv = k.shape[1]
     qd, kd, vd = t_bf16(q), t_bf16(k), t_bf16(v)
     req_ops = (tr.msg_len, tr.drop, tr.reposition)
-    plan0 = akv.build_visibility(akv.ops_from_messages(*req_ops))
+    bq = args.bq or akv.attention_bq(args.hq, k.shape[1])
+    plan0 = akv.build_visibility(akv.ops_from_messages(*req_ops), bq=bq)
     nv = int(plan0.info["n_versions"])
     pairs = int(plan0.info["visible_pairs"])
     attn_flop = 4.0 * d * hq * pairs
@@ -239,7 +257,7 @@ def main():
             # A1 on the host while the GPU still runs the previous step; the image goes up
             # on the copy stream into the buffer the step before the previous one used
             t0 = time.perf_counter()
-            plan = akv.build_visibility(akv.ops_from_messages(*req_ops))
+            plan = akv.build_visibility(akv.ops_from_messages(*req_ops), bq=bq)
             t1 = time.perf_counter()
             buf = dev_plans[i % 2]
             if plan_free[i % 2] is not None:
@@ -373,12 +391,7 @@ def main():
                    "attn_flop_per_step": attn_flop, "version_rows": nv,
                    "versions": "rotated while key tiles are staged" if fused else "built into buffers",
                    "stages": sorted(only)},
-        "roofline": {"bound": "mfma", "kernel": ("segment attention (seg_attn_bf16_pp, 8 query heads per kv head"
-                                                   + (", version rows rotated at staging)" if fused else ")")
-                                                   if hq // hkv == 8 else
-                                                   "segment attention (seg_attn_bf16_pp, 4 query heads per kv head, "
-                                                   "two kv heads per workgroup)" if hq // hkv == 4 and hkv % 2 == 0 else
-                                                   f"segment attention (seg_attn_bf16<{hq // hkv}>)"),
+        "roofline": {"bound": "mfma", "kernel": attn_kernel_name(hq, hkv, bq, fused),
                      "achieved": attn_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": (attn_tflops / PEAK_BF16_TFLOPS) if attn_tflops else None,
                      "traffic": traffic},

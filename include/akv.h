@@ -100,8 +100,9 @@ int akv_ops_from_messages(int32_t n_msgs, const int32_t* msg_len,
                           akv_op* ops_out, int64_t ops_cap, int64_t* n_ops_out);
 
 /* akv_build_visibility: replay the ops and compile the restore plan (all host).
- * bq / bk: query / key tile sizes of the tile-class lists (the GPU attention
- * kernel needs bq == 64 and bk == 64).
+ * bq / bk: query / key tile sizes of the tile-class lists (the bf16 attention
+ * kernels need bk == 64 and bq == 64 or, with hq / hkv in {1, 2, 4}, bq == 64 * 8 /
+ * (hq / hkv); akv_attention_bq gives the one they run fastest with).
  * Tables (all int32, see akv_plan_tables):
  *   T1 tok_pos[T]    position of each token when appended;
  *   T2 tok_drop[T]   token index of the boundary at which it is dropped, or INT32_MAX;
@@ -213,9 +214,19 @@ int akv_build_kv_versions(const akv_plan* plan, const void* dev_plan, const void
  * tok_drop[src] > i, then its own tokens j <= i with tok_drop[j] > i.
  * q, k: rotated to append positions; out [n_tokens][hq][d]; lse (nullable, float32
  * [n_tokens][hq]) receives the natural-log sum of exp(scale * score).
- * scale <= 0 means 1/sqrt(d).  bf16 needs d == 64 and plan bq == bk == 64; f32
- * (a vector-ALU path for small problems) needs d <= 128.
+ * scale <= 0 means 1/sqrt(d).  bf16 needs d == 64, hq / hkv in {1, 2, 4, 8}, a plan
+ * with bk == 64 and bq == 64 or (hq / hkv < 8) bq == 64 * 8 / (hq / hkv); f32 (a
+ * vector-ALU path for small problems) needs d <= 128 and bq <= 256.  Errors:
+ * AKV_EINVAL (NULL pointers, hq not a multiple of hkv, missing version buffers),
+ * AKV_EUNSUPPORTED (other shapes or tile sizes), AKV_EHIP (launch failure).
  */
+/* The plan query tile (bq for akv_build_visibility) with which the bf16 attention
+ * runs fastest for hq query heads over hkv kv heads: 64 for 8 query heads per kv
+ * head (one kv head per workgroup, eight waves of 64 query rows); 64 * 8 / (hq / hkv)
+ * for 1, 2 or 4, whose eight waves then take the 8 / (hq / hkv) 64-token parts of a
+ * query tile for each query head.  64 for any other shape.  Pure host function. */
+int32_t akv_attention_bq(int32_t hq, int32_t hkv);
+
 int akv_segment_attention(const akv_plan* plan, const void* dev_plan,
                           const void* q, const void* k, const void* v,
                           const void* k_ver, const void* v_ver, void* out, float* lse,

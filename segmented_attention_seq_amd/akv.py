@@ -111,6 +111,7 @@ _sig("akv_cache_alloc", C.c_int, _vp, _i32, _vp)
 _sig("akv_cache_insert", C.c_int, _vp, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _i64)
 _sig("akv_cache_unlock", C.c_int, _vp, _vp, _i64)
 _sig("akv_cache_stats_get", C.c_int, _vp, C.POINTER(akv_cache_stats))
+_sig("akv_attention_bq", _i32, _i32, _i32)
 
 EXPORTED = ["akv_status_string", "akv_last_error", "akv_version", "akv_ops_from_messages",
             "akv_build_visibility", "akv_plan_info_get", "akv_plan_tables_get", "akv_plan_upload",
@@ -118,7 +119,7 @@ EXPORTED = ["akv_status_string", "akv_last_error", "akv_version", "akv_ops_from_
             "akv_segment_attention", "akv_segment_attention_rope", "akv_decode_workspace_bytes", "akv_decode_attention",
             "akv_decode_attention_noalloc", "akv_rot_table_bytes", "akv_segment_attention_fused",
             "akv_cache_create", "akv_cache_destroy", "akv_cache_match", "akv_cache_alloc",
-            "akv_cache_insert", "akv_cache_unlock", "akv_cache_stats_get"]
+            "akv_cache_insert", "akv_cache_unlock", "akv_cache_stats_get", "akv_attention_bq"]
 
 
 def _check(status: int, where: str):
@@ -291,6 +292,11 @@ class Plan:
             torch.cuda.current_stream(dev).synchronize()
             self._dev[key] = buf
         return self._dev[key]
+
+
+def attention_bq(hq: int, hkv: int) -> int:
+    """Plan query tile the bf16 attention runs fastest with (akv_attention_bq)."""
+    return int(_lib.akv_attention_bq(hq, hkv))
 
 
 def build_visibility(ops, bq: int = 64, bk: int = 64) -> Plan:

@@ -215,6 +215,12 @@ int akv_build_kv_versions(const akv_plan* p, const void* dev_plan, const void* k
   return akv::launch_rope(a, stream);
 }
 
+int32_t akv_attention_bq(int32_t hq, int32_t hkv) {
+  if (hq < 1 || hkv < 1 || hq % hkv) return 64;
+  const int32_t grp = hq / hkv;
+  return (grp == 1 || grp == 2 || grp == 4) ? 512 / grp : 64;
+}
+
 namespace {
 
 int segment_attention(const akv_plan* p, const void* dev_plan, const void* q, const void* k, const void* v,
@@ -227,7 +233,8 @@ int segment_attention(const akv_plan* p, const void* dev_plan, const void* q, co
   const int32_t grp = hq / hkv;
   if (dtype == AKV_BF16) {
     if (d != 64) return fail(AKV_EUNSUPPORTED, "bf16 segment attention needs d == 64");
-    if (p->bq != 64 || p->bk != 64) return fail(AKV_EUNSUPPORTED, "bf16 segment attention needs a plan with bq == bk == 64");
+    if (p->bk != 64 || (p->bq != 64 && (grp >= 8 || p->bq * grp != 512)))
+      return fail(AKV_EUNSUPPORTED, "bf16 segment attention needs a plan with bk == 64 and bq == 64 or 64 * 8 / (hq / hkv)");
     if (grp != 1 && grp != 2 && grp != 4 && grp != 8)
       return fail(AKV_EUNSUPPORTED, "bf16 segment attention needs hq/hkv in {1, 2, 4, 8}");
   } else {

@@ -1204,16 +1204,25 @@ constexpr float kFastHi = 1.2676506002282294e30f;  // 2^100
 // group A (waves 0-3) the first one's four query heads and group B (waves 4-7) the
 // second one's; each slot of the ring holds both heads' tiles, so the K/V ring
 // takes 128 KB and the output is stored straight from the accumulators.
-template <bool ROT, int RL = AKV_ROPE_HALF, int HPW = 1>
+//
+// M > 1 (8 / M query heads per kv head, no ROT): a work item is a query tile of
+// 64 M tokens (a plan built with bq = 64 M), cut into M 64-token parts; wave w runs
+// part w / (8 / M) of query head w % (8 / M), so the eight waves still share every
+// K/V tile.  The plan's tile classes cover the whole 64 M-row tile: a FULL tile is
+// visible to every row, and each wave masks a PARTIAL tile by its own rows (a part
+// past the end of the item has no rows: it computes on zero queries and stores
+// nothing).
+template <bool ROT, int RL = AKV_ROPE_HALF, int HPW = 1, int M = 1>
 __global__ __launch_bounds__(kPPThreads) void seg_attn_bf16_pp(AKV_ATTN_PARAMS, const int* __restrict__ ver_run,
                                                                const float* __restrict__ rot_tab) {
-  static_assert(HPW == 1 || (HPW == 2 && !ROT), "two kv heads per workgroup only with version buffers");
-  constexpr int GROUP = 8 / HPW;  // query heads per kv head
+  static_assert(HPW == 1 || (HPW == 2 && !ROT && M == 1), "two kv heads per workgroup only with version buffers");
+  static_assert(M == 1 || (!ROT && (M == 2 || M == 4 || M == 8)), "query tile parts only with version buffers");
+  constexpr int GROUP = 8 / (HPW * M);  // query heads per kv head
   using Ctx = PPCtx<ROT, HPW>;
   __shared__ __attribute__((aligned(16))) uint16_t lk[Ctx::NS][HPW * Ctx::KSZ];
   __shared__ __attribute__((aligned(16))) uint16_t lv[Ctx::NS][HPW * Ctx::VSZ];
   __shared__ int mtok[Ctx::NS][BK], mdrop[Ctx::NS][BK];
-  __shared__ __attribute__((aligned(16))) uint16_t lqs[HPW == 1 ? GROUP : 1][64 * KP];
+  __shared__ __attribute__((aligned(16))) uint16_t lqs[HPW == 1 ? kPPThreads / 64 : 1][64 * KP];  // per wave
   __shared__ __attribute__((aligned(16))) float rtab[ROT ? GROUP * 512 : 4];  // ROT: 2 KB per wave
   __shared__ int redo;
 
@@ -1221,12 +1230,15 @@ __global__ __launch_bounds__(kPPThreads) void seg_attn_bf16_pp(AKV_ATTN_PARAMS, 
   const int hk0 = (blockIdx.x % npair) * HPW;  // the workgroup's first kv head
   const int item = order[blockIdx.x / npair];
   const int* dsc = item_desc + item * ID_WORDS;
-  const int q0 = dsc[ID_QBEGIN], q1 = dsc[ID_QEND], tb = dsc[ID_TB], te = dsc[ID_TE];
+  const int qi0 = dsc[ID_QBEGIN], qi1 = dsc[ID_QEND], tb = dsc[ID_TB], te = dsc[ID_TE];
   const int r = dsc[ID_R], voff = dsc[ID_VEROFF], t0 = dsc[ID_TILE0], t1 = dsc[ID_TILE1];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int hsel = HPW == 1 ? 0 : wave >> 2;  // this wave's kv head within the workgroup
   const int hk = hk0 + hsel;
   const int h = hk * GROUP + (wave & (GROUP - 1));
+  // this wave's query rows [q0, q1): the item's, or with M parts its part's
+  const int q0 = M == 1 ? qi0 : qi0 + 64 * (wave / GROUP);
+  const int q1 = M == 1 ? qi1 : min(qi1, q0 + 64);
   const int lq = lane & 31, lg = lane >> 5;
   uint16_t* lqw = lqs[HPW == 1 ? wave : 0];  // this wave's Q' rows (written and read by this wave only)
   const bool lag = wave >= 4;  // group B
@@ -1399,7 +1411,21 @@ int launch_segment_attention(const AttnArgs& a, void* stream) {
                      (const uint16_t*)a.k_ver, (const uint16_t*)a.v_ver, a.item_desc, a.tiles,      \
                      a.order, a.tok_drop, a.ver_src, (uint16_t*)a.out, a.lse, a.hq, a.hkv, a.scale,    \
                      a.tok_pos, a.rq)
-    switch (grp) {
+#define AKV_LAUNCH_PARTS(M)                                                                          \
+  hipLaunchKernelGGL((seg_attn_bf16_pp<false, AKV_ROPE_HALF, 1, M>), dim3((unsigned)blocks), dim3(512), 0, s, \
+                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,              \
+                     (const uint16_t*)a.k_ver, (const uint16_t*)a.v_ver, a.item_desc, a.tiles,      \
+                     a.order, a.tok_drop, a.ver_src, (uint16_t*)a.out, a.lse, a.hq, a.hkv, a.scale,    \
+                     a.tok_pos, a.rq, nullptr, nullptr)
+    if (a.bq != 64) {  // query tiles of 64 * 8 / grp tokens: the ping-pong pipeline with 8 / grp parts
+      if (a.fused || grp * a.bq != 512) return fail(AKV_EUNSUPPORTED, "bf16 segment attention needs bq == 64 * 8 / (hq / hkv)");
+      switch (grp) {
+        case 4: AKV_LAUNCH_PARTS(2); break;
+        case 2: AKV_LAUNCH_PARTS(4); break;
+        case 1: AKV_LAUNCH_PARTS(8); break;
+        default: return fail(AKV_EUNSUPPORTED, "bf16 segment attention needs bq == 64 * 8 / (hq / hkv)");
+      }
+    } else switch (grp) {
       case 1: AKV_LAUNCH_BF16(1); break;
       case 2: AKV_LAUNCH_BF16(2); break;
       case 4:
@@ -1438,6 +1464,7 @@ int launch_segment_attention(const AttnArgs& a, void* stream) {
         return fail(AKV_EUNSUPPORTED, "bf16 segment attention needs hq/hkv in {1, 2, 4, 8}");
     }
 #undef AKV_LAUNCH_BF16
+#undef AKV_LAUNCH_PARTS
   } else {
     const long long blocks = a.n_items * a.hq;
     if (blocks > 0x7fffffffLL) return fail(AKV_EINVAL, "too many work items");

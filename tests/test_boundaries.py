@@ -107,3 +107,4 @@ def test_bench_refuses_more_than_one_gpu():
                        text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+

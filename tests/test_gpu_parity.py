@@ -224,8 +224,8 @@ def test_repos_workload_96k_keys():
 
 # ---------------------------------------------------------------- segment attention
 
-def _run_restore(tr, hq, hkv, d, bf16, seed, layout=akv.ROPE_HALF, lse=True):
-    plan = akv.build_visibility(akv.ops_from_messages(tr.msg_len, tr.drop, tr.reposition))
+def _run_restore(tr, hq, hkv, d, bf16, seed, layout=akv.ROPE_HALF, lse=True, bq=64):
+    plan = akv.build_visibility(akv.ops_from_messages(tr.msg_len, tr.drop, tr.reposition), bq=bq)
     q, k, v = workload.prefill_tensors(tr.n_tokens, hq, hkv, d, seed=seed, bf16=bf16)
     dt = torch.bfloat16 if bf16 else torch.float32
     T = tr.n_tokens
@@ -335,12 +335,12 @@ EDGE = {
 }
 
 
-@pytest.mark.parametrize("hq", [16, 8])
+@pytest.mark.parametrize("hq,bq", [(16, 64), (8, 64), (4, 256), (2, 512)])
 @pytest.mark.parametrize("name", sorted(EDGE))
-def test_edge_cases_bf16(name, hq):
+def test_edge_cases_bf16(name, hq, bq):
     tr = EDGE[name]
     tr.name = name
-    plan, qkv, out, lse = _run_restore(tr, hq, 2, 64, bf16=True, seed=71)
+    plan, qkv, out, lse = _run_restore(tr, hq, 2, 64, bf16=True, seed=71, bq=bq)
     _check_rows(tr, qkv, out, lse, bf16=True)
 
 
@@ -375,6 +375,33 @@ def test_two_kv_heads_per_workgroup_every_tile_count(repos):
     _check_rows(tr, qkv, out, lse, bf16=True)
 
 
+# (query heads, kv heads, plan bq): 4, 2 and 1 query heads per kv head with query
+# tiles of 64 * 8 / group tokens, cut into 8 / group parts of the ping-pong kernel
+PARTS = [(8, 2, 128), (4, 2, 256), (2, 2, 512), (32, 8, 128), (16, 8, 256), (8, 8, 512)]
+
+
+@pytest.mark.parametrize("hq,hkv,bq", PARTS[:3])
+@pytest.mark.parametrize("repos", [False, True])
+def test_query_tile_parts_every_tile_count(repos, hq, hkv, bq):
+    """Query tiles of 128, 256 or 512 tokens cut into 64-token parts, one part per
+    wave group: work items of many tile counts, parts past a ragged item end, PARTIAL
+    tiles that are EMPTY for some parts, every row checked."""
+    lens, rp = ([1100], []) if not repos else ([530, 610], [0])
+    tr = workload.Trajectory(lens, ["x"] * len(lens), {}, rp, name=f"parts-{bq}-{repos}")
+    plan, qkv, out, lse = _run_restore(tr, hq, hkv, 64, bf16=True, seed=84, bq=bq)
+    assert plan.info["bq"] == bq
+    _check_rows(tr, qkv, out, lse, bf16=True)
+
+
+@pytest.mark.parametrize("hq,hkv,bq", PARTS)
+def test_query_tile_parts_random_plans(hq, hkv, bq):
+    tr = workload.agent_trajectory(5, seed=90 + bq + hq, total=2100, keep=1, repos="every" if hq % 3 else "none",
+                                   user_len=64, assist_range=(30, 200), tool_range=(100, 500),
+                                   name=f"parts-rand-{hq}-{hkv}-{bq}")
+    plan, qkv, out, lse = _run_restore(tr, hq, hkv, 64, bf16=True, seed=91, bq=bq)
+    _check_rows(tr, qkv, out, lse, bf16=True)
+
+
 def test_empty_plan_and_unsupported():
     plan = akv.build_visibility([])
     x = torch.empty((0, 8, 64), dtype=torch.bfloat16, device="cuda")
@@ -391,6 +418,13 @@ def test_empty_plan_and_unsupported():
     with pytest.raises(akv.AkvError) as e:
         akv.segment_attention(p, q3, kv, kv, None, None, torch.empty_like(q3))
     assert e.value.status == akv.EUNSUPPORTED
+    # query tiles of 64 * 8 / group tokens only: not 128 for 8 or 2 query heads per kv head
+    p128 = akv.build_visibility([(akv.OP_APPEND, 10)], bq=128)
+    for heads in (8, 2):
+        qh = torch.zeros((10, heads, 64), dtype=torch.bfloat16, device="cuda")
+        with pytest.raises(akv.AkvError) as e:
+            akv.segment_attention(p128, qh, kv, kv, None, None, torch.empty_like(qh))
+        assert e.value.status == akv.EUNSUPPORTED
 
 
 def test_deterministic():
@@ -520,14 +554,15 @@ def test_fused_versions_rejects_unsupported():
     assert e.value.status == akv.EINVAL
 
 
-@pytest.mark.parametrize("hq", [32, 16, 8])
-def test_48k_workload_smaller_head_groups_sampled(hq):
-    """The 48k restore with 4, 2 and 1 query heads per kv head (the one-wave-per-head
-    kernel, several workgroups per CU) at full size, checked on boundary and seeded
-    rows."""
+@pytest.mark.parametrize("hq,bq", [(32, 64), (16, 64), (8, 64), (32, 128), (16, 256), (8, 512)])
+def test_48k_workload_smaller_head_groups_sampled(hq, bq):
+    """The 48k restore with 4, 2 and 1 query heads per kv head at full size, checked
+    on boundary and seeded rows: with 64-token query tiles (two kv heads per
+    ping-pong workgroup for 4, else the one-wave-per-head kernel) and with query
+    tiles of 64 * 8 / group tokens in parts."""
     tr = workload.config_trajectory(2)
     q, k, v = workload.prefill_tensors(tr.n_tokens, hq, 8, 64, seed=300 + hq)
-    plan = akv.build_visibility(akv.ops_from_messages(tr.msg_len, tr.drop, tr.reposition))
+    plan = akv.build_visibility(akv.ops_from_messages(tr.msg_len, tr.drop, tr.reposition), bq=bq)
     T = tr.n_tokens
     bufs = {"out": nan_like((T, hq, 64), torch.bfloat16), "lse": nan_like((T, hq), torch.float32)}
     out, lse = akv.restore(plan, dev_tensor(q, True), dev_tensor(k, True), dev_tensor(v, True), BASE,

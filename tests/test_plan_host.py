@@ -191,3 +191,13 @@ def test_full_size_parity_parts_cover_every_boundary_row(cfg, parts, n_edge):
     assert np.array_equal(np.concatenate([g[1] for g in got]), edges)
     assert np.array_equal(np.concatenate([g[2] for g in got]), seeded)
     assert np.array_equal(np.concatenate([g[0] for g in got]), np.union1d(edges, seeded))
+
+
+def test_attention_bq_choice():
+    """The plan query tile the bf16 attention runs fastest with: 64 for 8 query heads
+    per kv head, 64 * 8 / group for groups of 1, 2 and 4 (eight waves take the
+    group's query heads over 8 / group 64-token parts), 64 otherwise."""
+    assert akv.attention_bq(64, 8) == 64
+    assert akv.attention_bq(32, 8) == 128 and akv.attention_bq(12, 3) == 128
+    assert akv.attention_bq(16, 8) == 256 and akv.attention_bq(8, 8) == 512
+    assert akv.attention_bq(24, 8) == 64 and akv.attention_bq(3, 2) == 64 and akv.attention_bq(0, 8) == 64
