@@ -377,7 +377,7 @@ def test_two_kv_heads_per_workgroup_every_tile_count(repos):
 
 # (query heads, kv heads, plan bq): 4, 2 and 1 query heads per kv head with query
 # tiles of 64 * 8 / group tokens, cut into 8 / group parts of the ping-pong kernel
-PARTS = [(8, 2, 128), (4, 2, 256), (2, 2, 512), (32, 8, 128), (16, 8, 256), (8, 8, 512)]
+PARTS = [(8, 2, 128), (4, 2, 256), (2, 2, 512), (32, 8, 128), (16, 8, 256), (8, 8, 512), (12, 3, 128)]
 
 
 @pytest.mark.parametrize("hq,hkv,bq", PARTS[:3])
