@@ -34,12 +34,14 @@
 //     place in LDS, between the QK MFMAs;
 //   * blockIdx -> (item, kv head) puts consecutive workgroups on different kv heads,
 //     so with 8 kv heads each XCD's L2 streams a single head's K/V;
-//   * 8 query heads per kv head (seg_attn_bf16_pp), or 4 with an even number of kv
-//     heads (two kv heads per workgroup): two wave groups ping-pong between
-//     softmax and MFMA phases; the fast pass keeps the exponent offset at 0 and
-//     takes the column sums from the matrix cores, with one range check per work
-//     item and a redo through the rescaling softmax when it fails;
-//   * 1 or 2 query heads per kv head, or 4 with an odd number of kv heads
+//   * 8 query heads per kv head (seg_attn_bf16_pp); 4, 2 or 1 with a plan whose
+//     query tiles hold 64 * 8 / group tokens, each wave taking one 64-token part
+//     of the tile for one query head; or 4 with an even number of kv heads and
+//     64-token query tiles (two kv heads per workgroup): two wave groups
+//     ping-pong between softmax and MFMA phases; the fast pass keeps the exponent
+//     offset at 0 and takes the column sums from the matrix cores, with one range
+//     check per work item and a redo through the rescaling softmax when it fails;
+//   * otherwise, 1, 2 or 4 query heads per kv head with 64-token query tiles
 //     (seg_attn_bf16<GROUP>): one wave per query
 //     head, one synchronously staged tile buffer, the rescaling softmax (lazily
 //     moved exponent offset, bf16 dot2 row sums, per-tile range check); several
@@ -909,8 +911,9 @@ __global__ __launch_bounds__(64 * GROUP, 2) void seg_attn_bf16(AKV_ATTN_PARAMS) 
   store_out<false>(w, out, lse, q0, q1, hq, h, lq, lg, nullptr, lane);
 }
 
-// Ping-pong pipeline for 8 query heads per kv head (8 waves, two per SIMD), or for
-// two kv heads of 4 query heads each.
+// Ping-pong pipeline for 8 query heads per kv head (8 waves, two per SIMD), for
+// two kv heads of 4 query heads each, or for 8 / M query heads over M parts of a
+// query tile.
 // Waves 0-3 (group A) and 4-7 (group B) run the same tile loop one phase apart,
 // separated by workgroup barriers, so while one wave of a SIMD issues MFMAs
 // (PV of tile t and QK of tile t+1) its partner runs the softmax of its tile on
@@ -1115,7 +1118,7 @@ __device__ __forceinline__ void pp_step(WaveState& w, f32x4 (&ls)[2], bf16x8 sel
   if (ver3)
     __builtin_amdgcn_s_waitcnt(kWaitVm4);
   else
-    __builtin_amdgcn_s_waitcnt(kWaitIter == kWaitVm4 && !ROT ? kWaitVm4 : kWaitVm2);
+    __builtin_amdgcn_s_waitcnt(HPW == 2 ? kWaitVm4 : kWaitVm2);
   lds_barrier();
   ent[0] = ent[1];
   ent[1] = ent[2];
