@@ -192,9 +192,12 @@ __global__ __launch_bounds__(256) void rope_row_kernel(T* __restrict__ out, cons
   constexpr int HG = 32 / CPR < 8 ? 32 / CPR : 8;   // heads per group
   constexpr int G = HG * LPH;
   constexpr int D = 16 * CPR;
+  // With one group per wave (G == 64) the group index is the wave's, made uniform
+  // by readfirstlane, so the row indices come by scalar loads.
   const long long tid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  const long long grp = tid / G;
-  const int l = (int)(tid - grp * G);
+  const long long grp = G == 64 ? (long long)blockIdx.x * (blockDim.x / 64) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6)
+                                : tid / G;
+  const int l = G == 64 ? (int)(threadIdx.x & 63) : (int)(tid - grp * G);
   const long long rb = grp / n_hg;
   if (rb * RPW >= n_rows) return;  // whole groups leave together
   const int hg = (int)(grp - rb * n_hg);
