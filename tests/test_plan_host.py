@@ -135,7 +135,7 @@ def test_tables_match_oracle_random(req, tiles):
 
 
 @settings(max_examples=60, deadline=None)
-@given(requests(max_msgs=12, max_len=150), st.sampled_from([(16, 16), (64, 64), (32, 16)]))
+@given(requests(max_msgs=12, max_len=150), st.sampled_from([(16, 16), (64, 64), (32, 16), (128, 64), (256, 64)]))
 def test_tables_match_oracle_longer(req, tiles):
     lens, drop, repos = req
     _compare(lens, drop, repos, *tiles)
@@ -153,6 +153,16 @@ def test_tables_48k_workload():
     tr = workload.config_trajectory(2)
     plan = _compare(tr.msg_len, tr.drop, tr.reposition, 64, 64)
     assert plan.info["n_segments"] == 8 and plan.info["n_versions"] == 0
+
+
+@pytest.mark.parametrize("bq", [128, 256, 512])
+def test_tables_48k_workload_large_query_tiles(bq):
+    """Query tiles of 128, 256 and 512 tokens (the plans the attention takes for 4,
+    2 and 1 query heads per kv head): items, tile lists and classes against the
+    oracle on sampled items."""
+    tr = workload.config_trajectory(2)
+    plan = _compare(tr.msg_len, tr.drop, tr.reposition, bq, 64, tiles="sampled", rng=np.random.default_rng(bq))
+    assert plan.info["n_items"] == sum(-(-(e[1] - e[0]) // bq) for e in plan.tables()["epochs"])
 
 
 @pytest.mark.parametrize("cfg", [3, 4])
