@@ -21,8 +21,12 @@ namespace akv {
 namespace {
 
 // Frequencies are stored in revolutions per position, theta_i / (2 pi), in fp64; the
-// angle evaluation is shared with the attention's query load (rope_angle.h).
-struct Freqs { double rev[128]; };
+// angle evaluation is shared with the attention's query load (rope_angle.h).  The
+// table travels as a kernel argument sized to the kernel's head dim (N = d / 2
+// entries for the row kernels): a smaller argument block is a shorter dispatch,
+// which shows on the 35 us repos launches.
+template <int N> struct FreqsN { double rev[N]; };
+using Freqs = FreqsN<128>;
 
 __device__ __forceinline__ void angle_cs(long long delta, double rev, float& c, float& s) {
   rope_angle_cs((double)delta, rev, c, s);
@@ -187,7 +191,7 @@ __global__ __launch_bounds__(256) void rope_row_kernel(T* __restrict__ out, cons
                                                        long long n_rows, int heads, int n_hg,
                                                        const int* __restrict__ gather,
                                                        const int* __restrict__ pos_from, int from_by_src,
-                                                       const int* __restrict__ pos_to, Freqs fr) {
+                                                       const int* __restrict__ pos_to, FreqsN<8 * CPR> fr) {
   constexpr int LPH = 2 * CPR;                      // lanes (16-byte chunks) per head
   constexpr int HG = 32 / CPR < 8 ? 32 / CPR : 8;   // heads per group
   constexpr int G = HG * LPH;
@@ -289,9 +293,11 @@ __global__ __launch_bounds__(256) void rope_row_kernel(T* __restrict__ out, cons
 constexpr int kRowsPerGroup = 2;
 
 template <typename T, int LAYOUT, int CPR, int IX>
-void launch_row_ix(const RopeArgs& a, const Freqs& fr, hipStream_t s) {
+void launch_row_ix(const RopeArgs& a, const Freqs& all, hipStream_t s) {
   constexpr int HG = 32 / CPR < 8 ? 32 / CPR : 8;
   constexpr int RPW = kRowsPerGroup;
+  FreqsN<8 * CPR> fr;  // the head dim's d / 2 = 8 CPR frequencies
+  for (int i = 0; i < 8 * CPR; ++i) fr.rev[i] = all.rev[i];
   const int n_hg = (a.heads + HG - 1) / HG;
   const long long threads = (a.n_rows + RPW - 1) / RPW * n_hg * (long long)(HG * 2 * CPR);
   const unsigned blocks = (unsigned)((threads + 255) / 256);
