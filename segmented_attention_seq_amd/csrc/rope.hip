@@ -290,7 +290,7 @@ __global__ __launch_bounds__(256) void rope_row_kernel(T* __restrict__ out, cons
 }
 
 // Rows per group of the row kernel.
-constexpr int kRowsPerGroup = 2;
+constexpr int kRowsPerGroup = 3;
 
 template <typename T, int LAYOUT, int CPR, int IX>
 void launch_row_ix(const RopeArgs& a, const Freqs& all, hipStream_t s) {
