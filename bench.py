@@ -77,7 +77,7 @@ def attn_kernel_name(hq, hkv, bq, fused):
                 + (", version rows rotated at staging)" if fused else ")"))
     if bq != 64:
         return (f"segment attention (seg_attn_bf16_pp, {g} query heads per kv head, query tiles of {bq} "
-                f"tokens in {bq // 64} parts)")
+                f"tokens in {bq // 64} parts" + (", version rows rotated at staging)" if fused else ")"))
     if g == 4 and hkv % 2 == 0:
         return "segment attention (seg_attn_bf16_pp, 4 query heads per kv head, two kv heads per workgroup)"
     return f"segment attention (seg_attn_bf16<{g}>)"

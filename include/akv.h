@@ -263,8 +263,10 @@ int akv_segment_attention_rope(const akv_plan* plan, const void* dev_plan,
  * q_raw: raw queries [T][hq][d] (rotated on load as in akv_segment_attention_rope);
  * k: keys rotated to their append positions (akv_rope_apply); v: values.
  * ws: caller device memory of at least akv_rot_table_bytes(plan, d) bytes (may be
- * NULL when that is 0), overwritten.  bf16 only, d == 64, hq == 8 * hkv, and k and
- * v under 4 GiB each (T * hkv * d * 2 bytes < 2^32, T = the plan's token count);
+ * NULL when that is 0), overwritten.  bf16 only, d == 64, hq == 8 * hkv with a plan
+ * of bq == 64, or hq / hkv in {1, 2, 4} with bq == 64 * 8 / (hq / hkv) (as
+ * akv_attention_bq gives), and k and v under 4 GiB each (T * hkv * d * 2 bytes <
+ * 2^32, T = the plan's token count);
  * other shapes: AKV_EUNSUPPORTED, use the version-buffer path.  Other errors as
  * akv_segment_attention_rope, plus AKV_EINVAL for a short workspace.
  */

@@ -302,8 +302,14 @@ int akv_segment_attention_fused(const akv_plan* p, const void* dev_plan, const v
   if (!(rope_base > 1.0) || !std::isfinite(rope_base)) return fail(AKV_EINVAL, "RoPE base must be finite and > 1");
   if (rope_layout != AKV_ROPE_HALF && rope_layout != AKV_ROPE_INTERLEAVED)
     return fail(AKV_EINVAL, "rope_layout must be AKV_ROPE_HALF or AKV_ROPE_INTERLEAVED");
-  if (dtype != AKV_BF16 || d != 64 || hkv < 1 || hq != 8 * hkv)
-    return fail(AKV_EUNSUPPORTED, "fused version rotation needs bf16, d == 64 and hq == 8 * hkv");
+  // 8 query heads per kv head with 64-token query tiles, or 4, 2, 1 with query tiles
+  // of 64 * 8 / (hq / hkv) tokens: the ping-pong kernel
+  const bool heads_ok = hkv >= 1 && hq % hkv == 0 &&
+                        ((hq == 8 * hkv && p->bq == 64) || ((hq / hkv == 4 || hq / hkv == 2 || hq == hkv) &&
+                                                            p->bq * (hq / hkv) == 512));
+  if (dtype != AKV_BF16 || d != 64 || !heads_ok)
+    return fail(AKV_EUNSUPPORTED, "fused version rotation needs bf16, d == 64, and hq == 8 * hkv with bq == 64 "
+                                  "or hq / hkv in {1, 2, 4} with bq == 64 * 8 / (hq / hkv)");
   // the kernel's gathered copies address k and v by 32-bit byte offsets
   if ((uint64_t)p->T * (uint64_t)hkv * (uint64_t)d * 2 > 0xffffffffull)
     return fail(AKV_EUNSUPPORTED, "fused version rotation needs k and v under 4 GiB each");

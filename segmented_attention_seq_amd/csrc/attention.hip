@@ -1208,7 +1208,7 @@ constexpr float kFastHi = 1.2676506002282294e30f;  // 2^100
 // second one's; each slot of the ring holds both heads' tiles, so the K/V ring
 // takes 128 KB and the output is stored straight from the accumulators.
 //
-// M > 1 (8 / M query heads per kv head, no ROT): a work item is a query tile of
+// M > 1 (8 / M query heads per kv head): a work item is a query tile of
 // 64 M tokens (a plan built with bq = 64 M), cut into M 64-token parts; wave w runs
 // part w / (8 / M) of query head w % (8 / M), so the eight waves still share every
 // K/V tile.  The plan's tile classes cover the whole 64 M-row tile: a FULL tile is
@@ -1219,14 +1219,14 @@ template <bool ROT, int RL = AKV_ROPE_HALF, int HPW = 1, int M = 1>
 __global__ __launch_bounds__(kPPThreads) void seg_attn_bf16_pp(AKV_ATTN_PARAMS, const int* __restrict__ ver_run,
                                                                const float* __restrict__ rot_tab) {
   static_assert(HPW == 1 || (HPW == 2 && !ROT && M == 1), "two kv heads per workgroup only with version buffers");
-  static_assert(M == 1 || (!ROT && (M == 2 || M == 4 || M == 8)), "query tile parts only with version buffers");
+  static_assert(M == 1 || M == 2 || M == 4 || M == 8, "1, 2, 4 or 8 query tile parts");
   constexpr int GROUP = 8 / (HPW * M);  // query heads per kv head
   using Ctx = PPCtx<ROT, HPW>;
   __shared__ __attribute__((aligned(16))) uint16_t lk[Ctx::NS][HPW * Ctx::KSZ];
   __shared__ __attribute__((aligned(16))) uint16_t lv[Ctx::NS][HPW * Ctx::VSZ];
   __shared__ int mtok[Ctx::NS][BK], mdrop[Ctx::NS][BK];
   __shared__ __attribute__((aligned(16))) uint16_t lqs[HPW == 1 ? kPPThreads / 64 : 1][64 * KP];  // per wave
-  __shared__ __attribute__((aligned(16))) float rtab[ROT ? GROUP * 512 : 4];  // ROT: 2 KB per wave
+  __shared__ __attribute__((aligned(16))) float rtab[ROT ? (kPPThreads / 64) * 512 : 4];  // ROT: 2 KB per wave
   __shared__ int redo;
 
   const int npair = hkv / HPW;
@@ -1414,19 +1414,49 @@ int launch_segment_attention(const AttnArgs& a, void* stream) {
                      (const uint16_t*)a.k_ver, (const uint16_t*)a.v_ver, a.item_desc, a.tiles,      \
                      a.order, a.tok_drop, a.ver_src, (uint16_t*)a.out, a.lse, a.hq, a.hkv, a.scale,    \
                      a.tok_pos, a.rq)
+#define AKV_LAUNCH_PARTS_ROT(M, RL)                                                                  \
+  hipLaunchKernelGGL((seg_attn_bf16_pp<true, RL, 1, M>), dim3((unsigned)blocks), dim3(512), 0, s,    \
+                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,              \
+                     (const uint16_t*)a.k_ver, (const uint16_t*)a.v_ver, a.item_desc, a.tiles,      \
+                     a.order, a.tok_drop, a.ver_src, (uint16_t*)a.out, a.lse, a.hq, a.hkv, a.scale,    \
+                     a.tok_pos, a.rq, a.ver_run, (const float*)a.rot_tab)
 #define AKV_LAUNCH_PARTS(M)                                                                          \
   hipLaunchKernelGGL((seg_attn_bf16_pp<false, AKV_ROPE_HALF, 1, M>), dim3((unsigned)blocks), dim3(512), 0, s, \
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,              \
                      (const uint16_t*)a.k_ver, (const uint16_t*)a.v_ver, a.item_desc, a.tiles,      \
                      a.order, a.tok_drop, a.ver_src, (uint16_t*)a.out, a.lse, a.hq, a.hkv, a.scale,    \
                      a.tok_pos, a.rq, nullptr, nullptr)
+    if (a.fused && a.n_runs > 0) {  // the (cos, sin) of every run, for the staging-time rotation
+      const long long n = a.n_runs * (a.d / 2);
+      hipLaunchKernelGGL(rot_table_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a.run_delta, a.n_runs,
+                         a.d / 2, a.rq, a.rot_tab);
+    }
     if (a.bq != 64) {  // query tiles of 64 * 8 / grp tokens: the ping-pong pipeline with 8 / grp parts
-      if (a.fused || grp * a.bq != 512) return fail(AKV_EUNSUPPORTED, "bf16 segment attention needs bq == 64 * 8 / (hq / hkv)");
-      switch (grp) {
-        case 4: AKV_LAUNCH_PARTS(2); break;
-        case 2: AKV_LAUNCH_PARTS(4); break;
-        case 1: AKV_LAUNCH_PARTS(8); break;
-        default: return fail(AKV_EUNSUPPORTED, "bf16 segment attention needs bq == 64 * 8 / (hq / hkv)");
+      if (grp * a.bq != 512) return fail(AKV_EUNSUPPORTED, "bf16 segment attention needs bq == 64 * 8 / (hq / hkv)");
+      if (a.fused) {
+        const bool half = a.rq.layout == AKV_ROPE_HALF;
+        switch (grp) {
+          case 4:
+            if (half) AKV_LAUNCH_PARTS_ROT(2, AKV_ROPE_HALF);
+            else AKV_LAUNCH_PARTS_ROT(2, AKV_ROPE_INTERLEAVED);
+            break;
+          case 2:
+            if (half) AKV_LAUNCH_PARTS_ROT(4, AKV_ROPE_HALF);
+            else AKV_LAUNCH_PARTS_ROT(4, AKV_ROPE_INTERLEAVED);
+            break;
+          case 1:
+            if (half) AKV_LAUNCH_PARTS_ROT(8, AKV_ROPE_HALF);
+            else AKV_LAUNCH_PARTS_ROT(8, AKV_ROPE_INTERLEAVED);
+            break;
+          default: return fail(AKV_EUNSUPPORTED, "bf16 segment attention needs bq == 64 * 8 / (hq / hkv)");
+        }
+      } else {
+        switch (grp) {
+          case 4: AKV_LAUNCH_PARTS(2); break;
+          case 2: AKV_LAUNCH_PARTS(4); break;
+          case 1: AKV_LAUNCH_PARTS(8); break;
+          default: return fail(AKV_EUNSUPPORTED, "bf16 segment attention needs bq == 64 * 8 / (hq / hkv)");
+        }
       }
     } else switch (grp) {
       case 1: AKV_LAUNCH_BF16(1); break;
@@ -1444,11 +1474,6 @@ int launch_segment_attention(const AttnArgs& a, void* stream) {
         break;
       case 8:
         if (a.fused) {
-          if (a.n_runs > 0) {
-            const long long n = a.n_runs * (a.d / 2);
-            hipLaunchKernelGGL(rot_table_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a.run_delta,
-                               a.n_runs, a.d / 2, a.rq, a.rot_tab);
-          }
           auto kern = a.rq.layout == AKV_ROPE_HALF ? seg_attn_bf16_pp<true, AKV_ROPE_HALF>
                                                    : seg_attn_bf16_pp<true, AKV_ROPE_INTERLEAVED>;
           hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(512), 0, s, (const uint16_t*)a.q,
@@ -1468,6 +1493,7 @@ int launch_segment_attention(const AttnArgs& a, void* stream) {
     }
 #undef AKV_LAUNCH_BF16
 #undef AKV_LAUNCH_PARTS
+#undef AKV_LAUNCH_PARTS_ROT
   } else {
     const long long blocks = a.n_items * a.hq;
     if (blocks > 0x7fffffffLL) return fail(AKV_EINVAL, "too many work items");

@@ -480,10 +480,10 @@ def test_workloads_full_size_boundary_and_seeded_rows(cfg, part, parts):
 
 # ---------------------------------------------------------------- fused version rows
 
-def _restore_both(tr, q, k, v, hq, hkv, layout=akv.ROPE_HALF):
+def _restore_both(tr, q, k, v, hq, hkv, layout=akv.ROPE_HALF, bq=64):
     """The same restore with version buffers and with version rows rotated while
     key tiles are staged."""
-    plan = akv.build_visibility(akv.ops_from_messages(tr.msg_len, tr.drop, tr.reposition))
+    plan = akv.build_visibility(akv.ops_from_messages(tr.msg_len, tr.drop, tr.reposition), bq=bq)
     T = tr.n_tokens
     res = []
     for fused in (False, True):
@@ -506,6 +506,21 @@ def test_fused_versions_equal_version_buffers(seed, layout, keep):
                                    assist_range=(20, 200), tool_range=(60, 500), name=f"fused{seed}")
     q, k, v = workload.prefill_tensors(tr.n_tokens, 16, 2, 64, seed=seed + 1)
     plan, ((o0, l0), (o1, l1)) = _restore_both(tr, q, k, v, 16, 2, layout)
+    assert plan.info["n_versions"] > 0 and plan.info["n_runs"] > 1
+    assert torch.equal(o0.view(torch.int16), o1.view(torch.int16))
+    assert torch.equal(l0, l1)
+    _check_rows(tr, (q, k, v), o1, l1, bf16=True, layout=layout)
+
+
+@pytest.mark.parametrize("hq,hkv,bq,layout", [(8, 2, 128, akv.ROPE_HALF), (4, 2, 256, akv.ROPE_INTERLEAVED),
+                                             (2, 2, 512, akv.ROPE_HALF), (12, 3, 128, akv.ROPE_HALF)])
+def test_fused_versions_query_tile_parts(hq, hkv, bq, layout):
+    """4, 2 and 1 query heads per kv head over query-tile parts with version rows
+    rotated at staging time: bit for bit the version-buffer path, and the oracle."""
+    tr = workload.agent_trajectory(5, seed=175 + hq, total=2300, keep=2, repos="every", user_len=50,
+                                   assist_range=(20, 200), tool_range=(60, 500), name=f"fused-parts{bq}")
+    q, k, v = workload.prefill_tensors(tr.n_tokens, hq, hkv, 64, seed=176 + hq)
+    plan, ((o0, l0), (o1, l1)) = _restore_both(tr, q, k, v, hq, hkv, layout, bq=bq)
     assert plan.info["n_versions"] > 0 and plan.info["n_runs"] > 1
     assert torch.equal(o0.view(torch.int16), o1.view(torch.int16))
     assert torch.equal(l0, l1)
@@ -541,7 +556,7 @@ def test_fused_versions_rejects_unsupported():
     plan = akv.build_visibility(akv.ops_from_messages(tr.msg_len, tr.drop, tr.reposition))
     q, k, v = workload.prefill_tensors(tr.n_tokens, 8, 2, 64, seed=182)
     out = nan_like((tr.n_tokens, 8, 64), torch.bfloat16)
-    with pytest.raises(akv.AkvError) as e:   # 4 query heads per kv head
+    with pytest.raises(akv.AkvError) as e:   # 4 query heads per kv head with 64-token query tiles
         akv.segment_attention_fused(plan, dev_tensor(q, True), dev_tensor(k, True), dev_tensor(v, True), out)
     assert e.value.status == akv.EUNSUPPORTED
     q8 = workload.prefill_tensors(tr.n_tokens, 16, 2, 64, seed=183)[0]
