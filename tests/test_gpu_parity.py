@@ -305,6 +305,8 @@ SMALL = [
     (4, 999, 2, "every", 16, 8),
     (4, 2000, 1, "every", 32, 8),   # 4 query heads per kv head: two kv heads per workgroup
     (5, 1600, 2, "every", 12, 3),   # 4 per kv head with an odd kv head count: one-wave-per-head kernel
+    (3, 1200, 1, "every", 128, 16),  # 8 per kv head over 16 kv heads
+    (3, 900, 2, "every", 8, 1),      # 8 query heads over a single kv head
 ]
 
 
@@ -377,7 +379,7 @@ def test_two_kv_heads_per_workgroup_every_tile_count(repos):
 
 # (query heads, kv heads, plan bq): 4, 2 and 1 query heads per kv head with query
 # tiles of 64 * 8 / group tokens, cut into 8 / group parts of the ping-pong kernel
-PARTS = [(8, 2, 128), (4, 2, 256), (2, 2, 512), (32, 8, 128), (16, 8, 256), (8, 8, 512), (12, 3, 128)]
+PARTS = [(8, 2, 128), (4, 2, 256), (2, 2, 512), (32, 8, 128), (16, 8, 256), (8, 8, 512), (12, 3, 128), (32, 16, 256)]
 
 
 @pytest.mark.parametrize("hq,hkv,bq", PARTS[:3])
