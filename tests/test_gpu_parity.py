@@ -699,25 +699,28 @@ def test_decode_equals_last_prefill_row():
     assert (o[0].float() - out[T - 1].float()).abs().max().item() <= 2e-2
 
 
-@pytest.mark.parametrize("hq,hkv", [(16, 2), (8, 2), (4, 2), (2, 2)])
+@pytest.mark.parametrize("hq,hkv,bq", [(16, 2, 64), (8, 2, 64), (4, 2, 64), (2, 2, 64),
+                                       (8, 2, 128), (4, 2, 256), (2, 2, 512)])
 @pytest.mark.parametrize("offset", [300.0, -300.0, 600.0, 1000.0])
-def test_score_jumps_past_running_max_bf16(offset, hq, hkv):
+def test_score_jumps_past_running_max_bf16(offset, hq, hkv, bq):
     """Scores of a block of keys shifted by a common offset C/8 (C/8 * log2 e in the
     kernels' log2 units): +C on the later half of the keys (scores jump far above
     those of earlier tiles) or -C on the first third (early scores far below later
     ones).  In log2 units the shifts are 54 (C = 300), 108 (C = 600) and 180
-    (C = 1000).  The 8-head-group kernel's fast pass keeps the exponent offset at 0:
-    at -300 every column sum of the early tiles falls under 2^-40, at +600 the sums
-    exceed the 2^100 the fast pass accepts and at +1000 exp2 overflows float32 to
-    inf, so the work item is redone with the rescaling softmax.  The kernels for 1,
-    2 and 4 query heads per kv head rescale a tile whenever its column sums leave
-    [2^-40, 2^40], which every offset here triggers.  The offset rides on the
+    (C = 1000).  The ping-pong kernel's fast pass (8 query heads per kv head; 4 with
+    two kv heads per workgroup; 4, 2 or 1 over query-tile parts) keeps the exponent
+    offset at 0: at -300 every column sum of the early tiles falls under 2^-40, at
+    +600 the sums exceed the 2^100 the fast pass accepts and at +1000 exp2 overflows
+    float32 to inf, so the work item is redone with the rescaling softmax.  The
+    one-wave-per-head kernels (1 and 2 query heads per kv head with 64-token query
+    tiles) rescale a tile whenever its column sums leave [2^-40, 2^40], which every
+    offset here triggers.  The offset rides on the
     lowest-frequency RoPE pair (i = 31, which turns ~1e-5 rad per position, so it
     is position independent here) with q = 1 on that dimension, so it shifts whole
     blocks of scores without sharpening the softmax within them."""
     tr = workload.agent_trajectory(3, seed=111, total=1400, keep=1, repos="every", user_len=64,
                                    assist_range=(30, 200), tool_range=(100, 500), name=f"jump{offset}")
-    plan = akv.build_visibility(akv.ops_from_messages(tr.msg_len, tr.drop, tr.reposition))
+    plan = akv.build_visibility(akv.ops_from_messages(tr.msg_len, tr.drop, tr.reposition), bq=bq)
     q, k, v = workload.prefill_tensors(tr.n_tokens, hq, hkv, 64, seed=112)
     qf, kf = workload.bf16_bits_to_f32(q), workload.bf16_bits_to_f32(k)
     T = tr.n_tokens
@@ -739,6 +742,6 @@ def test_score_jumps_past_running_max_bf16(offset, hq, hkv):
     # q * scale * log2(e) scales every score by 1 +- 2^-9, so the bound is relative
     lerr = np.abs(host_f64(lse) - l_ref).max()
     lbound = 2e-2 + 2.0 ** -8 * np.abs(l_ref).max()
-    print(f"[attn jump offset={offset} hq/hkv={hq}/{hkv}] max-abs {err:.3e} lse {lerr:.3e} (bound {lbound:.3f})")
+    print(f"[attn jump offset={offset} hq/hkv={hq}/{hkv} bq={bq}] max-abs {err:.3e} lse {lerr:.3e} (bound {lbound:.3f})")
     assert np.isfinite(host_f64(out)).all()
     assert err <= 2e-2 and lerr <= lbound
