@@ -745,3 +745,13 @@ def test_score_jumps_past_running_max_bf16(offset, hq, hkv, bq):
     print(f"[attn jump offset={offset} hq/hkv={hq}/{hkv} bq={bq}] max-abs {err:.3e} lse {lerr:.3e} (bound {lbound:.3f})")
     assert np.isfinite(host_f64(out)).all()
     assert err <= 2e-2 and lerr <= lbound
+    if hq == 8 * hkv or bq * (hq // hkv) == 512:
+        # the fused kernel (version rows rotated at staging) redoes the same items
+        # and its redo pass rotates them again: bit for bit the version-buffer path
+        assert plan.info["n_versions"] > 0
+        bufs = {"out": nan_like((T, hq, 64), torch.bfloat16), "lse": nan_like((T, hq), torch.float32)}
+        out_f, lse_f = akv.restore(plan, dev_tensor(q, True), dev_tensor(k, True), dev_tensor(v, True), BASE,
+                                   with_lse=True, bufs=bufs, fused_versions=True)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), out_f.view(torch.int16))
+        assert torch.equal(lse, lse_f)
