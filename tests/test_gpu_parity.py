@@ -478,6 +478,44 @@ def test_workloads_full_size_boundary_and_seeded_rows(cfg, part, parts):
           f"{s_part.size} seeded rows", flush=True)
     assert e_part.size > 0
     _check_rows(tr, qkv, out, lse, bf16=True, rows=rows)
+    if part == 0:
+        # bench.py's own call passes no lse: the same output bit for bit
+        q, k, v = qkv
+        plan = akv.build_visibility(akv.ops_from_messages(tr.msg_len, tr.drop, tr.reposition))
+        o2, l2 = akv.restore(plan, dev_tensor(q, True), dev_tensor(k, True), dev_tensor(v, True), BASE,
+                             bufs={"out": nan_like(tuple(out.shape), torch.bfloat16)})
+        torch.cuda.synchronize()
+        assert l2 is None and torch.equal(out.view(torch.int16), o2.view(torch.int16))
+        del o2
+
+
+# (query heads, kv heads, plan bq, fused version rows, bf16): one case per kernel form
+NO_LSE = [(16, 2, 64, False, True), (16, 2, 64, True, True), (8, 2, 64, False, True), (8, 2, 128, False, True),
+          (8, 2, 128, True, True), (4, 2, 64, False, True), (2, 2, 512, True, True), (12, 3, 64, False, True),
+          (16, 2, 64, False, False)]
+
+
+@pytest.mark.parametrize("hq,hkv,bq,fused,bf16", NO_LSE)
+def test_output_without_lse_is_the_same(hq, hkv, bq, fused, bf16):
+    """Without an lse buffer (the way bench.py calls the attention) every kernel form
+    writes the same output bit for bit as with one."""
+    tr = workload.agent_trajectory(4, seed=141, total=1700, keep=1, repos="every", user_len=50,
+                                   assist_range=(20, 200), tool_range=(60, 400), name="no-lse")
+    plan = akv.build_visibility(akv.ops_from_messages(tr.msg_len, tr.drop, tr.reposition), bq=bq)
+    q, k, v = workload.prefill_tensors(tr.n_tokens, hq, hkv, 64, seed=142, bf16=bf16)
+    dt = torch.bfloat16 if bf16 else torch.float32
+    res = []
+    for with_lse in (True, False):
+        bufs = {"out": nan_like((tr.n_tokens, hq, 64), dt), "lse": nan_like((tr.n_tokens, hq), torch.float32)}
+        out, lse = akv.restore(plan, dev_tensor(q, bf16), dev_tensor(k, bf16), dev_tensor(v, bf16), BASE,
+                               with_lse=with_lse, bufs=bufs, fused_versions=fused)
+        torch.cuda.synchronize()
+        res.append((out, lse, bufs["lse"]))
+    (o1, l1, _), (o2, l2, lb2) = res
+    assert plan.info["n_versions"] > 0 and l2 is None
+    assert torch.equal(o1.view(torch.int32 if not bf16 else torch.int16), o2.view(torch.int32 if not bf16 else torch.int16))
+    assert torch.isnan(lb2).all()   # the lse buffer the call was not given stays untouched
+    _check_rows(tr, (q, k, v), o1, l1, bf16=bf16)
 
 
 # ---------------------------------------------------------------- fused version rows
