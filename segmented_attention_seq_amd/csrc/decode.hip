@@ -155,7 +155,7 @@ __device__ __forceinline__ void decode_step(WaveDecode& st, const StepRows& cur,
   lds_sync();  // this step's LDS reads done before the next step's writes
 }
 
-// Kernel 1.  grid (kDecodeWGs, ceil(hkv / 8)); wave g of workgroup (w, y) handles
+// Kernel 1.  grid (kDecodeWGs, ceil(hkv / 8)), exactly; wave g of workgroup (w, y) handles
 // kv head 8y + g over workgroup w's key range.
 __global__ __launch_bounds__(64 * HG) void decode_split(const uint16_t* __restrict__ q,
                                                         const uint16_t* __restrict__ k,
@@ -165,23 +165,37 @@ __global__ __launch_bounds__(64 * HG) void decode_split(const uint16_t* __restri
                                                         int hkv, float sl2, float* __restrict__ ws) {
   __shared__ int sidx[IDX];
   __shared__ __attribute__((aligned(16))) uint16_t lvs[HG][STEP * VP];
-  const long long P = gridDim.x, w = blockIdx.x;
+  __shared__ int s_first;
+  // the grid is always kDecodeWGs wide: with a power-of-two constant the range
+  // bounds take shifts instead of a branching 64-bit division
+  static_assert((kDecodeWGs & (kDecodeWGs - 1)) == 0, "kDecodeWGs must be a power of two");
+  constexpr long long P = kDecodeWGs;
+  const long long w = blockIdx.x;
+  // The request bounds of the first blockDim requests are read together with N,
+  // so finding the range's first request costs no round trip of its own.
+  const int t = threadIdx.x;
+  const int tc = t < batch ? t : batch;  // clamped, so the loads need no branch
+  const int ip0 = indptr[tc], ip1 = indptr[tc < batch ? tc + 1 : batch];
   const long long N = indptr[batch];
   const long long r0 = range_begin(w, N, P), r1 = range_begin(w + 1, N, P);
-  if (r0 >= r1) return;  // uniform: fewer keys than workgroups
   const int grp = hq / hkv;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g = blockIdx.y * HG + wave;
   const bool active = g < hkv;  // waves past hkv still take part in the barriers
   uint16_t* lv = lvs[wave];
   const int qj = lane & 15, G = lane >> 4;
-  // first request with a key in the range: the last b with indptr[b] <= r0
-  int lo = 0, hi = batch;  // invariant: indptr[lo] <= r0 < indptr[hi] (r0 < N = indptr[batch])
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (indptr[mid] <= r0) lo = mid;
-    else hi = mid;
+  // First request with a key in the range: the one b with indptr[b] <= r0 <
+  // indptr[b + 1] (r0 < N = indptr[batch]; indptr is nondecreasing from 0).
+  if (t < batch && ip0 <= r0 && r0 < ip1) s_first = t;
+  for (int t0 = blockDim.x; t0 < batch; t0 += blockDim.x) {
+    const int u = t0 + t;
+    if (u < batch && indptr[u] <= r0 && r0 < indptr[u + 1]) s_first = u;
   }
+  __syncthreads();
+  if (r0 >= r1) return;  // uniform: fewer keys than workgroups (after the barrier, so the
+                         // bound loads above are issued with N's)
+  const int first = s_first;
+  const int lo = first < 0 ? 0 : first < batch ? first : batch - 1;  // bounded for malformed indptr too
   for (int b = lo; b < batch; ++b) {
     const long long rb = indptr[b], re = indptr[b + 1];
     if (rb >= r1) break;
@@ -203,7 +217,21 @@ __global__ __launch_bounds__(64 * HG) void decode_split(const uint16_t* __restri
     for (long long p0 = s0; p0 < e0; p0 += IDX) {
       const int n = (int)((e0 - p0) < IDX ? (e0 - p0) : IDX);
       __syncthreads();  // earlier readers of sidx are done
-      for (int i = threadIdx.x; i < n; i += blockDim.x) sidx[i] = indices[p0 + i];
+      // eight index loads per thread in flight before the first LDS write (a loop
+      // storing each load before the next waits out one round trip per pass)
+      for (int i0 = threadIdx.x; i0 < n; i0 += 8 * blockDim.x) {
+        int ix[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int i = i0 + j * (int)blockDim.x;
+          ix[j] = indices[p0 + (i < n ? i : n - 1)];  // clamped, so the loads need no branch
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int i = i0 + j * (int)blockDim.x;
+          if (i < n) sidx[i] = ix[j];
+        }
+      }
       __syncthreads();
       if (!active) continue;
       // four-deep ring: steps base .. base + 96 in flight while base computes
