@@ -167,8 +167,9 @@ def _back_to_back(ms, nbytes):
 def main():
     args = parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
-              "the per-GPU shard design is in DESIGN.md", file=sys.stderr)
+        print(f"bench.py: runs on one GPU only (asked for --gpus {args.gpus}); the library has no "
+              "multi-GPU path: each GPU would run these kernels on its own kv heads or requests",
+              file=sys.stderr)
         sys.exit(2)
     import torch
     from segmented_attention_seq_amd import akv, workload

@@ -4,7 +4,7 @@
 
 Every HIP translation unit is compiled with packed-FP32 instructions disabled
 (-Xclang -target-feature -Xclang -packed-fp32-ops); the library is linked next
-to this file so the Python binding (and a GPU machine receiving the tree) finds it.
+to this file so the Python binding finds it, also in a copy of the tree on another machine.
 """
 from __future__ import annotations
 

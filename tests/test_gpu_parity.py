@@ -1,6 +1,6 @@
 """GPU parity: every libakv kernel against the CPU oracle on the same seeded inputs.
 
-Tolerances (written here, reasoned in the design doc):
+Tolerances (written here; each follows from the roundings of the kernel's arithmetic):
   bf16 attention / decode outputs  max-abs 2e-2
   fp32 attention                   max-abs 1e-5 (also lse)
   fp32 repos / RoPE                max-abs 1e-5
