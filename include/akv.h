@@ -280,8 +280,11 @@ int akv_segment_attention_fused(const akv_plan* plan, const void* dev_plan, cons
  *
  * One query token per request b < batch: out[b][h] = attention of q[b][h] over the
  * pool rows indices[indptr[b] .. indptr[b+1]) (its active cache plus its own new
- * slot, gathered at page size 1).  q, k_pool, v_pool: bf16; indptr/indices: device
- * int32 (indptr[batch] = total gathered keys).  max_n: host-side bound on every
+ * slot, gathered at page size 1).  q [batch][hq][d], k_pool/v_pool [slots][hkv][d]:
+ * bf16; indptr/indices: device int32, indptr nondecreasing from indptr[0] = 0
+ * (indptr[batch] = total gathered keys).  out [batch][hq][d] bf16; lse [batch][hq]
+ * float32 (natural log of the softmax denominator of the scaled scores), nullable.
+ * max_n: host-side bound on every
  * request's key count, in [1, 2^31); it is checked but does not shape the launch,
  * which cuts all the batch's gathered keys into equal ranges, one per CU, and merges
  * each request's partials.  A request with zero keys (indptr[b+1] <= indptr[b])

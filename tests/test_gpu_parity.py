@@ -641,7 +641,12 @@ def _decode_case(batch, lo, hi, seed, hq=64, hkv=8, shuffle=False):
     max_n = int(np.diff(db.indptr).max())
     akv.decode_attention(dev_tensor(db.q, True), pool_k, pool_v, dev_int(db.indptr),
                          dev_int(db.indices), max_n, out, lse)
+    # without lse (bench.py's call): the same output bit for bit
+    out2 = nan_like((batch, hq, db.d), torch.bfloat16)
+    akv.decode_attention(dev_tensor(db.q, True), pool_k, pool_v, dev_int(db.indptr),
+                         dev_int(db.indices), max_n, out2)
     torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
     o_ref, l_ref = oracle.decode(Bf16Rows(db.q)[:], Bf16Rows(db.k_rows), Bf16Rows(db.v_rows), db.indptr)
     err = np.abs(host_f64(out) - o_ref).max()
     lerr = np.abs(host_f64(lse) - l_ref).max()
