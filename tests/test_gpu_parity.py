@@ -663,10 +663,12 @@ def test_decode_small(args):
 
 # The split kernel cuts all gathered keys of the batch into 256 equal ranges: more
 # requests than ranges (several requests per range), fewer keys than ranges (most
-# ranges empty), one request spread over every range (256 partials to merge), and
-# more than 8 kv heads (two head groups per range).
+# ranges empty), one request spread over every range (256 partials to merge), more
+# than 8 kv heads (two head groups per range), and more requests than threads in a
+# workgroup (512 with 8 kv heads, 128 with 2), so a range's first request is found
+# past the bounds read with N.
 @pytest.mark.parametrize("args", [(300, 1, 40, 95, 64, 8), (2, 1, 4, 96, 8, 8), (1, 9000, 9001, 97, 64, 8),
-                                  (3, 100, 2000, 98, 32, 16)])
+                                  (3, 100, 2000, 98, 32, 16), (700, 1, 40, 99, 64, 8), (300, 1, 60, 100, 16, 2)])
 def test_decode_balanced_split_edges(args):
     batch, lo, hi, seed, hq, hkv = args
     _decode_case(batch, lo, hi, seed, hq=hq, hkv=hkv)
